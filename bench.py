@@ -1,0 +1,278 @@
+"""Benchmark: one step of the QJL hot path on the Llama-2-7B-shaped decode cache.
+
+A step = quantize every key of the cache (batch 8 x 32 heads x 8192 tokens,
+head_dim 128, dense m = 256 sketch, bf16 keys with per-channel outliers),
+project the 256 queries (one per head), and score every (query, key) pair.
+All inputs are synthetic (seeded) and already resident in HBM when the timed
+region starts.
+
+Printed (one JSON line): whole-step algorithmic throughput (GB/s), plus
+  roofline      the dominant kernel (dense quantize), timed live with HIP
+                events on the library's stream, against MI355X HBM peak;
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same step;
+and extra per-kernel figures: keys quantized/s, the score kernel's GB/s on
+caches rotated beyond the 256 MB Infinity Cache, and the long-context
+(131072 tokens, m = 512) score.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QJL score GB/s (% of HBM peak) + keys quantized/s, 7B-shape decode"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "quantize_dense_llama7b_decode_pmc.txt")
+QUANT_KERNEL_SRC = os.path.join(ROOT, "bit_quantized_jl_amd", "csrc", "k_quantize_mfma.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time for the oracle baseline sample")
+    p.add_argument("--skip-extras", action="store_true",
+                   help="only the timed step (used under profilers)")
+    return p.parse_args()
+
+
+def kernel_src_hash() -> str:
+    with open(QUANT_KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per quantize launch from the committed rocprofv3 PMC summary,
+    or None when absent or taken on another version of the kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_src_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds: float):
+    """The float64 oracle on whole (batch, head) groups of the same step until
+    about `seconds` of CPU time; throughput in the metric's unit (GB/s)."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from oracle import qjl as oq
+    from oracle import sketch as osk
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    sk = osk.make_dense(w.seed, w.d, w.m)
+    one = w.scaled(batch=1, heads=1)
+    K = wl.make_keys(one, "cpu").double().numpy()   # one group's keys (same recipe)
+    q = wl.make_queries(one, "cpu").double().numpy()
+    t0 = time.perf_counter()
+    groups = 0
+    while True:
+        bits, norms, _, _ = oq.quantize(sk, K, w.dtype)
+        Sq = oq.project(sk, q, w.dtype)
+        oq.score(Sq, bits, norms, w.m, 0.0, 1, w.n_q, w.n_k)
+        groups += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or groups >= w.groups:
+            break
+    per_group_bytes = step_bytes(w) / w.groups
+    return {"value": per_group_bytes * groups / el / 1e9, "unit": "GB/s",
+            "cores": int(min(cores, blas_threads)),
+            "host_cores": cores, "blas_threads": blas_threads, "kind": "oracle",
+            "sample": f"{groups} of {w.groups} (batch, head) groups of the same step "
+                      f"({groups * w.n_k} keys: quantize + project + score, float64 numpy), "
+                      f"{el:.1f} s"}
+
+
+def quantize_bytes(w) -> float:
+    esz = 2 if w.dtype == "bf16" else 4
+    return w.n_keys * (w.d * esz + w.m / 8 + 4)
+
+
+def score_bytes(w) -> float:
+    return (w.groups * w.n_k * (w.m / 8 + 4) + w.groups * w.n_q * w.n_k * 4
+            + w.groups * w.n_q * w.m * 4)
+
+
+def project_bytes(w) -> float:
+    esz = 2 if w.dtype == "bf16" else 4
+    return w.n_queries * (w.d * esz + w.m * 4)
+
+
+def step_bytes(w) -> float:
+    return quantize_bytes(w) + project_bytes(w) + score_bytes(w)
+
+
+def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
+    """Score kernel alone over `n_sets` distinct (bits, norms, Sq) sets, so the
+    working set exceeds the 256 MB Infinity Cache; returns mean seconds."""
+    import workloads as wl
+    dev = "cuda:0"
+    sets = []
+    for s in range(n_sets):
+        bits = wl.make_random_bits(w.groups * w.n_k, w.m, seed=100 + s, device=dev)
+        norms = torch.rand(w.groups * w.n_k, device=dev) * 10 + 1
+        Sq = torch.randn(w.groups * w.n_q, w.m, device=dev) * 11
+        out = torch.empty(w.groups, w.n_q, w.n_k, device=dev)
+        sets.append((Sq, bits, norms, out))
+    for i in range(2 * n_sets):
+        Sq, bits, norms, out = sets[i % n_sets]
+        qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k, scores_out=out)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i in range(iters):
+        Sq, bits, norms, out = sets[i % n_sets]
+        evs[i][0].record(st)
+        qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k, scores_out=out)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) / 1e3 for a, b in evs)
+    del sets
+    torch.cuda.empty_cache()
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the kernels work on one GPU's shard; see the sharding note in the design).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_quantized_jl_amd as qj
+    import workloads as wl
+
+    qj.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    w = wl.DECODE_7B
+    K = wl.make_keys(w, dev)
+    q = wl.make_queries(w, dev)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    norms = torch.empty(w.n_keys, dtype=torch.float32, device=dev)
+    bits = torch.empty((w.n_keys, w.m // 32), dtype=torch.int32, device=dev)
+    Sq = torch.empty((w.n_queries, w.m), dtype=torch.float32, device=dev)
+    scores = torch.empty((w.groups, w.n_q, w.n_k), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+        if ev is not None:
+            ev[1].record(st)
+        qj.project_query(sk, q, Sq_out=Sq, stream=st)
+        qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k, scores_out=scores, stream=st)
+        if ev is not None:
+            ev[2].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(st)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(st)
+    torch.cuda.synchronize()
+    total_s = t_start.elapsed_time(t_end) / 1e3
+    per_step = total_s / args.steps
+    q_times = [a.elapsed_time(b) / 1e3 for a, b, _ in evs]
+    ps_times = [b.elapsed_time(c) / 1e3 for _, b, c in evs]
+    q_avg = sum(q_times) / len(q_times)
+    ps_avg = sum(ps_times) / len(ps_times)
+
+    qb = quantize_bytes(w)
+    q_flops = 2.0 * w.n_keys * w.d * w.m
+    achieved = qb / q_avg / 1e9
+    traffic = read_traffic()
+    result = {
+        "metric": METRIC,
+        "value": step_bytes(w) / per_step / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "context": w.n_k,
+                   "head_dim": w.d, "m": w.m, "sketch": w.variant, "queries_per_head": w.n_q,
+                   "keys": "bf16 N(0,1), 4 outlier channels x15 per head"},
+        "roofline": {"kernel": "quantize_mfma_kernel<128,256>", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": qb, "avg_launch_s": q_avg,
+                     "mfma_tflops": q_flops / q_avg / 1e12,
+                     "mfma_frac_bf16": q_flops / q_avg / 1e12 / BF16_PEAK_TFLOPS},
+        "keys_quantized_per_s": w.n_keys / q_avg,
+        "project_plus_score_s": ps_avg,
+    }
+    if not args.skip_extras:
+        # score kernel alone, cache rotated past the 256 MB Infinity Cache
+        sb = score_bytes(w)
+        s_mean, s_med = time_score_rotating(qj, torch, w, sk, n_sets=4, iters=40)
+        result["score_decode7b"] = {"GBps": sb / s_mean / 1e9, "frac_hbm": sb / s_mean / 1e9 / HBM_PEAK_GBPS,
+                                    "scores_per_s": w.groups * w.n_q * w.n_k / s_mean,
+                                    "mean_s": s_mean, "median_s": s_med, "bytes": sb,
+                                    "rotation": "4 sets x 75.8 MB"}
+        del K
+        torch.cuda.empty_cache()
+        wl2 = wl.LONG_CTX
+        sk2 = qj.make_sketch(wl2.seed, wl2.d, wl2.m, wl2.variant)
+        sb2 = score_bytes(wl2)
+        s2_mean, s2_med = time_score_rotating(qj, torch, wl2, sk2, n_sets=2, iters=20)
+        result["score_long_context"] = {"workload": wl2.name, "GBps": sb2 / s2_mean / 1e9,
+                                        "frac_hbm": sb2 / s2_mean / 1e9 / HBM_PEAK_GBPS,
+                                        "scores_per_s": wl2.groups * wl2.n_k / s2_mean,
+                                        "mean_s": s2_mean, "median_s": s2_med, "bytes": sb2,
+                                        "rotation": "2 sets x 302 MB"}
+        sk2.close()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    sk.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

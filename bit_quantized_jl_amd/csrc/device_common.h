@@ -1,0 +1,50 @@
+// Device helpers shared by the libqjl kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qjl_internal.h"
+
+namespace qjl {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float *p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+// Dither draw for one coordinate pair (D-FQJL's Gaussian dither, "Fast
+// Quantized Johnson-Lindenstrauss Transforms" page).  One SplitMix64 word
+// h = r(seed, 4, ctr) per pair; a = h >> 40 and b = (h >> 16) & 0xFFFFFF give
+// u1 = (a + 1) 2^-24 and u2 = b 2^-24 (exact in float32); Box-Muller returns
+// R cos(2 pi u2) for the even and R sin(2 pi u2) for the odd coordinate.
+__device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &xc, float &xs) {
+  const uint64_t h = stream_draw(key, ctr);
+  const uint32_t a = (uint32_t)(h >> 40);
+  const uint32_t b = (uint32_t)(h >> 16) & 0xFFFFFFu;
+  const float u1 = (float)(a + 1u) * 0x1p-24f;
+  const float u2 = (float)b * 0x1p-24f;
+  const float r = sqrtf(-2.0f * logf(u1));
+  float sn, cs;
+  sincospif(2.0f * u2, &sn, &cs);
+  xc = r * cs;
+  xs = r * sn;
+}
+
+__device__ __forceinline__ float dither_one(uint64_t key, uint64_t key_index, int m, int j) {
+  float c, s;
+  dither_pair(key, key_index * (uint64_t)(m / 2) + (uint64_t)(j >> 1), c, s);
+  return (j & 1) ? s : c;
+}
+
+}  // namespace qjl

@@ -1,0 +1,224 @@
+// FQJL sketch kernel: stacked blocks H diag(G_b) Pi_b (H/sqrt d) diag(D_b)
+// ("Fast Quantized Johnson-Lindenstrauss Transforms" page: randomized
+// Hadamard transforms with a Gaussian second diagonal and a uniform random
+// permutation between them; optional Gaussian dither before the sign).
+//
+// One row (key or query) per lane.  The d coordinates of a row live in the
+// lane's registers, so both Walsh-Hadamard transforms are unrolled butterfly
+// networks with no cross-lane traffic (O(d log d) additions per block).  The
+// permutation is the only data-dependent step: each lane stores its vector to
+// its own column of an LDS tile (element c at c*64 + lane, which is bank-
+// conflict free because the 64 lanes hit consecutive words) and gathers it
+// back in the order P_b.  A lane reads only what it wrote, so no barrier is
+// needed.  Sign bits are packed per lane into 32-bit words (bit = [y >= 0],
+// which maps -0 to 1 like +0).  All arithmetic is float32.
+//
+// Coordinates: block b produces sketch coordinates [b d, (b+1) d).  G_b is
+// pre-scaled by 1/sqrt(d) on the host, so the kernel computes
+// H (Gs_b * (H (D_b x))[P_b]).
+#include "device_common.h"
+
+namespace qjl {
+
+namespace {
+
+template <int D>
+__device__ __forceinline__ void fwht_reg(float (&u)[D]) {
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = u[j], b = u[j + h];
+        u[j] = a + b;
+        u[j + h] = a - b;
+      }
+    }
+  }
+}
+
+template <int D, typename T, bool PROJECT, bool DITHER>
+__global__ __launch_bounds__(64) void fqjl_kernel(
+    const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
+    const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
+    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    float *__restrict__ Y) {
+  __shared__ float lds[D * 64];
+  const int lane = threadIdx.x;
+  const int W = m / 32;
+  constexpr bool HOLD = true;  // keep the input row in registers across blocks
+  for (int64_t r0 = (int64_t)blockIdx.x * 64; r0 < n; r0 += (int64_t)gridDim.x * 64) {
+    const int64_t row = r0 + lane;
+    const bool valid = row < n;
+    const T *xr = X + (valid ? row : 0) * (int64_t)D;
+    float x[HOLD ? D : 1];
+    float nrm = 0.f;
+    if (HOLD) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) x[c] = valid ? load_as_f32(xr, c) : 0.f;
+    }
+    if (!PROJECT) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        const float v = HOLD ? x[c] : (valid ? load_as_f32(xr, c) : 0.f);
+        s = fmaf(v, v, s);
+      }
+      nrm = sqrtf(s);
+      if (valid) norms[row] = nrm;
+    }
+    for (int b = 0; b < nb; ++b) {
+      float u[D];
+      const uint32_t *ds = Dsign + b * D;
+#pragma unroll
+      for (int c = 0; c < D; ++c) {
+        const float v = HOLD ? x[c] : (valid ? load_as_f32(xr, c) : 0.f);
+        u[c] = __uint_as_float(__float_as_uint(v) ^ ds[c]);
+      }
+      fwht_reg<D>(u);
+#pragma unroll
+      for (int c = 0; c < D; ++c) lds[c * 64 + lane] = u[c];
+      const int32_t *pb = P + b * D;
+      const float *gb = Gs + b * D;
+#pragma unroll
+      for (int c = 0; c < D; ++c) u[c] = lds[pb[c] * 64 + lane] * gb[c];
+      fwht_reg<D>(u);
+      if (PROJECT) {
+        if (valid) {
+          float *yr = Y + row * (int64_t)m + b * D;
+#pragma unroll
+          for (int c = 0; c < D; ++c) yr[c] = u[c];
+        }
+      } else {
+        if (DITHER) {
+          const float amp = rho * nrm;
+          const uint64_t pair0 = (uint64_t)(base + (valid ? row : 0)) * (uint64_t)(m / 2) +
+                                 (uint64_t)(b * D / 2);
+#pragma unroll
+          for (int c = 0; c < D; c += 2) {
+            float xc, xs;
+            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            u[c] += amp * xc;
+            u[c + 1] += amp * xs;
+          }
+        }
+        if (valid) {
+          uint32_t *br = bits + row * (int64_t)W + b * (D / 32);
+#pragma unroll
+          for (int w = 0; w < D / 32; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int t = 0; t < 32; ++t) word |= (u[32 * w + t] >= 0.f ? 1u : 0u) << t;
+            br[w] = word;
+          }
+        }
+      }
+    }
+  }
+}
+
+// d = 8 or 16: a block is narrower than one 32-bit word, so the bits of
+// consecutive blocks share words.  These small sizes exist so the GPU chain
+// can be checked against explicit matrices; they run a plain per-lane loop
+// that writes whole words after all blocks of a word are done.
+template <int D, typename T, bool PROJECT, bool DITHER>
+__global__ __launch_bounds__(64) void fqjl_small_kernel(
+    const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
+    const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
+    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    float *__restrict__ Y) {
+  const int lane = threadIdx.x;
+  const int W = m / 32;
+  for (int64_t r0 = (int64_t)blockIdx.x * 64; r0 < n; r0 += (int64_t)gridDim.x * 64) {
+    const int64_t row = r0 + lane;
+    if (row >= n) continue;
+    float x[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) x[c] = load_as_f32(X + row * (int64_t)D, c);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) s = fmaf(x[c], x[c], s);
+    const float nrm = sqrtf(s);
+    if (!PROJECT) norms[row] = nrm;
+    uint32_t word = 0;
+    for (int b = 0; b < nb; ++b) {
+      float u[D], v[D];
+#pragma unroll
+      for (int c = 0; c < D; ++c) u[c] = __uint_as_float(__float_as_uint(x[c]) ^ Dsign[b * D + c]);
+      fwht_reg<D>(u);
+      for (int c = 0; c < D; ++c) {
+        // gather u[P[c]] from registers with a select chain (D <= 16)
+        const int p = P[b * D + c];
+        float g = 0.f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) g = (e == p) ? u[e] : g;
+        v[c] = g * Gs[b * D + c];
+      }
+      fwht_reg<D>(v);
+      for (int c = 0; c < D; ++c) {
+        const int j = b * D + c;
+        float y = v[c];
+        if (PROJECT) {
+          Y[row * (int64_t)m + j] = y;
+          continue;
+        }
+        if (DITHER) y += (rho * nrm) * dither_one(dkey, (uint64_t)(base + row), m, j);
+        word |= (y >= 0.f ? 1u : 0u) << (j & 31);
+        if ((j & 31) == 31) {
+          bits[row * (int64_t)W + (j >> 5)] = word;
+          word = 0;
+        }
+      }
+    }
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t base,
+                         float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+  const HostSketch &h = sk->host;
+  const int nb = h.m / D;
+  const int64_t tiles = (n + 63) / 64;
+  const int grid = (int)(tiles < 16384 ? tiles : 16384);
+  const bool proj = Y != nullptr;
+  const bool dith = !proj && h.rho > 0.f;
+#define QJL_FQJL_LAUNCH(KERNEL, PJ, DT)                                                        \
+  hipLaunchKernelGGL((KERNEL<D, T, PJ, DT>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign, \
+                     sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
+  if (D >= 32) {
+    if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, true, false);
+    else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, false, true);
+    else QJL_FQJL_LAUNCH(fqjl_kernel, false, false);
+  } else {
+    if (proj) QJL_FQJL_LAUNCH(fqjl_small_kernel, true, false);
+    else if (dith) QJL_FQJL_LAUNCH(fqjl_small_kernel, false, true);
+    else QJL_FQJL_LAUNCH(fqjl_small_kernel, false, false);
+  }
+#undef QJL_FQJL_LAUNCH
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t base,
+                         float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+  switch (sk->host.d) {
+    case 8: return launch_fqjl_t<8>(sk, X, n, base, norms, bits, Y, st);
+    case 16: return launch_fqjl_t<16>(sk, X, n, base, norms, bits, Y, st);
+    case 32: return launch_fqjl_t<32>(sk, X, n, base, norms, bits, Y, st);
+    case 64: return launch_fqjl_t<64>(sk, X, n, base, norms, bits, Y, st);
+    case 128: return launch_fqjl_t<128>(sk, X, n, base, norms, bits, Y, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
+                       float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+  if (dtype == QJL_DTYPE_F32)
+    return launch_fqjl_d(sk, static_cast<const float *>(X), n, base, norms, bits, Y, st);
+  return launch_fqjl_d(sk, static_cast<const uint16_t *>(X), n, base, norms, bits, Y, st);
+}
+
+}  // namespace qjl

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host API and the HIP kernels of libqjl.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/qjl.h"
+
+namespace qjl {
+
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014) and the
+// counter streams built on it:  key(seed, s) = mix64(seed + PHI (s + 1)),
+// r(seed, s, i) = mix64(key + PHI (i + 1)).
+constexpr uint64_t PHI = 0x9E3779B97F4A7C15ull;
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+  z ^= z >> 30;
+  z *= 0xBF58476D1CE4E5B9ull;
+  z ^= z >> 27;
+  z *= 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z;
+}
+__host__ __device__ inline uint64_t stream_key(uint64_t seed, uint64_t stream) {
+  return mix64(seed + PHI * (stream + 1));
+}
+__host__ __device__ inline uint64_t stream_draw(uint64_t key, uint64_t i) {
+  return mix64(key + PHI * (i + 1));
+}
+
+enum : int { STREAM_DENSE = 0, STREAM_D = 1, STREAM_P = 2, STREAM_G = 3, STREAM_DITHER = 4 };
+
+// Host-side random parameters of one sketch (no device state).
+struct HostSketch {
+  uint64_t seed = 0;
+  int d = 0, m = 0, variant = 0;
+  float rho = 0.f;
+  std::vector<float> S32;      // dense: m*d, float32 rounding of the Gaussian draws
+  std::vector<uint16_t> S16;   // dense: m*d, bfloat16 bits (RNE of S32)
+  std::vector<int8_t> D;       // FQJL: nb*d, +1/-1
+  std::vector<int32_t> P;      // FQJL: nb*d, permutation of [0, d) per block
+  std::vector<float> G;        // FQJL: nb*d, float32 Gaussians
+};
+
+qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho);
+void generate_host_sketch(HostSketch &hs);
+uint16_t f32_to_bf16_rne(float x);
+// Explicit m x d FQJL matrix (double), for export.
+void fqjl_explicit(const HostSketch &hs, std::vector<double> &out);
+
+}  // namespace qjl
+
+// Device-resident sketch.  All device arrays live in one allocation `dmem`.
+struct qjl_sketch {
+  qjl::HostSketch host;
+  int device = -1;
+  uint64_t dither_key = 0;       // key(seed, 4)
+  void *dmem = nullptr;
+  // dense
+  const float *S32 = nullptr;    // m*d  float32 S (row-major)
+  const float *S16f = nullptr;   // m*d  bfloat16-rounded S widened to float32 (row-major)
+  const uint16_t *S16mfma = nullptr;  // m*d bf16 in the MFMA B-operand order (see k_quantize_mfma)
+  // FQJL
+  const uint32_t *Dsign = nullptr;    // nb*d sign masks: 0 (D=+1) or 0x80000000 (D=-1)
+  const int32_t *P = nullptr;         // nb*d
+  const float *Gs = nullptr;          // nb*d  G_b[c] / sqrt(d), rounded to float32
+};
+
+namespace qjl {
+
+// Kernel launchers (each returns hipGetLastError() of its launch).
+hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtype, int64_t n,
+                                   int64_t base, float *norms, uint32_t *bits, hipStream_t st);
+hipError_t launch_project_dense(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
+                                float *Sq, hipStream_t st);
+bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
+                             const uint32_t *bits);
+hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, float *norms,
+                                uint32_t *bits, hipStream_t st);
+hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
+                       float *norms, uint32_t *bits, float *Y, hipStream_t st);
+hipError_t launch_score_generic(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                const float *norms, int64_t G, int64_t nq, int64_t nk,
+                                float *scores, hipStream_t st);
+hipError_t launch_score(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                        const float *norms, int64_t G, int64_t nq, int64_t nk, float *scores,
+                        hipStream_t st);
+
+// Host-computed data the score kernels take per launch.
+float estimator_scale(int m, float rho);
+
+}  // namespace qjl

@@ -1,0 +1,185 @@
+/*
+ * qjl.h -- C ABI of libqjl: the QJL key-cache sketch and its asymmetric
+ * inner-product estimator, for AMD Instinct MI355X (gfx950).
+ *
+ * The method: "QJL" abstract (Zandieh, Daliri, Han) on Majid Daliri's
+ * scholarfeed author page.  A key k (dimension d) is projected by a random
+ * m x d sketch S; only sign(S k) is kept, m bits, plus the float32 norm ||k||.
+ * A query q is projected (S q) but not quantized.  The attention score
+ * q.k is estimated as
+ *
+ *     sqrt(pi/2) * sqrt(1 + rho^2) / m * ||k|| * sum_j (2 b_j - 1) (S q)_j
+ *
+ * where b_j = [ (S k)_j + rho ||k|| xi_j >= 0 ] and rho is the optional
+ * dither level (rho = 0: no dither).  sqrt(pi/2)/m is the constant that makes
+ * the estimate unbiased for Gaussian rows; sqrt(1 + rho^2) undoes the
+ * shrinkage that dither adds.
+ *
+ * Sketches (qjl_variant):
+ *   QJL_VARIANT_DENSE  S[j][c] iid N(0, 1)  (the dense Gaussian projection of
+ *                      the QJL abstract and the "Fast Quantized
+ *                      Johnson-Lindenstrauss Transforms" page).
+ *   QJL_VARIANT_FQJL   m/d stacked blocks  H diag(G_b) Pi_b (H/sqrt d) diag(D_b)
+ *                      with Sylvester H (+-1 entries, natural order), D_b
+ *                      Rademacher, Pi_b a uniform random permutation used as
+ *                      a gather (Pi u)_i = u[P_b[i]], and G_b Gaussian -- the
+ *                      composition of randomized Hadamard transforms with a
+ *                      Gaussian second diagonal and a permutation between the
+ *                      transforms ("Fast Quantized Johnson-Lindenstrauss
+ *                      Transforms" page: abstract; "Key concepts", P-FQJL).
+ *                      Dither (rho > 0) is the D-FQJL smoothing of the sign
+ *                      quantizer on the same page, added after the transform
+ *                      and before the sign.
+ *
+ * Every random quantity comes from SplitMix64 counter streams keyed by the
+ * seed (stream 0: dense S, 1: D, 2: P, 3: G, 4: dither), so a sketch and its
+ * dither are reproducible from (seed, d, m, variant, rho) alone.
+ *
+ * Layouts (all dense, row-major, no strides):
+ *   K[n_keys][d], q[n_queries][d]      float32 or bfloat16 (qjl_dtype)
+ *   Sq[n_queries][m]                   float32
+ *   bits[n_keys][m/32]                 uint32; bit t of word w is coordinate
+ *                                      32 w + t (LSB-first); bit = 1 <=> the
+ *                                      (dithered) coordinate is >= 0.  Read as
+ *                                      little-endian u64 words, bit t of word
+ *                                      w is coordinate 64 w + t.
+ *   norms[n_keys]                      float32 ||k||_2
+ *   scores[n_groups][n_q][n_k]         float32
+ * Group g owns key rows [g n_k, (g+1) n_k) and query rows [g n_q, (g+1) n_q)
+ * (a group is one (batch, head) pair of a KV cache).
+ *
+ * Precision contract: bfloat16 keys and queries are projected with the
+ * bfloat16 rounding of the float32 sketch (S_bf16 = RNE(S_f32)); float32
+ * inputs with S_f32.  Accumulation is float32.  Keys and the queries scored
+ * against them should use the same dtype so both see the same S.
+ *
+ * Ownership and execution:
+ *   - The caller owns every device buffer (K, q, Sq, bits, norms, scores);
+ *     all of them are device pointers on the sketch's device.
+ *   - The library owns the sketch (host and device copies) from
+ *     qjl_make_sketch to qjl_destroy_sketch.  A sketch is immutable, so
+ *     concurrent calls with one sketch on different streams are safe.
+ *   - The hot calls (quantize, project, score) never allocate; they enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *     return.  Kernel faults surface at the caller's next synchronization.
+ *   - Argument validation happens before any HIP call.  n = 0 is a no-op.
+ */
+#ifndef QJL_H
+#define QJL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QJL_OK = 0,
+  QJL_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative count, bad enum, misaligned pointer,
+                                   wrong device, m not a multiple of 32, bad rho */
+  QJL_ERR_UNSUPPORTED = 2,      /* valid but outside the implemented shapes */
+  QJL_ERR_OUT_OF_MEMORY = 3,    /* host or device allocation failed (qjl_make_sketch only) */
+  QJL_ERR_DEVICE = 4            /* no usable GPU, or a HIP call / kernel launch failed */
+} qjl_status;
+
+typedef enum { QJL_VARIANT_DENSE = 0, QJL_VARIANT_FQJL = 1 } qjl_variant;
+typedef enum { QJL_DTYPE_F32 = 0, QJL_DTYPE_BF16 = 1 } qjl_dtype;
+
+typedef struct qjl_sketch qjl_sketch; /* opaque, library-owned */
+
+/* Limits of this build.  dense: 1 <= d <= 512;  FQJL: d a power of two in
+ * [8, 128] and m a multiple of d;  both: 32 <= m <= 8192, m % 32 == 0. */
+#define QJL_MAX_D 512
+#define QJL_MAX_M 8192
+
+/*
+ * Draw a sketch (the random JL matrix of the QJL abstract, or the FQJL
+ * composition) from `seed` on the host, upload it to the current HIP device
+ * and return it in *out.  rho >= 0 is the dither level (0: none).
+ * Errors: out == NULL, m % 32 != 0, m or d out of range, bad variant,
+ * rho < 0 or not finite -> INVALID_ARGUMENT / UNSUPPORTED (per the limits
+ * above); no GPU -> DEVICE; allocation failure -> OUT_OF_MEMORY.  On error
+ * *out is set to NULL (when out is not NULL).
+ */
+qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant, float rho,
+                           qjl_sketch **out);
+
+/* Free a sketch.  NULL -> INVALID_ARGUMENT.  The caller must not destroy a
+ * sketch while work that uses it is still queued. */
+qjl_status qjl_destroy_sketch(qjl_sketch *sk);
+
+/* Read back a sketch's parameters (any output pointer may be NULL). */
+qjl_status qjl_sketch_info(const qjl_sketch *sk, uint64_t *seed, int32_t *d, int32_t *m,
+                           int32_t *variant, float *rho, int32_t *device);
+
+/*
+ * Copy the sketch's effective m x d matrix (row-major) to host memory:
+ * S_f32 gets the float32 matrix applied to float32 inputs, S_bf16 the
+ * bfloat16 bit patterns applied to bfloat16 inputs (dense only; for FQJL the
+ * float32 matrix is the explicit product of the blocks, evaluated in double
+ * and rounded, and S_bf16 must be NULL).  Either pointer may be NULL.
+ */
+qjl_status qjl_sketch_export(const qjl_sketch *sk, float *S_f32, uint16_t *S_bf16);
+
+/*
+ * Host-only: generate the random parameters of a sketch without a GPU, into
+ * caller-owned host buffers (any may be NULL).  Dense: S_f32[m*d],
+ * S_bf16[m*d].  FQJL: D_signs[(m/d)*d] (+1/-1), perm[(m/d)*d], G[(m/d)*d].
+ * Same validation as qjl_make_sketch.
+ */
+qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t variant,
+                                    float *S_f32, uint16_t *S_bf16, int8_t *D_signs,
+                                    int32_t *perm, float *G);
+
+/*
+ * Quantize n_keys keys: bits_out[i] = packed signs of S k_i (+ dither),
+ * norms_out[i] = ||k_i||_2 (QJL abstract: JL transform followed by sign-bit
+ * quantization; no per-block constants, one norm per key).
+ * key_index_base is the global index of row 0; the dither of key i is drawn
+ * from counter (key_index_base + i), so a cache appended in pieces gets the
+ * same bits as one quantized whole.
+ * K: device, [n_keys][d] in `dtype`, aligned to its element size.
+ * norms_out: device float[n_keys]; bits_out: device uint32[n_keys][m/32].
+ * Errors: NULL pointers (n_keys > 0), n_keys < 0, key_index_base < 0, bad
+ * dtype, misalignment, sketch of another device -> INVALID_ARGUMENT;
+ * launch failure -> DEVICE.
+ */
+qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype, int64_t n_keys,
+                             int64_t key_index_base, float *norms_out, uint32_t *bits_out,
+                             void *stream);
+
+/*
+ * Project n_queries queries: Sq_out[i] = S q_i in float32, not quantized (the
+ * "standard JL transform without quantization" of the QJL abstract; no
+ * dither).  q: device [n_queries][d] in `dtype`; Sq_out: device
+ * float[n_queries][m].  Errors as for qjl_quantize_keys.
+ */
+qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
+                             int64_t n_queries, float *Sq_out, void *stream);
+
+/*
+ * Estimate scores[g][i][t] = sqrt(pi/2) sqrt(1+rho^2)/m * norms[g n_k + t]
+ *   * sum_j (2 bit[g n_k + t][j] - 1) * Sq[g n_q + i][j]
+ * for every group g, query i < n_q and key t < n_k (the asymmetric
+ * estimator of the QJL abstract).  All pointers are device pointers
+ * (Sq: float[n_groups*n_q][m], bits: uint32[n_groups*n_k][m/32],
+ * norms: float[n_groups*n_k], scores_out: float[n_groups][n_q][n_k]).
+ * Any count 0 -> no-op.  Errors: NULL pointers, negative counts,
+ * misalignment (4 bytes), sketch of another device -> INVALID_ARGUMENT;
+ * launch failure -> DEVICE.
+ */
+qjl_status qjl_score(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                     const float *norms, int64_t n_groups, int64_t n_q_per_group,
+                     int64_t n_k_per_group, float *scores_out, void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *qjl_status_string(qjl_status s);
+
+/* Library version string, e.g. "qjl 0.1.0 gfx950". */
+const char *qjl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QJL_H */

@@ -62,9 +62,12 @@ def project(sk, X: np.ndarray, in_dtype: str) -> np.ndarray:
     return X @ S.T
 
 
-def quantize(sk, K: np.ndarray, in_dtype: str, key_index_base: int = 0):
+def quantize(sk, K: np.ndarray, in_dtype: str, key_index_base: int = 0, key_index=None):
     """Quantize keys.  Returns (bits uint32 [n, m/32], norms float64 [n],
     margin float64 [n, m], Y float64 [n, m]).
+
+    Row i's dither counter is key_index_base + i, or key_index[i] when an
+    explicit array of global key indices is given (for sampled rows).
 
     Y = S k (+ rho ||k|| xi), bit = [Y >= 0], norm = ||k||_2 and
     margin = |Y| / (||k|| sqrt(d)): how far a coordinate is from the sign
@@ -82,7 +85,9 @@ def quantize(sk, K: np.ndarray, in_dtype: str, key_index_base: int = 0):
         e = min(n, s + CHUNK)
         Y = project(sk, K[s:e], in_dtype)
         if sk.rho > 0:
-            xi = rng.dither_pairs(sk.seed, np.arange(key_index_base + s, key_index_base + e), m)
+            ids = (np.arange(key_index_base + s, key_index_base + e) if key_index is None
+                   else np.asarray(key_index)[s:e])
+            xi = rng.dither_pairs(sk.seed, ids, m)
             Y = Y + sk.rho * norms[s:e, None] * xi
         bits[s:e] = pack_bits(Y >= 0)
         scale = norms[s:e, None] * math.sqrt(d)

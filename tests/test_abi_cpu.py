@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+validates arguments before touching a GPU, and its host sketch generator
+matches the oracle's independent one bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_jl_amd as qj
+from bit_quantized_jl_amd import _lib
+from oracle import sketch as osk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qjl.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qjl_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = qj.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the shared object's dynamic symbol table lists them (extern "C")
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", qj.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT (qjl_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    for code, name in [(0, "QJL_OK"), (1, "QJL_ERR_INVALID_ARGUMENT"), (2, "QJL_ERR_UNSUPPORTED"),
+                       (3, "QJL_ERR_OUT_OF_MEMORY"), (4, "QJL_ERR_DEVICE")]:
+        assert qj.status_string(code) == name
+    assert qj.status_string(99) == "QJL_ERR_UNKNOWN"
+    assert "gfx950" in qj.version()
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 128, 250, 0, 0.0), 1),      # m % 32 != 0
+    ((0, 128, 0, 0, 0.0), 1),        # m = 0
+    ((0, 0, 256, 0, 0.0), 1),        # d = 0
+    ((0, 128, 256, 7, 0.0), 1),      # bad variant
+    ((0, 128, 256, 0, -0.1), 1),     # rho < 0
+    ((0, 128, 256, 0, float("nan")), 1),
+    ((0, 128, 256, 0, float("inf")), 1),
+    ((0, 1024, 256, 0, 0.0), 2),     # dense d too large
+    ((0, 128, 16384, 0, 0.0), 2),    # m too large
+    ((0, 96, 192, 1, 0.0), 2),       # FQJL d not a power of two
+    ((0, 128, 320, 1, 0.0), 2),      # FQJL m % d != 0
+    ((0, 4, 32, 1, 0.0), 2),         # FQJL d < 8
+    ((0, 256, 512, 1, 0.0), 2),      # FQJL d > 128
+])
+def test_make_sketch_validation(args, expect):
+    lib = qj.load()
+    out = ctypes.c_void_p(123)
+    st = lib.qjl_make_sketch(*args, ctypes.byref(out))
+    assert st == expect
+    assert out.value is None
+
+
+def test_make_sketch_null_out_and_no_gpu():
+    lib = qj.load()
+    assert lib.qjl_make_sketch(0, 128, 256, 0, 0.0, None) == 1
+    import torch
+    if not torch.cuda.is_available():
+        out = ctypes.c_void_p()
+        assert lib.qjl_make_sketch(0, 128, 256, 0, 0.0, ctypes.byref(out)) == qj.ERR_DEVICE
+        assert out.value is None
+
+
+def test_null_handles_rejected():
+    lib = qj.load()
+    assert lib.qjl_destroy_sketch(None) == 1
+    assert lib.qjl_sketch_info(None, None, None, None, None, None, None) == 1
+    assert lib.qjl_sketch_export(None, None, None) == 1
+    assert lib.qjl_quantize_keys(None, None, 1, 4, 0, None, None, None) == 1
+    assert lib.qjl_project_query(None, None, 1, 4, None, None) == 1
+    assert lib.qjl_score(None, None, None, None, 1, 1, 1, None, None) == 1
+
+
+@pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (0, 128, 512), (7, 16, 32), (3, 100, 64)])
+def test_host_dense_sketch_equals_oracle(seed, d, m):
+    got = qj.generate_sketch_host(seed, d, m, "dense")
+    ref = osk.make_dense(seed, d, m)
+    assert np.array_equal(got["S_f32"].astype(np.float64), ref.S32)
+    assert np.array_equal(got["S_bf16"], osk.bf16_bits(ref.S16))
+
+
+@pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (5, 8, 32), (9, 64, 192), (2, 128, 512)])
+def test_host_fqjl_params_equal_oracle(seed, d, m):
+    got = qj.generate_sketch_host(seed, d, m, "fqjl")
+    ref = osk.make_fqjl(seed, d, m)
+    assert np.array_equal(got["D"].astype(np.float64), ref.D)
+    assert np.array_equal(got["P"].astype(np.int64), ref.P)
+    assert np.array_equal(got["G"].astype(np.float64), ref.G)
+
+
+def test_host_generation_validates():
+    with pytest.raises(qj.QJLError) as e:
+        qj.generate_sketch_host(0, 128, 100, "dense")
+    assert e.value.status == qj.ERR_INVALID_ARGUMENT
+    with pytest.raises(qj.QJLError) as e:
+        qj.generate_sketch_host(0, 96, 192, "fqjl")
+    assert e.value.status == qj.ERR_UNSUPPORTED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises((ValueError, RuntimeError, qj.QJLError)):
+        sk = _lib.Sketch(0, 0, 128, 256, "dense", 0.0)
+        qj.quantize_keys(sk, torch.zeros(4, 128))

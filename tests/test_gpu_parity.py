@@ -1,0 +1,296 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Small and medium shapes are checked element by element; the full-size
+workloads (run in the same launch configuration the benchmark times) are
+checked on sampled rows that the oracle recomputes one by one.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_jl_amd as qj
+import workloads as wl
+from gpu_helpers import (bits_np, check_bits, check_norms, check_projection, check_scores,
+                         to_np_f64)
+from oracle import qjl as oq
+from oracle import sketch as osk
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def note(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+_osk_cache: dict = {}
+
+
+def oracle_sketch(seed, d, m, variant, rho):
+    key = (seed, d, m, variant, rho)
+    if key not in _osk_cache:
+        _osk_cache[key] = osk.make_sketch(seed, d, m, variant, rho)
+    return _osk_cache[key]
+
+
+def run_quantize_case(w: wl.Workload, n_k: int | None = None, base: int = 0):
+    note("quantize", w.name, w.d, w.m, w.variant, w.dtype, w.rho, n_k)
+    K = wl.make_keys(w, "cpu", n_k=n_k).to(DEV)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    norms, bits = qj.quantize_keys(sk, K, key_index_base=base)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    Kd = to_np_f64(K)
+    rb, rn, mg, _ = oq.quantize(ref, Kd, w.dtype, key_index_base=base)
+    nband = check_bits(bits_np(bits), rb, mg, w.m)
+    check_norms(to_np_f64(norms), rn)
+    sk.close()
+    return nband, K, bits, norms
+
+
+QUANT_CASES = [
+    wl.TINY,
+    wl.DECODE_7B.scaled(batch=1, heads=4, n_k=1000),
+    wl.LONG_CTX.scaled(heads=2, n_k=1531),
+    wl.PREFILL.scaled(batch=1, heads=3, n_k=777),
+    wl.FQJL_7B.scaled(batch=1, heads=2, n_k=1000),
+    wl.FQJL_7B_DITHER.scaled(batch=1, heads=2, n_k=1000),
+]
+
+
+@pytest.mark.parametrize("w", QUANT_CASES, ids=lambda w: w.name)
+def test_quantize_workloads_scaled(w):
+    nband, *_ = run_quantize_case(w)
+    note("in-band sign differences:", nband)
+
+
+SHAPES = (
+    [("dense", d, m, dt, 0.0) for d in (16, 64, 100, 128, 256) for m in (32, 96, 512)
+     for dt in ("f32", "bf16")]
+    + [("dense", 128, 256, "bf16", 0.5), ("dense", 64, 128, "f32", 0.1)]
+    + [("fqjl", d, m, dt, rho) for (d, m) in ((8, 32), (16, 32), (16, 64), (32, 32), (32, 96),
+                                              (64, 64), (64, 256), (128, 128), (128, 512))
+       for dt in ("f32", "bf16") for rho in (0.0, 0.3)]
+)
+
+
+@pytest.mark.parametrize("variant,d,m,dt,rho", SHAPES)
+def test_quantize_shapes(variant, d, m, dt, rho):
+    w = wl.Workload(f"shape_{variant}_{d}_{m}_{dt}_{rho}", d, m, variant, 1, 1, 203, 5, dt,
+                    "normal", rho, seed=3)
+    run_quantize_case(w, base=11)
+
+
+@pytest.mark.parametrize("variant,d,m,dt", [("dense", 128, 256, "f32"), ("dense", 128, 256, "bf16"),
+                                            ("dense", 100, 96, "bf16"), ("dense", 16, 512, "f32"),
+                                            ("fqjl", 128, 256, "bf16"), ("fqjl", 8, 32, "f32"),
+                                            ("fqjl", 64, 192, "f32"), ("fqjl", 128, 512, "bf16")])
+def test_project_query(variant, d, m, dt):
+    note("project", variant, d, m, dt)
+    w = wl.Workload("proj", d, m, variant, 1, 1, 1, 37, dt, seed=5)
+    q = wl.make_queries(w, "cpu").to(DEV)
+    sk = qj.make_sketch(5, d, m, variant)
+    Sq = qj.project_query(sk, q)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(5, d, m, variant, 0.0)
+    qd = to_np_f64(q)
+    check_projection(to_np_f64(Sq), oq.project(ref, qd, dt), qd, m)
+    sk.close()
+
+
+@pytest.mark.parametrize("m,G,nq,nk", [(256, 1, 16, 4096), (256, 3, 1, 1000), (512, 2, 1, 777),
+                                       (32, 2, 3, 65), (96, 1, 2, 130), (1024, 1, 1, 300),
+                                       (128, 5, 4, 17), (256, 2, 7, 1), (2048, 1, 2, 64)])
+def test_score_random_bits(m, G, nq, nk):
+    note("score", m, G, nq, nk)
+    rs = np.random.default_rng(m + G + nq + nk)
+    sk = qj.make_sketch(0, 128, m, "dense", 0.0)
+    bits = wl.make_random_bits(G * nk, m, seed=7).to(DEV)
+    norms = torch.from_numpy(np.abs(rs.standard_normal(G * nk)).astype(np.float32) * 10).to(DEV)
+    Sq = torch.from_numpy((rs.standard_normal((G * nq, m)) * 11).astype(np.float32)).to(DEV)
+    out = qj.score(sk, Sq, bits, norms, G, nq, nk)
+    torch.cuda.synchronize()
+    ref = oq.score(to_np_f64(Sq), bits_np(bits), to_np_f64(norms), m, 0.0, G, nq, nk)
+    check_scores(to_np_f64(out), ref)
+    sk.close()
+
+
+def test_score_dither_constant():
+    # rho enters the score only through sqrt(1 + rho^2)
+    m, G, nq, nk = 256, 1, 2, 300
+    rs = np.random.default_rng(1)
+    sk = qj.make_sketch(0, 128, m, "fqjl", 0.7)
+    bits = wl.make_random_bits(G * nk, m, seed=9).to(DEV)
+    norms = torch.ones(G * nk, device=DEV)
+    Sq = torch.from_numpy(rs.standard_normal((nq, m)).astype(np.float32)).to(DEV)
+    out = qj.score(sk, Sq, bits, norms, G, nq, nk)
+    ref = oq.score(to_np_f64(Sq), bits_np(bits), to_np_f64(norms), m, 0.7, G, nq, nk)
+    check_scores(to_np_f64(out), ref)
+
+
+@pytest.mark.parametrize("w", [wl.TINY, wl.DECODE_7B.scaled(batch=1, heads=2, n_k=999),
+                               wl.FQJL_7B_DITHER.scaled(batch=1, heads=2, n_k=500)],
+                         ids=lambda w: w.name)
+def test_end_to_end_scores(w):
+    note("e2e", w.name)
+    _, K, bits, norms = run_quantize_case(w)
+    q = wl.make_queries(w, "cpu").to(DEV)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    Sq = qj.project_query(sk, q)
+    out = qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    Sq_ref = oq.project(ref, to_np_f64(q), w.dtype)
+    _, rn, _, _ = oq.quantize(ref, to_np_f64(K[:1]), w.dtype)
+    s_ref = oq.score(Sq_ref, bits_np(bits), to_np_f64(norms), w.m, w.rho, w.groups, w.n_q, w.n_k)
+    check_scores(to_np_f64(out), s_ref)
+    sk.close()
+
+
+def test_zero_key_and_empty_calls():
+    note("edge zero/empty")
+    for variant, dt in (("dense", torch.float32), ("dense", torch.bfloat16), ("fqjl", torch.bfloat16)):
+        sk = qj.make_sketch(0, 128, 256, variant, 0.2)
+        K = torch.zeros(70, 128, dtype=dt, device=DEV)
+        norms, bits = qj.quantize_keys(sk, K)
+        torch.cuda.synchronize()
+        assert np.all(bits_np(bits) == 0xFFFFFFFF)
+        assert float(norms.abs().max()) == 0.0
+        Sq = qj.project_query(sk, torch.randn(1, 128, device=DEV).to(dt))
+        s = qj.score(sk, Sq, bits, norms, 1, 1, 70)
+        torch.cuda.synchronize()
+        assert float(s.abs().max()) == 0.0
+        lib = qj.load()
+        assert lib.qjl_quantize_keys(sk.handle, None, 1, 0, 0, None, None, None) == 0
+        assert lib.qjl_project_query(sk.handle, None, 1, 0, None, None) == 0
+        assert lib.qjl_score(sk.handle, None, None, None, 0, 1, 1, None, None) == 0
+        assert lib.qjl_score(sk.handle, None, None, None, 1, 1, 0, None, None) == 0
+        sk.close()
+
+
+def test_invalid_arguments_on_gpu():
+    note("edge invalid")
+    sk = qj.make_sketch(0, 128, 256, "dense")
+    lib = qj.load()
+    K = torch.zeros(8, 128, dtype=torch.bfloat16, device=DEV)
+    nrm = torch.zeros(8, device=DEV)
+    bits = torch.zeros(8, 8, dtype=torch.int32, device=DEV)
+    p = K.data_ptr()
+    assert lib.qjl_quantize_keys(sk.handle, p + 1, 1, 8, 0, nrm.data_ptr(), bits.data_ptr(), None) == 1
+    assert lib.qjl_quantize_keys(sk.handle, p, 5, 8, 0, nrm.data_ptr(), bits.data_ptr(), None) == 1
+    assert lib.qjl_quantize_keys(sk.handle, p, 1, -1, 0, nrm.data_ptr(), bits.data_ptr(), None) == 1
+    assert lib.qjl_quantize_keys(sk.handle, p, 1, 8, -5, nrm.data_ptr(), bits.data_ptr(), None) == 1
+    assert lib.qjl_quantize_keys(sk.handle, p, 1, 8, 0, nrm.data_ptr() + 2, bits.data_ptr(), None) == 1
+    assert lib.qjl_score(sk.handle, nrm.data_ptr(), bits.data_ptr(), nrm.data_ptr(), 1, -1, 1,
+                         nrm.data_ptr(), None) == 1
+    sk.close()
+    assert sk._h.value is None
+
+
+def test_sketch_export_matches_oracle():
+    note("export")
+    for (d, m) in ((128, 256), (128, 512), (100, 64)):
+        sk = qj.make_sketch(0, d, m, "dense")
+        s32, s16 = qj.sketch_export(sk, bf16=True)
+        ref = oracle_sketch(0, d, m, "dense", 0.0)
+        assert np.array_equal(s32.astype(np.float64), ref.S32)
+        assert np.array_equal(s16, osk.bf16_bits(ref.S16))
+        assert sk.info()["device"] == 0
+        sk.close()
+    for (d, m) in ((128, 256), (16, 64)):
+        sk = qj.make_sketch(0, d, m, "fqjl")
+        s32, _ = qj.sketch_export(sk)
+        E = oracle_sketch(0, d, m, "fqjl", 0.0).explicit()
+        assert np.allclose(s32, E, rtol=1e-6, atol=1e-6 * np.abs(E).max())
+        sk.close()
+
+
+def test_dither_key_index_base_appends():
+    note("dither base")
+    w = wl.FQJL_7B_DITHER.scaled(batch=1, heads=1, n_k=300)
+    K = wl.make_keys(w, "cpu").to(DEV)
+    sk = qj.make_sketch(0, 128, 256, "fqjl", 0.1)
+    _, whole = qj.quantize_keys(sk, K, key_index_base=1000)
+    _, a = qj.quantize_keys(sk, K[:123].contiguous(), key_index_base=1000)
+    _, b = qj.quantize_keys(sk, K[123:].contiguous(), key_index_base=1123)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, torch.cat([a, b]))
+    sk.close()
+
+
+# ---------------------------------------------------------------- full size
+def _sample_rows(n, count, seed):
+    rs = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                    rs.choice(n, count, replace=False)]))
+    return idx
+
+
+def full_size_quantize(w: wl.Workload, sample=3000):
+    note("full quantize", w.name)
+    K = wl.make_keys(w, DEV)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    norms, bits = qj.quantize_keys(sk, K)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    idx = _sample_rows(K.shape[0], sample, 1)
+    it = torch.from_numpy(idx).to(DEV)
+    Kd = to_np_f64(K[it])
+    rb, rn, mg, _ = oq.quantize(ref, Kd, w.dtype, key_index=idx)
+    nband = check_bits(bits_np(bits[it]), rb, mg, w.m)
+    check_norms(to_np_f64(norms[it]), rn)
+    note("in-band sign differences on sample:", nband)
+    return sk, K, norms, bits
+
+
+def full_size_score(w: wl.Workload, sk, norms, bits, groups_checked=4):
+    q = wl.make_queries(w, DEV)
+    Sq = qj.project_query(sk, q)
+    out = qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    rs = np.random.default_rng(2)
+    gs = sorted(set([0, w.groups - 1] + rs.choice(w.groups, groups_checked, replace=False).tolist()))
+    for g in gs:
+        sl = slice(g * w.n_k, (g + 1) * w.n_k)
+        qd = to_np_f64(q[g * w.n_q:(g + 1) * w.n_q])
+        Sq_ref = oq.project(ref, qd, w.dtype)
+        check_projection(to_np_f64(Sq[g * w.n_q:(g + 1) * w.n_q]), Sq_ref, qd, w.m)
+        s_ref = oq.score(Sq_ref, bits_np(bits[sl]), to_np_f64(norms[sl]), w.m, w.rho, 1, w.n_q, w.n_k)
+        check_scores(to_np_f64(out[g]), s_ref[0])
+    # every group: finite and zero exactly where the norm is zero
+    assert torch.isfinite(out).all()
+
+
+def test_full_size_decode_7b():
+    w = wl.DECODE_7B
+    sk, K, norms, bits = full_size_quantize(w)
+    del K
+    full_size_score(w, sk, norms, bits)
+    sk.close()
+
+
+def test_full_size_long_context():
+    w = wl.LONG_CTX
+    sk, K, norms, bits = full_size_quantize(w, sample=2000)
+    del K
+    torch.cuda.empty_cache()
+    full_size_score(w, sk, norms, bits, groups_checked=2)
+    sk.close()
+
+
+def test_full_size_prefill():
+    sk, *_ = full_size_quantize(wl.PREFILL)
+    sk.close()
+
+
+@pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER], ids=lambda w: w.name)
+def test_full_size_fqjl(w):
+    sk, K, norms, bits = full_size_quantize(w, sample=2000)
+    del K
+    full_size_score(w, sk, norms, bits, groups_checked=2)
+    sk.close()
