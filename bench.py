@@ -46,7 +46,22 @@ def parse():
                    help="target CPU time for the oracle baseline sample")
     p.add_argument("--skip-extras", action="store_true",
                    help="only the timed step (used under profilers)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, the
+    reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": a.numel() * 4,
+                      "calibrate_copy_bytes_written": a.numel() * 4}), flush=True)
 
 
 def kernel_src_hash() -> str:
@@ -168,6 +183,9 @@ def main():
               "(the kernels work on one GPU's shard; see the sharding note in the design).",
               file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import torch
 
     import bit_quantized_jl_amd as qj
@@ -216,12 +234,23 @@ def main():
     per_step = total_s / args.steps
     q_times = [a.elapsed_time(b) / 1e3 for a, b, _ in evs]
     ps_times = [b.elapsed_time(c) / 1e3 for _, b, c in evs]
-    q_avg = sum(q_times) / len(q_times)
+    q_step_avg = sum(q_times) / len(q_times)
     ps_avg = sum(ps_times) / len(ps_times)
+    # The dominant kernel's launch duration: the same launch repeated back to
+    # back between two HIP events on the library's stream (the per-step events
+    # above also count the event-to-kernel gaps).
+    qa, qb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(args.steps, 10)
+    qa.record(st)
+    for _ in range(reps):
+        qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+    qb.record(st)
+    torch.cuda.synchronize()
+    q_avg = qa.elapsed_time(qb) / 1e3 / reps
 
-    qb = quantize_bytes(w)
+    qbytes = quantize_bytes(w)
     q_flops = 2.0 * w.n_keys * w.d * w.m
-    achieved = qb / q_avg / 1e9
+    achieved = qbytes / q_avg / 1e9
     traffic = read_traffic()
     result = {
         "metric": METRIC,
@@ -242,7 +271,8 @@ def main():
         "roofline": {"kernel": "quantize_mfma_kernel<128,256>", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": qb, "avg_launch_s": q_avg,
+                     "algorithmic_bytes_per_launch": qbytes, "avg_launch_s": q_avg,
+                     "avg_launch_s_in_step": q_step_avg,
                      "mfma_tflops": q_flops / q_avg / 1e12,
                      "mfma_frac_bf16": q_flops / q_avg / 1e12 / BF16_PEAK_TFLOPS},
         "keys_quantized_per_s": w.n_keys / q_avg,

@@ -101,20 +101,29 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
   // Lay out every device array in one allocation.
   const size_t md = (size_t)m * d;
   std::vector<unsigned char> blob;
-  size_t off_a = 0, off_b = 0, off_c = 0, total = 0;
+  size_t off_a = 0, off_b = 0, off_c = 0, off_d = 0, off_e = 0, total = 0;
   try {
     if (variant == QJL_VARIANT_DENSE) {
-      off_a = 0;                                             // S32  float[md]
-      off_b = round_up(off_a + md * 4, 256);                 // S16f float[md]
+      off_a = 0;                                             // S32   float[md]
+      off_b = round_up(off_a + md * 4, 256);                 // S16f  float[md]
       off_c = round_up(off_b + md * 4, 256);                 // S16mfma u16[md]
-      total = round_up(off_c + md * 2, 256);
+      off_d = round_up(off_c + md * 2, 256);                 // S32T  float[md]
+      off_e = round_up(off_d + md * 4, 256);                 // S16fT float[md]
+      total = round_up(off_e + md * 4, 256);
       blob.assign(total, 0);
       std::memcpy(blob.data() + off_a, hs.S32.data(), md * 4);
       float *s16f = reinterpret_cast<float *>(blob.data() + off_b);
+      float *s32t = reinterpret_cast<float *>(blob.data() + off_d);
+      float *s16ft = reinterpret_cast<float *>(blob.data() + off_e);
       for (size_t i = 0; i < md; ++i) {
         const uint32_t u = (uint32_t)hs.S16[i] << 16;
         std::memcpy(&s16f[i], &u, 4);
       }
+      for (int j = 0; j < m; ++j)
+        for (int c = 0; c < d; ++c) {
+          s32t[(size_t)c * m + j] = hs.S32[(size_t)j * d + c];
+          s16ft[(size_t)c * m + j] = s16f[(size_t)j * d + c];
+        }
       build_mfma_b_layout(hs.S16.data(), d, m, reinterpret_cast<uint16_t *>(blob.data() + off_c));
     } else {
       const size_t nbd = (size_t)(m / d) * d;
@@ -151,6 +160,8 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
     sk->S32 = reinterpret_cast<const float *>(base + off_a);
     sk->S16f = reinterpret_cast<const float *>(base + off_b);
     sk->S16mfma = reinterpret_cast<const uint16_t *>(base + off_c);
+    sk->S32T = reinterpret_cast<const float *>(base + off_d);
+    sk->S16fT = reinterpret_cast<const float *>(base + off_e);
   } else {
     sk->Dsign = reinterpret_cast<const uint32_t *>(base + off_a);
     sk->P = reinterpret_cast<const int32_t *>(base + off_b);

@@ -1,6 +1,7 @@
 // Generic dense-sketch kernels: any d <= 512, any m % 32 == 0, float32 or
 // bfloat16 rows, optional dither.  Used for float32 keys, dithered dense
-// sketches, shapes the MFMA kernel does not cover, and query projection.
+// sketches and shapes the MFMA kernel does not cover; and the dense query
+// projection.
 //
 // y_j = sum_c x_c S[j][c] is accumulated in float32 with one fused
 // multiply-add per c, in increasing c.  For quantization the sign bits of 64
@@ -16,11 +17,10 @@ namespace {
 constexpr int GEN_THREADS = 256;
 constexpr int GEN_KEYS = 16;  // rows per block tile
 
-template <typename T, bool PROJECT, bool DITHER>
+template <typename T, bool DITHER>
 __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
     const T *__restrict__ X, const float *__restrict__ S, int d, int m, int64_t n, int64_t base,
-    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
-    float *__restrict__ Y) {
+    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits) {
   extern __shared__ float smem[];
   float *sX = smem;                        // [GEN_KEYS][d]
   float *sNorm = smem + GEN_KEYS * d;      // [GEN_KEYS]
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
       sX[i] = r < nr ? load_as_f32(X, (r0 + r) * (int64_t)d + (i - r * d)) : 0.f;
     }
     __syncthreads();
-    if (!PROJECT && tid < GEN_KEYS) {
+    if (tid < GEN_KEYS) {
       float s = 0.f;
       for (int c = 0; c < d; ++c) s = fmaf(sX[tid * d + c], sX[tid * d + c], s);
       const float nrm = sqrtf(s);
@@ -58,21 +58,16 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
           for (int r = 0; r < GEN_KEYS; ++r) acc[r] = fmaf(sX[r * d + c], s, acc[r]);
         }
       }
-      if (PROJECT) {
-        if (valid)
-          for (int r = 0; r < nr; ++r) Y[(r0 + r) * (int64_t)m + j] = acc[r];
-      } else {
-        const int w0 = (jb + wave * 64) / 32;  // word of lane 0 in this wave
+      const int w0 = (jb + wave * 64) / 32;  // word of lane 0 in this wave
 #pragma unroll
-        for (int r = 0; r < GEN_KEYS; ++r) {
-          float y = acc[r];
-          if (DITHER && valid) y += (rho * sNorm[r]) * dither_one(dkey, (uint64_t)(base + r0 + r), m, j);
-          const uint64_t msk = __ballot(valid && y >= 0.f);
-          if (r < nr) {
-            uint32_t *brow = bits + (r0 + r) * (int64_t)W;
-            if (lane == 0 && w0 < W) brow[w0] = (uint32_t)msk;
-            if (lane == 32 && w0 + 1 < W) brow[w0 + 1] = (uint32_t)(msk >> 32);
-          }
+      for (int r = 0; r < GEN_KEYS; ++r) {
+        float y = acc[r];
+        if (DITHER && valid) y += (rho * sNorm[r]) * dither_one(dkey, (uint64_t)(base + r0 + r), m, j);
+        const uint64_t msk = __ballot(valid && y >= 0.f);
+        if (r < nr) {
+          uint32_t *brow = bits + (r0 + r) * (int64_t)W;
+          if (lane == 0 && w0 < W) brow[w0] = (uint32_t)msk;
+          if (lane == 32 && w0 + 1 < W) brow[w0 + 1] = (uint32_t)(msk >> 32);
         }
       }
     }
@@ -80,15 +75,15 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
   }
 }
 
-template <typename T, bool PROJECT, bool DITHER>
+template <typename T, bool DITHER>
 hipError_t launch_generic_t(const T *X, const float *S, int d, int m, int64_t n, int64_t base,
-                            float rho, uint64_t dkey, float *norms, uint32_t *bits, float *Y,
+                            float rho, uint64_t dkey, float *norms, uint32_t *bits,
                             hipStream_t st) {
   const int64_t tiles = (n + GEN_KEYS - 1) / GEN_KEYS;
   const int grid = (int)(tiles < 8192 ? tiles : 8192);
   const size_t shmem = (size_t)(GEN_KEYS * d + GEN_KEYS) * sizeof(float);
-  hipLaunchKernelGGL((dense_generic_kernel<T, PROJECT, DITHER>), dim3(grid), dim3(GEN_THREADS),
-                     shmem, st, X, S, d, m, n, base, rho, dkey, norms, bits, Y);
+  hipLaunchKernelGGL((dense_generic_kernel<T, DITHER>), dim3(grid), dim3(GEN_THREADS), shmem, st,
+                     X, S, d, m, n, base, rho, dkey, norms, bits);
   return hipGetLastError();
 }
 
@@ -100,26 +95,59 @@ hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtyp
   const bool dith = h.rho > 0.f;
   if (dtype == QJL_DTYPE_F32) {
     const float *X = static_cast<const float *>(K);
-    return dith ? launch_generic_t<float, false, true>(X, sk->S32, h.d, h.m, n, base, h.rho,
-                                                      sk->dither_key, norms, bits, nullptr, st)
-                : launch_generic_t<float, false, false>(X, sk->S32, h.d, h.m, n, base, h.rho,
-                                                       sk->dither_key, norms, bits, nullptr, st);
+    return dith ? launch_generic_t<float, true>(X, sk->S32, h.d, h.m, n, base, h.rho,
+                                               sk->dither_key, norms, bits, st)
+                : launch_generic_t<float, false>(X, sk->S32, h.d, h.m, n, base, h.rho,
+                                                sk->dither_key, norms, bits, st);
   }
   const uint16_t *X = static_cast<const uint16_t *>(K);
-  return dith ? launch_generic_t<uint16_t, false, true>(X, sk->S16f, h.d, h.m, n, base, h.rho,
-                                                       sk->dither_key, norms, bits, nullptr, st)
-              : launch_generic_t<uint16_t, false, false>(X, sk->S16f, h.d, h.m, n, base, h.rho,
-                                                        sk->dither_key, norms, bits, nullptr, st);
+  return dith ? launch_generic_t<uint16_t, true>(X, sk->S16f, h.d, h.m, n, base, h.rho,
+                                                sk->dither_key, norms, bits, st)
+              : launch_generic_t<uint16_t, false>(X, sk->S16f, h.d, h.m, n, base, h.rho,
+                                                 sk->dither_key, norms, bits, st);
 }
+
+namespace {
+
+// Query projection Sq = q S^T (the QJL abstract's unquantized JL transform of
+// the query).  One block per (query, 256 coordinates); the query row sits in
+// LDS and S is read transposed (S^T[c][j]) so consecutive lanes read
+// consecutive addresses.  Same float32 fused multiply-add order as the
+// quantizer: increasing c.
+template <typename T>
+__global__ __launch_bounds__(256) void project_dense_kernel(const T *__restrict__ q,
+                                                            const float *__restrict__ ST, int d,
+                                                            int m, int64_t n,
+                                                            float *__restrict__ Sq) {
+  __shared__ float sq[QJL_MAX_D];
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    __syncthreads();
+    for (int c = threadIdx.x; c < d; c += 256) sq[c] = load_as_f32(q, i * (int64_t)d + c);
+    __syncthreads();
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j < m) {
+      float acc = 0.f;
+      const float *col = ST + j;
+#pragma unroll 16
+      for (int c = 0; c < d; ++c) acc = fmaf(sq[c], col[(int64_t)c * m], acc);
+      Sq[i * (int64_t)m + j] = acc;
+    }
+  }
+}
+
+}  // namespace
 
 hipError_t launch_project_dense(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
                                 float *Sq, hipStream_t st) {
   const HostSketch &h = sk->host;
+  dim3 grid((unsigned)((h.m + 255) / 256), (unsigned)(n < 65535 ? n : 65535));
   if (dtype == QJL_DTYPE_F32)
-    return launch_generic_t<float, true, false>(static_cast<const float *>(q), sk->S32, h.d, h.m,
-                                                n, 0, 0.f, 0, nullptr, nullptr, Sq, st);
-  return launch_generic_t<uint16_t, true, false>(static_cast<const uint16_t *>(q), sk->S16f, h.d,
-                                                 h.m, n, 0, 0.f, 0, nullptr, nullptr, Sq, st);
+    hipLaunchKernelGGL(project_dense_kernel<float>, grid, dim3(256), 0, st,
+                       static_cast<const float *>(q), sk->S32T, h.d, h.m, n, Sq);
+  else
+    hipLaunchKernelGGL(project_dense_kernel<uint16_t>, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t *>(q), sk->S16fT, h.d, h.m, n, Sq);
+  return hipGetLastError();
 }
 
 }  // namespace qjl

@@ -68,55 +68,266 @@ __device__ __forceinline__ int digit_of(int X, int c) {
   return L;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Wavefront reductions with DPP: row_shr 1, 2, 4, 8 fold each 16-lane row
+// into its lane 15, row_bcast 15 and 31 fold the rows into lane 63, which is
+// then read as a scalar.  Lanes without a DPP source keep the identity.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp(int identity, int v) {
+  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWMASK, 0xf, false);
 }
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  int x = __float_as_int(v);  // v >= 0: max on floats, identity 0
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x111, 0xf>(0, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x112, 0xf>(0, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x114, 0xf>(0, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x118, 0xf>(0, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x142, 0xa>(0, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x143, 0xc>(0, x))));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
+__device__ __forceinline__ int wave_sum(int x) {
+  x += dpp<0x111, 0xf>(0, x);
+  x += dpp<0x112, 0xf>(0, x);
+  x += dpp<0x114, 0xf>(0, x);
+  x += dpp<0x118, 0xf>(0, x);
+  x += dpp<0x142, 0xa>(0, x);
+  x += dpp<0x143, 0xc>(0, x);
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Keys stream through a per-wave LDS ring filled by global_load_lds (the
+// gfx950 direct HBM -> LDS path): no registers are held by loads in flight,
+// so a wave keeps R - 1 stages of 64 keys outstanding while it computes one.
+constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
+
+template <int T>
+struct Ring {
+  static constexpr int R = T <= 2 ? 4 : (T <= 4 ? 3 : 2);  // stages in the ring
+  static constexpr int BITS_BYTES = SM_STAGE * 16 * T;     // 64 keys x 4T words
+  static constexpr int STAGE_BYTES = BITS_BYTES + SM_STAGE * 4;
+  static constexpr int L = T + 1;                          // DMA instructions per stage
+};
+
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int T>
+__device__ __forceinline__ void wait_stages(int pending) {
+  constexpr int L = Ring<T>::L;
+  switch (pending) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    case 2: if constexpr (Ring<T>::R > 2) wait_vmcnt<2 * L>(); break;
+    default: if constexpr (Ring<T>::R > 3) wait_vmcnt<3 * L>(); break;
+  }
+}
+
+// Issue the DMA of one stage: keys [k0, k0 + 64) of the group (keys past kend
+// re-read key kend - 1; their results are never stored).
+template <int T>
+__device__ __forceinline__ void issue_stage(unsigned char *slot, const uint32_t *__restrict__ gbits,
+                                            const float *__restrict__ gnorm, int64_t k0,
+                                            int64_t kend, int lane) {
+  constexpr int W = 4 * T;
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int off = i * 1024 + lane * 16;          // byte offset inside the stage
+    const int kl = off / (W * 4);
+    const int64_t key = (k0 + kl) < kend ? (k0 + kl) : (kend - 1);
+    const uint32_t *src = gbits + key * W + (off % (W * 4)) / 4;
+    __builtin_amdgcn_global_load_lds((const gbl_void_t *)src, (lds_void_t *)(slot + i * 1024), 16,
+                                     0, 0);
+  }
+  const int64_t key = (k0 + lane) < kend ? (k0 + lane) : (kend - 1);
+  __builtin_amdgcn_global_load_lds((const gbl_void_t *)(gnorm + key),
+                                   (lds_void_t *)(slot + Ring<T>::BITS_BYTES), 4, 0, 0);
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() also fences global
+// memory, which would wait for every ring DMA in flight; LDS writes of a wave
+// are complete once its lgkmcnt drains.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)((const lds_u8_t *)p);
+}
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Read one ring stage for this lane: the T words of key 16 u + (lane % 16),
+// lane group lane / 16, for the 4 tiles u, and the 4 norms.  The reads are
+// inline asm that waits for its own results: the ring is written by DMA,
+// which the compiler would otherwise guard with a full vmcnt(0) before every
+// read (the explicit wait_stages() before this call is the real guard).
+template <int T>
+struct StageRead;
+
+template <>
+struct StageRead<1> {
+  uint32_t w[4][1];
+  float n[4];
+  __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
+    asm volatile(
+        "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
+        "ds_read_b32 %2, %8 offset:512\n\tds_read_b32 %3, %8 offset:768\n\t"
+        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
+        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0][0]), "=&v"(w[1][0]), "=&v"(w[2][0]), "=&v"(w[3][0]), "=&v"(n[0]),
+          "=&v"(n[1]), "=&v"(n[2]), "=&v"(n[3])
+        : "v"(aw), "v"(an));
+  }
+};
+
+template <>
+struct StageRead<2> {
+  uint32_t w[4][2];
+  float n[4];
+  __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
+    u32x2_t a, b, c, d;
+    asm volatile(
+        "ds_read_b64 %0, %8\n\tds_read_b64 %1, %8 offset:512\n\t"
+        "ds_read_b64 %2, %8 offset:1024\n\tds_read_b64 %3, %8 offset:1536\n\t"
+        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
+        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]),
+          "=&v"(n[3])
+        : "v"(aw), "v"(an));
+    w[0][0] = a.x; w[0][1] = a.y; w[1][0] = b.x; w[1][1] = b.y;
+    w[2][0] = c.x; w[2][1] = c.y; w[3][0] = d.x; w[3][1] = d.y;
+  }
+};
+
+template <>
+struct StageRead<4> {
+  uint32_t w[4][4];
+  float n[4];
+  __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
+    u32x4_t a, b, c, d;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
+        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]),
+          "=&v"(n[3])
+        : "v"(aw), "v"(an));
+    const u32x4_t v[4] = {a, b, c, d};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u][0] = v[u].x; w[u][1] = v[u].y; w[u][2] = v[u].z; w[u][3] = v[u].w;
+    }
+  }
+};
+
+template <>
+struct StageRead<8> {
+  uint32_t w[4][8];
+  float n[4];
+  __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
+    u32x4_t a0, a1, b0, b1, c0, c1, d0, d1;
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:16\n\t"
+        "ds_read_b128 %2, %12 offset:2048\n\tds_read_b128 %3, %12 offset:2064\n\t"
+        "ds_read_b128 %4, %12 offset:4096\n\tds_read_b128 %5, %12 offset:4112\n\t"
+        "ds_read_b128 %6, %12 offset:6144\n\tds_read_b128 %7, %12 offset:6160\n\t"
+        "ds_read_b32 %8, %13\n\tds_read_b32 %9, %13 offset:64\n\t"
+        "ds_read_b32 %10, %13 offset:128\n\tds_read_b32 %11, %13 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1), "=&v"(c0), "=&v"(c1), "=&v"(d0),
+          "=&v"(d1), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]), "=&v"(n[3])
+        : "v"(aw), "v"(an));
+    const u32x4_t v[8] = {a0, a1, b0, b1, c0, c1, d0, d1};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u][0] = v[2 * u].x; w[u][1] = v[2 * u].y; w[u][2] = v[2 * u].z; w[u][3] = v[2 * u].w;
+      w[u][4] = v[2 * u + 1].x; w[u][5] = v[2 * u + 1].y;
+      w[u][6] = v[2 * u + 1].z; w[u][7] = v[2 * u + 1].w;
+    }
+  }
+};
 
 template <int T, int QP>
 __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
-    const float *__restrict__ norms, int m, int64_t G, int64_t nq, int64_t nk, int chunk,
-    float cscale, float *__restrict__ out) {
+    const float *__restrict__ norms, int64_t G, int64_t nq, int64_t nk, int chunk, float cscale,
+    float *__restrict__ out) {
+  constexpr int W = 4 * T;         // 32-bit words per key (m = 128 T)
+  constexpr int m = 32 * W;
   constexpr int NQ = 2 * QP;       // queries per pass
-  constexpr int JP = T * 128;      // padded coordinate count
-  __shared__ int sX[NQ][JP];
+  constexpr int R = Ring<T>::R;
+  constexpr int SB = Ring<T>::STAGE_BYTES;
+  __shared__ int sX[NQ][m];
   __shared__ uint4 sA[QP][T][64][2];
   __shared__ int sF[NQ];
   __shared__ int sC[NQ][5];
-  const int W = m / 32;
+  __shared__ __attribute__((aligned(16))) unsigned char sRing[SM_WAVES][R][SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int gq = lane >> 4;  // lane group 0..3
   const int64_t kbeg = (int64_t)blockIdx.x * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
+  // this wave's stages: kbeg + 64 (wave + 4 j), j < ns
+  const int64_t nstage_blk = (kend - kbeg + SM_STAGE - 1) / SM_STAGE;
+  const int ns = (int)((nstage_blk - wave + SM_WAVES - 1) / SM_WAVES);
 
   for (int64_t g = blockIdx.y; g < G; g += gridDim.y) {
+    const uint32_t *gbits = bits + g * nk * (int64_t)W;
+    const float *gnorm = norms + g * nk;
     for (int64_t q0 = 0; q0 < nq; q0 += NQ) {
       const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
-      __syncthreads();
-      // ---- per query: exponent F, fixed-point values, digit sums C_c
-      for (int qi = wave; qi < NQ; qi += SM_WAVES) {
+      // ---- query values to registers first, then start the key DMA so it
+      // overlaps the query set-up (register loads complete before the DMA).
+      constexpr int JL = (m + 63) / 64;
+      float sv[(NQ + SM_WAVES - 1) / SM_WAVES][JL];
+#pragma unroll
+      for (int a = 0; a < (NQ + SM_WAVES - 1) / SM_WAVES; ++a) {
+        const int qi = wave + SM_WAVES * a;
         const bool qv = qi < nqp;
         const float *s = Sq + (g * nq + q0 + (qv ? qi : 0)) * (int64_t)m;
+#pragma unroll
+        for (int b = 0; b < JL; ++b) {
+          const int j = lane + 64 * b;
+          sv[a][b] = (qv && j < m) ? s[j] : 0.f;
+        }
+      }
+      lds_barrier();  // previous pass done with sX / sA (its ring DMA is drained)
+      // ---- per query: exponent F, fixed-point values, digit sums C_c.  This
+      // part reads Sq from global memory and runs before any ring DMA: the
+      // compiler waits for all outstanding loads when it mixes the two kinds.
+#pragma unroll
+      for (int a = 0; a < (NQ + SM_WAVES - 1) / SM_WAVES; ++a) {
+        const int qi = wave + SM_WAVES * a;
+        if (qi >= NQ) continue;
         float amax = 0.f;
-        if (qv)
-          for (int j = lane; j < m; j += 64) amax = fmaxf(amax, fabsf(s[j]));
-        amax = wave_max(amax);
+#pragma unroll
+        for (int b = 0; b < JL; ++b) amax = fmaxf(amax, fabsf(sv[a][b]));
+        amax = wave_max_nonneg(amax);
         int e2 = 0;
         (void)frexpf(amax, &e2);
         const int F = amax > 0.f ? 23 - e2 : 0;
         int C[5] = {0, 0, 0, 0, 0};
-        for (int j = lane; j < JP; j += 64) {
-          int X = 0;
-          if (qv && j < m) X = (int)rintf(ldexpf(s[j], F));
+#pragma unroll
+        for (int b = 0; b < JL; ++b) {
+          const int j = lane + 64 * b;
+          if (j >= m) continue;
+          const int X = (int)rintf(ldexpf(sv[a][b], F));
           sX[qi][j] = X;
           const int wj = (j & 3) == 0 ? 5 : ((j & 3) == 3 ? 0 : 1);
           int rem = X;
@@ -135,35 +346,52 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
           for (int k = 0; k < 5; ++k) sC[qi][k] = C[k];
         }
       }
-      __syncthreads();
-      // ---- A operand fragments (limb rows) in MFMA order
-      for (int idx = tid; idx < QP * T * 64; idx += SM_THREADS) {
-        const int l = idx & 63;
-        const int t = (idx >> 6) % T;
-        const int qp = idx / (64 * T);
-        const int row = l & 15, grp = l >> 4;
-        const int qi = 2 * qp + (row >> 3), c = row & 7;
-        uint32_t wd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (c < 5 && qi < nqp) {
-#pragma unroll
-          for (int e = 0; e < 32; ++e) {
-            // fp8 element e of lane group grp is contraction index k; the fp4
-            // operand holds k as element k % 32 of lane group k / 32.
-            const int k = e < 16 ? 16 * grp + e : 64 + 16 * grp + (e - 16);
-            const int gb = k >> 5, eb = k & 31;
-            const int wi = T * gb + t;
-            if (wi < W) {
-              const int s = eb >> 3;
-              const int j = 32 * wi + 4 * (eb & 7) + s;
-              const int f = s == 0 ? 4 : (s == 1 ? 2 : (s == 2 ? 1 : -1));
-              wd[e >> 2] |= e4m3_of_int(f * digit_of(sX[qi][j], c)) << (8 * (e & 3));
-            }
-          }
-        }
-        sA[qp][t][l][0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-        sA[qp][t][l][1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+      // ---- A operand (limb rows) in MFMA order: zero, then one task per
+      // (pair, slot, lane group, pair member, byte) writes its five limb bytes.
+      {
+        uint4 *z = &sA[0][0][0][0];
+        for (int i = tid; i < QP * T * 64 * 2; i += SM_THREADS) z[i] = make_uint4(0, 0, 0, 0);
       }
-      __syncthreads();
+      lds_barrier();
+      // Start the key stream now: the limb build below touches only LDS.  The
+      // first R - 1 stages are issued unconditionally (a stage past the wave's
+      // range re-reads clamped, valid keys and is never consumed), so the
+      // number of loads in flight is static.
+#pragma unroll
+      for (int j = 0; j < R - 1; ++j)
+        issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
+                       kend, lane);
+      unsigned char *sAb = reinterpret_cast<unsigned char *>(&sA[0][0][0][0]);
+      for (int idx = tid; idx < QP * T * 4 * 2 * 32; idx += SM_THREADS) {
+        const int e = idx & 31;
+        const int qq = (idx >> 5) & 1;
+        const int grp = (idx >> 6) & 3;
+        const int t = (idx >> 8) % T;
+        const int qp = idx / (256 * T);
+        const int qi = 2 * qp + qq;
+        if (qi >= nqp) continue;
+        // fp8 byte e of lane group grp is contraction index k; the fp4 bits
+        // operand holds k as element k % 32 of lane group k / 32.
+        const int k = e < 16 ? 16 * grp + e : 64 + 16 * grp + (e - 16);
+        const int gb = k >> 5, eb = k & 31;
+        const int wi = T * gb + t;
+        const int sreg = eb >> 3;
+        const int j = 32 * wi + 4 * (eb & 7) + sreg;
+        const int f = sreg == 0 ? 4 : (sreg == 1 ? 2 : (sreg == 2 ? 1 : -1));
+        int rem = sX[qi][j];
+        int L[5];
+#pragma unroll
+        for (int c = 4; c >= 0; --c) {
+          L[c] = ((rem + 16) & 31) - 16;
+          rem = (rem - L[c]) >> 5;
+        }
+#pragma unroll
+        for (int c = 0; c < 5; ++c) {
+          const int l = (8 * qq + c) + 16 * grp;
+          sAb[(((qp * T + t) * 64 + l) * 32) + e] = (unsigned char)e4m3_of_int(f * L[c]);
+        }
+      }
+      lds_barrier();
       v8i_t A[QP][T];
 #pragma unroll
       for (int qp = 0; qp < QP; ++qp)
@@ -193,41 +421,51 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         }
         qscale[qp] = qv ? ldexpf(cscale, -sF[qi]) : 0.f;
       }
-      // ---- stream the keys: 16 per MFMA tile, tiles round-robin over waves
-      const uint32_t *gbits = bits + g * nk * (int64_t)W;
-      const float *gnorm = norms + g * nk;
-      for (int64_t k0 = kbeg + 16 * wave; k0 < kend; k0 += 16 * SM_WAVES) {
-        const int64_t key = k0 + (lane & 15);
-        const bool kv = key < kend;
-        uint32_t wb[T];
-        const uint32_t *src = gbits + key * (int64_t)W + T * gq;
+      // ---- stream this wave's stages through the ring
+      for (int j = 0; j < ns; ++j) {
+        if (j + R - 1 < ns)
+          issue_stage<T>(&sRing[wave][(j + R - 1) % R][0], gbits, gnorm,
+                         kbeg + SM_STAGE * (wave + SM_WAVES * (j + R - 1)), kend, lane);
+        // stages issued after stage j: up to the last real one, and at least
+        // the R - 2 issued before the loop
+        const int last = (ns - 1) < (j + R - 1) ? (ns - 1) : (j + R - 1);
+        wait_stages<T>((last > R - 2 ? last : R - 2) - j);
+        const unsigned char *slot = &sRing[wave][j % R][0];
+        const int64_t k0 = kbeg + SM_STAGE * (wave + SM_WAVES * j);
+        StageRead<T> sr;
+        sr.read(lds_address(slot + ((lane & 15) * W + T * gq) * 4),
+                lds_address(slot + Ring<T>::BITS_BYTES + (lane & 15) * 4));
 #pragma unroll
-        for (int i = 0; i < T; ++i) wb[i] = (kv && T * gq + i < W) ? src[i] : 0u;
-        const float nrm = kv ? gnorm[key] : 0.f;
-        v4f_t acc[QP];
+        for (int u = 0; u < SM_STAGE / 16; ++u) {
+          const int kl = 16 * u + (lane & 15);
+          const int64_t key = k0 + kl;
+          const uint32_t *wb = sr.w[u];
+          const float nrm = sr.n[u];
+          v4f_t acc[QP];
 #pragma unroll
-        for (int qp = 0; qp < QP; ++qp) acc[qp] = cinit[qp];
+          for (int qp = 0; qp < QP; ++qp) acc[qp] = cinit[qp];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const uint32_t w = wb[t];
-          const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
-                                (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
-                                0, 0, 0, 0};
+          for (int t = 0; t < T; ++t) {
+            const uint32_t w = wb[t];
+            const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
+                                  (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
+                                  0, 0, 0, 0};
 #pragma unroll
-          for (int qp = 0; qp < QP; ++qp)
-            acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qp][t], B, acc[qp], 0, 4,
-                                                                        0, 127, 0, 127);
-        }
+            for (int qp = 0; qp < QP; ++qp)
+              acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qp][t], B, acc[qp], 0,
+                                                                          4, 0, 127, 0, 127);
+          }
 #pragma unroll
-        for (int qp = 0; qp < QP; ++qp) {
-          float e = acc[qp][0] * wgt[0];
-          e = fmaf(acc[qp][1], wgt[1], e);
-          e = fmaf(acc[qp][2], wgt[2], e);
-          e = fmaf(acc[qp][3], wgt[3], e);
-          e += __shfl_xor(e, 16);
-          const int qi = 2 * qp + (gq >> 1);
-          if ((gq & 1) == 0 && kv && qi < nqp)
-            out[(g * nq + q0 + qi) * nk + key] = (e * qscale[qp]) * nrm;
+          for (int qp = 0; qp < QP; ++qp) {
+            float e = acc[qp][0] * wgt[0];
+            e = fmaf(acc[qp][1], wgt[1], e);
+            e = fmaf(acc[qp][2], wgt[2], e);
+            e = fmaf(acc[qp][3], wgt[3], e);
+            e += __shfl_xor(e, 16);
+            const int qi = 2 * qp + (gq >> 1);
+            if ((gq & 1) == 0 && key < kend && qi < nqp)
+              out[(g * nq + q0 + qi) * nk + key] = (e * qscale[qp]) * nrm;
+          }
         }
       }
     }
@@ -237,10 +475,12 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
 template <int T, int QP>
 hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, int m, int64_t G,
                      int64_t nq, int64_t nk, float c, float *scores, hipStream_t st) {
+  (void)m;
+  // chunk: a multiple of the 256 keys one block step covers
   int64_t chunk = 2048;
   while (chunk > 256 && G * ((nk + chunk - 1) / chunk) < 1024) chunk /= 2;
   dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
-  hipLaunchKernelGGL((score_mfma_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms, m,
+  hipLaunchKernelGGL((score_mfma_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms,
                      G, nq, nk, (int)chunk, c, scores);
   return hipGetLastError();
 }
@@ -265,9 +505,11 @@ hipError_t launch_score(const qjl_sketch *sk, const float *Sq, const uint32_t *b
                         const float *norms, int64_t G, int64_t nq, int64_t nk, float *scores,
                         hipStream_t st) {
   const int m = sk->host.m;
-  if (m > 1024) return launch_score_generic(sk, Sq, bits, norms, G, nq, nk, scores, st);
+  // the MFMA path covers m = 128 T, T <= 8, with 16-byte aligned bits
+  if (m > 1024 || m % 128 != 0 || ((uintptr_t)bits & 15) != 0)
+    return launch_score_generic(sk, Sq, bits, norms, G, nq, nk, scores, st);
   const int W = m / 32;
-  const int T = (W + 3) / 4;
+  const int T = W / 4;
   const int qp_max = T <= 2 ? 8 : (T <= 4 ? 4 : 2);
   int qp = 1;
   while (qp < qp_max && 2 * qp < nq) qp *= 2;
@@ -275,14 +517,10 @@ hipError_t launch_score(const qjl_sketch *sk, const float *Sq, const uint32_t *b
   switch (T) {
     case 1: return launch_sm_t<1>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
     case 2: return launch_sm_t<2>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
-    case 3: return launch_sm_t<3>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
     case 4: return launch_sm_t<4>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
-    case 5: return launch_sm_t<5>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
-    case 6: return launch_sm_t<6>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
-    case 7: return launch_sm_t<7>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
     case 8: return launch_sm_t<8>(qp, Sq, bits, norms, m, G, nq, nk, c, scores, st);
   }
-  return hipErrorInvalidValue;
+  return launch_score_generic(sk, Sq, bits, norms, G, nq, nk, scores, st);
 }
 
 }  // namespace qjl

@@ -61,6 +61,8 @@ struct qjl_sketch {
   const float *S32 = nullptr;    // m*d  float32 S (row-major)
   const float *S16f = nullptr;   // m*d  bfloat16-rounded S widened to float32 (row-major)
   const uint16_t *S16mfma = nullptr;  // m*d bf16 in the MFMA B-operand order (see k_quantize_mfma)
+  const float *S32T = nullptr;   // d*m  float32 S transposed (column j of row c at c*m + j)
+  const float *S16fT = nullptr;  // d*m  bfloat16-rounded S transposed, widened to float32
   // FQJL
   const uint32_t *Dsign = nullptr;    // nb*d sign masks: 0 (D=+1) or 0x80000000 (D=-1)
   const int32_t *P = nullptr;         // nb*d
