@@ -476,9 +476,24 @@ template <int T, int QP>
 hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, int m, int64_t G,
                      int64_t nq, int64_t nk, float c, float *scores, hipStream_t st) {
   (void)m;
+  // One resident round: size the chunks so the grid is (about) the number of
+  // workgroups the chip holds at once, so no partial second round idles CUs.
+  static int resident = 0;
+  if (resident == 0) {
+    int dev = 0, cus = 256, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<T, QP>,
+                                                     SM_THREADS, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    resident = cus * per_cu;
+  }
   // chunk: a multiple of the 256 keys one block step covers
-  int64_t chunk = 2048;
-  while (chunk > 256 && G * ((nk + chunk - 1) / chunk) < 1024) chunk /= 2;
+  int64_t chunk = (G * nk + resident - 1) / resident;
+  chunk = (chunk + 255) / 256 * 256;
   dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
   hipLaunchKernelGGL((score_mfma_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms,
                      G, nq, nk, (int)chunk, c, scores);
