@@ -102,6 +102,12 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 // gfx950 direct HBM -> LDS path): no registers are held by loads in flight,
 // so a wave keeps R - 1 stages of 64 keys outstanding while it computes one.
 constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
+#ifndef QJL_SM_EARLY_DMA
+#define QJL_SM_EARLY_DMA 0      // issue the first ring stages before the query set-up
+#endif
+// The first R - 1 stages are issued unconditionally (a stage past the wave's
+// range re-reads clamped, valid keys and is never consumed), so the number of
+// loads in flight is static when the loop starts.
 
 template <int T>
 struct Ring {
@@ -307,10 +313,19 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
           sv[a][b] = (qv && j < m) ? s[j] : 0.f;
         }
       }
-      lds_barrier();  // previous pass done with sX / sA (its ring DMA is drained)
-      // ---- per query: exponent F, fixed-point values, digit sums C_c.  This
-      // part reads Sq from global memory and runs before any ring DMA: the
-      // compiler waits for all outstanding loads when it mixes the two kinds.
+#if QJL_SM_EARLY_DMA
+      // Start the key stream together with the query loads: the compiler waits
+      // for every outstanding load before the query values are used, so the
+      // first stages land within the same memory latency.  Each wave's ring is
+      // its own and its previous pass is fully consumed, so this is safe
+      // before the barrier.
+#pragma unroll
+      for (int j = 0; j < R - 1; ++j)
+        issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
+                       kend, lane);
+#endif
+      lds_barrier();  // previous pass done with sX / sA
+      // ---- per query: exponent F, fixed-point values, digit sums C_c
 #pragma unroll
       for (int a = 0; a < (NQ + SM_WAVES - 1) / SM_WAVES; ++a) {
         const int qi = wave + SM_WAVES * a;
@@ -353,14 +368,13 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         for (int i = tid; i < QP * T * 64 * 2; i += SM_THREADS) z[i] = make_uint4(0, 0, 0, 0);
       }
       lds_barrier();
-      // Start the key stream now: the limb build below touches only LDS.  The
-      // first R - 1 stages are issued unconditionally (a stage past the wave's
-      // range re-reads clamped, valid keys and is never consumed), so the
-      // number of loads in flight is static.
+#if !QJL_SM_EARLY_DMA
+      // Start the key stream now: the limb build below touches only LDS.
 #pragma unroll
       for (int j = 0; j < R - 1; ++j)
         issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
                        kend, lane);
+#endif
       unsigned char *sAb = reinterpret_cast<unsigned char *>(&sA[0][0][0][0]);
       for (int idx = tid; idx < QP * T * 4 * 2 * 32; idx += SM_THREADS) {
         const int e = idx & 31;
