@@ -2,17 +2,17 @@
 //
 // Computes, for bfloat16 keys, Y = K S^T with v_mfma_f32_32x32x16_bf16
 // (float32 accumulation; bf16 x bf16 products are exact), and fuses in
-// registers: the sign test, packing of the signs into 32-bit words with a
-// wavefront ballot, and the key norm ||k||.  This is the QJL abstract's
-// "JL transform followed by sign-bit quantization" with a dense Gaussian S.
+// registers: the sign test, packing of the signs into 32-bit words, and the
+// key norm ||k||.  This is the QJL abstract's "JL transform followed by
+// sign-bit quantization" with a dense Gaussian S.
 //
 // Tiling.  A workgroup keeps the whole bf16 sketch in LDS (m*d*2 bytes: 64 KB
 // at d=128, m=256) and its waves stream keys.  S is the MFMA A operand (rows
 // are sketch coordinates), keys the B operand (columns): one wave owns 64 keys
 // (two 32-key column tiles).  Each lane loads its key fragment straight from
-// HBM: lane (c, h) = (lane % 32, lane / 32) holds the contiguous half h of key
-// c (d/2 bf16 = d bytes), and MFMA step t contracts elements [8t, 8t+8) of
-// both halves.  The contraction index is therefore a permutation of the key
+// HBM: lane (c, h) = (lane % 32, lane / 32) holds half of the 16-byte chunks
+// of key c (qm_chunk says which), and MFMA step t contracts one chunk from
+// each lane half.  The contraction index is therefore a permutation of the key
 // dimension; the S fragments use the same permutation, which the host bakes
 // into the LDS image of S (build_mfma_b_layout), so every S fragment is one
 // conflict-free ds_read_b128.
@@ -27,18 +27,35 @@
 // key of norm 0 (all products zero) is written as all ones, so a zero of
 // either sign counts as non-negative.  Lane (c, h) ends up with words
 // [h W/2, (h+1) W/2) of key c and stores them contiguously.
+//
+// Schedule.  The W passes of a tile (one 32-coordinate tile each) run as
+// T = d/16 MFMA steps; the S fragments stream from LDS through a ring of
+// QM_RING registers refilled one step at a time, and, where registers allow,
+// the sign bits of pass q - 1 are packed a few per step while pass q runs so
+// that the VALU packing overlaps the matrix cores.  Bits and norms are
+// written with non-temporal stores: a later kernel reads them, this one does
+// not, and streaming them past the caches measured markedly faster.
 #include "device_common.h"
 
 namespace qjl {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// The 16-byte chunk (8 bf16 values) of a key that lane half h feeds to MFMA
+// step t: the two lanes of a key read adjacent chunks in the same load
+// instruction, so one instruction covers 32 contiguous bytes of each of its
+// 32 key rows.
+__host__ __device__ constexpr int qm_chunk(int h, int t) { return 2 * t + h; }
 
 // Host: write S (bf16 bits, m x d row-major) in the operand order used by
 // quantize_mfma_kernel.  Tile tau = 2 p + s (p < W/2 word pairs, s < 2),
 // row r = 8 a + 4 h + b of the tile is coordinate 32 (p + h W/2) + 16 s + 4 a + b;
 // for tile tau, step t and lane l = r + 32 hh the 8 values
-// S[row][hh d/2 + 8 t + e], e < 8, are contiguous.
+// S[row][8 qm_chunk(hh, t) + e], e < 8, are contiguous.
 void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out) {
   if (d % 16 != 0 || m % 64 != 0) return;  // the MFMA path's shapes; image unused otherwise
   const int T = d / 16, W = m / 32;
@@ -51,37 +68,26 @@ void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out) {
         const int j = 32 * (p + h * (W / 2)) + 16 * s + 4 * a + b;
         for (int e = 0; e < 8; ++e)
           out[(((size_t)tau * T + t) * 64 + l) * 8 + e] =
-              S16[(size_t)j * d + hh * (d / 2) + 8 * t + e];
+              S16[(size_t)j * d + 8 * qm_chunk(hh, t) + e];
       }
   }
 }
 
 namespace {
 
-// Launch shape (compile-time; the defaults are the measured best on MI355X).
-#ifndef QJL_QM_WAVES
-#define QJL_QM_WAVES 4      // waves per workgroup (all share one LDS copy of S)
+#ifndef QJL_QM_RING
+#define QJL_QM_RING 4  // S fragments in flight from LDS
 #endif
-#ifndef QJL_QM_RT
-#define QJL_QM_RT 2         // 32-key column tiles per wave (S fragments reused RT times)
-#endif
-#ifndef QJL_QM_PREFETCH
-#define QJL_QM_PREFETCH 0   // load the next key tile while computing the current one
-#endif
-#ifndef QJL_QM_MINWAVES
-#define QJL_QM_MINWAVES 2   // waves per SIMD the register allocation must allow
-#endif
-constexpr int QM_WAVES = QJL_QM_WAVES;
-constexpr int QM_THREADS = 64 * QM_WAVES;
-constexpr int QM_RT = QJL_QM_RT;
-constexpr int QM_KEYS = 32 * QM_RT;   // keys per wave iteration
+constexpr int QM_RING = QJL_QM_RING;
+constexpr int QM_RT = 2;     // 32-key column tiles per wave (each S fragment feeds 2 MFMAs)
+constexpr int QM_KEYS = 64;  // keys per wave tile
 
 template <int T>
 struct KeyTile {
   bf16x8_t a[QM_RT][T];
 };
 
-// Load the A fragments of the 64 keys starting at k0.  Rows past n re-read
+// Load the B fragments of the 64 keys starting at k0.  Rows past n re-read
 // row n-1 (their results are never stored): the loads stay unconditional, so
 // the compiler can count them and wait only for the tile it needs.
 template <int D>
@@ -92,29 +98,59 @@ __device__ __forceinline__ void load_tile(KeyTile<D / 16> &kt, const uint16_t *_
   for (int rt = 0; rt < QM_RT; ++rt) {
     int64_t row = k0 + 32 * rt + r;
     row = row < n ? row : n - 1;
-    const uint4 *src = reinterpret_cast<const uint4 *>(K + row * D + h * (D / 2));
+    const uint4 *src = reinterpret_cast<const uint4 *>(K + row * D);
 #pragma unroll
-    for (int t = 0; t < T; ++t) kt.a[rt][t] = __builtin_bit_cast(bf16x8_t, src[t]);
+    for (int t = 0; t < T; ++t) kt.a[rt][t] = __builtin_bit_cast(bf16x8_t, src[qm_chunk(h, t)]);
   }
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// S fragment number g of a tile walk: pass q = g / T covers coordinate tile
+// tau = q ^ 1 (s = 1 before s = 0 within a word pair), step t = g % T.
+template <int T>
+__device__ __forceinline__ bf16x8_t s_fragment(const uint4 *sS, int g, int lane) {
+  const int tau = (g / T) ^ 1, t = g % T;
+  return __builtin_bit_cast(bf16x8_t, sS[(tau * T + t) * 64 + lane]);
+}
 
-// Norms, projection, sign packing and stores for one 64-key tile.
-template <int D, int M>
+// Shift the sign bits of acc[v1], acc[v1 - 1], ..., acc[v0] into x.
+template <int V1, int V0>
+__device__ __forceinline__ uint32_t pack_signs(uint32_t x, const floatx16_t &acc) {
+#pragma unroll
+  for (int v = V1; v >= V0; --v) x = __builtin_amdgcn_alignbit(x, __float_as_uint(acc[v]), 31);
+  // Keep the packing here: left alone, the compiler sinks it to the stores
+  // and every pass's accumulators stay live at once.
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Norms, projection, sign packing and stores for one 64-key tile.  With
+// DEFER the bits of pass q - 1 are packed during pass q (one more pair of
+// accumulators live); otherwise each pass is packed when it ends.  A
+// scheduling barrier closes every MFMA step: without it the scheduler hoists
+// all MFMAs of the tile and runs out of registers.  Norms of the two column
+// tiles leave in one 64-lane store (lane half h writes column tile h).
+template <int D, int M, bool DEFER>
 __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const uint4 *sS,
                                              int64_t k0, int64_t n, int lane, int r, int h,
                                              float *__restrict__ norms,
                                              uint32_t *__restrict__ bits) {
   constexpr int T = D / 16;
   constexpr int W = M / 32;
-  // Keep the LDS reads of S inside the tile loop: hoisting all m*d/512 B
-  // fragments into registers would not fit and would spill.
+  constexpr int NF = W * T;    // S fragments per tile walk
+  constexpr int R = QM_RING;
+  constexpr int PER = 16 / T;  // deferred packing steps per MFMA step
+  // The S reads below must stay inside the tile loop: hoisted out of it, all
+  // m*d/512 fragments would be held in registers.
   asm volatile("" ::: "memory");
-  bool zero[QM_RT];
+  bf16x8_t ring[R];
+#pragma unroll
+  for (int g = 0; g < R; ++g) ring[g] = s_fragment<T>(sS, g, lane);
+
+  uint32_t zm[QM_RT];
+  float nrm[QM_RT];
 #pragma unroll
   for (int rt = 0; rt < QM_RT; ++rt) {
-    float s = 0.f;
+    float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const uint4 v = __builtin_bit_cast(uint4, kt.a[rt][t]);
@@ -122,65 +158,101 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w[q]);
-        s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
       }
     }
-    const float tot = s + __shfl_xor(s, 32);
-    zero[rt] = !(tot > 0.f);
-    const int64_t row = k0 + 32 * rt + r;
-    if (h == 0 && row < n) norms[row] = sqrtf(tot);
+    const float tot = acc + __shfl_xor(acc, 32);
+    zm[rt] = tot > 0.f ? 0u : 0xFFFFFFFFu;
+    nrm[rt] = sqrtf(tot);
   }
+  {
+    const int64_t key = k0 + 32 * h + r;
+    if (key < n) __builtin_nontemporal_store(h ? nrm[1] : nrm[0], norms + key);
+  }
+
   uint32_t Wd[QM_RT][W / 2];
+  uint32_t x[QM_RT] = {};
+  floatx16_t prev[QM_RT];
 #pragma unroll
-  for (int p = 0; p < W / 2; ++p) {
-    uint32_t x[QM_RT] = {};
+  for (int q = 0; q < W; ++q) {
+    floatx16_t acc[QM_RT];
 #pragma unroll
-    for (int s = 1; s >= 0; --s) {
-      const int tau = 2 * p + s;
-      asm volatile("" ::: "memory");  // bound the S fragments held in registers to one pass
-      floatx16_t acc[QM_RT];
+    for (int rt = 0; rt < QM_RT; ++rt) acc[rt] = floatx16_t{};
 #pragma unroll
-      for (int rt = 0; rt < QM_RT; ++rt) acc[rt] = floatx16_t{};
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, sS[(tau * T + t) * 64 + lane]);
-#pragma unroll
-        for (int rt = 0; rt < QM_RT; ++rt)
-          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kt.a[rt][t], acc[rt], 0, 0, 0);
-      }
+    for (int t = 0; t < T; ++t) {
+      const int g = q * T + t;
+      const bf16x8_t A = ring[g % R];
 #pragma unroll
       for (int rt = 0; rt < QM_RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kt.a[rt][t], acc[rt], 0, 0, 0);
+      if (g + R < NF) ring[g % R] = s_fragment<T>(sS, g + R, lane);
+      if (DEFER && q > 0) {
 #pragma unroll
-        for (int v = 15; v >= 0; --v)
-          x[rt] = __builtin_amdgcn_alignbit(x[rt], __float_as_uint(acc[rt][v]), 31);
+        for (int rt = 0; rt < QM_RT; ++rt) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k)
+            x[rt] = __builtin_amdgcn_alignbit(x[rt], __float_as_uint(prev[rt][15 - PER * t - k]), 31);
+          asm volatile("" : "+v"(x[rt]));
+        }
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (DEFER) {
+      if (q > 0 && (q - 1) % 2 == 1) {  // pass q - 1 completed word (q - 1) / 2
 #pragma unroll
-    for (int rt = 0; rt < QM_RT; ++rt) Wd[rt][p] = zero[rt] ? 0xFFFFFFFFu : ~x[rt];
+        for (int rt = 0; rt < QM_RT; ++rt) {
+          Wd[rt][(q - 1) / 2] = ~x[rt] | zm[rt];
+          x[rt] = 0;
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < QM_RT; ++rt) prev[rt] = acc[rt];
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < QM_RT; ++rt) {
+        x[rt] = pack_signs<15, 0>(x[rt], acc[rt]);
+        if (q % 2 == 1) {
+          Wd[rt][q / 2] = ~x[rt] | zm[rt];
+          x[rt] = 0;
+        }
+      }
+    }
   }
+  if (DEFER) {
+#pragma unroll
+    for (int rt = 0; rt < QM_RT; ++rt) {
+      x[rt] = pack_signs<15, 0>(x[rt], prev[rt]);
+      Wd[rt][W / 2 - 1] = ~x[rt] | zm[rt];
+    }
+  }
+
 #pragma unroll
   for (int rt = 0; rt < QM_RT; ++rt) {
     const int64_t key = k0 + 32 * rt + r;
     if (key < n) {
       if constexpr ((W / 2) % 4 == 0) {
-        uint4 *dst = reinterpret_cast<uint4 *>(bits + key * W + h * (W / 2));
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(bits + key * W + h * (W / 2));
 #pragma unroll
         for (int q = 0; q < W / 8; ++q)
-          dst[q] = make_uint4(Wd[rt][4 * q], Wd[rt][4 * q + 1], Wd[rt][4 * q + 2],
-                              Wd[rt][4 * q + 3]);
+          __builtin_nontemporal_store(
+              u32x4_t{Wd[rt][4 * q], Wd[rt][4 * q + 1], Wd[rt][4 * q + 2], Wd[rt][4 * q + 3]},
+              dst + q);
       } else {
-        uint2 *dst = reinterpret_cast<uint2 *>(bits + key * W + h * (W / 2));
+        u32x2_t *dst = reinterpret_cast<u32x2_t *>(bits + key * W + h * (W / 2));
 #pragma unroll
-        for (int q = 0; q < W / 4; ++q) dst[q] = make_uint2(Wd[rt][2 * q], Wd[rt][2 * q + 1]);
+        for (int q = 0; q < W / 4; ++q)
+          __builtin_nontemporal_store(u32x2_t{Wd[rt][2 * q], Wd[rt][2 * q + 1]}, dst + q);
       }
     }
   }
 }
 
-// Persistent kernel: each wave walks key tiles with a stride of all waves in
-// the grid.  With prefetch, tile i+1 is loaded into a second register buffer
-// while tile i is computed, so HBM latency overlaps the MFMA and packing work.
-template <int D, int M>
-__global__ __launch_bounds__(QM_THREADS, QJL_QM_MINWAVES) void quantize_mfma_kernel(
+// Persistent kernel: each wave walks 64-key tiles with a stride of all waves
+// in the grid; the grid is sized to what is resident at once.  Two waves per
+// SIMD hide one another's HBM latency.
+template <int D, int M, int WAVES, bool DEFER>
+__global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int64_t n,
     float *__restrict__ norms, uint32_t *__restrict__ bits) {
   static_assert(M % 128 == 0, "each lane stores whole 8-byte groups of words");
@@ -188,58 +260,48 @@ __global__ __launch_bounds__(QM_THREADS, QJL_QM_MINWAVES) void quantize_mfma_ker
   const int tid = threadIdx.x;
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(Simg);
-    for (int i = tid; i < M * D / 8; i += QM_THREADS) sS[i] = src[i];
+    for (int i = tid; i < M * D / 8; i += 64 * WAVES) sS[i] = src[i];
   }
   __syncthreads();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int64_t ntiles = (n + QM_KEYS - 1) / QM_KEYS;
-  const int64_t stride = (int64_t)gridDim.x * QM_WAVES;
-  int64_t tile = (int64_t)blockIdx.x * QM_WAVES + wave;
-#if QJL_QM_PREFETCH
-  KeyTile<D / 16> ka, kb;
-  if (tile < ntiles) load_tile<D>(ka, K, tile * QM_KEYS, n, r, h);
-  while (tile < ntiles) {
-    const int64_t t1 = tile + stride;
-    if (t1 < ntiles) load_tile<D>(kb, K, t1 * QM_KEYS, n, r, h);
-    process_tile<D, M>(ka, sS, tile * QM_KEYS, n, lane, r, h, norms, bits);
-    if (t1 >= ntiles) break;
-    const int64_t t2 = t1 + stride;
-    if (t2 < ntiles) load_tile<D>(ka, K, t2 * QM_KEYS, n, r, h);
-    process_tile<D, M>(kb, sS, t1 * QM_KEYS, n, lane, r, h, norms, bits);
-    tile = t2;
-  }
-#else
-  for (; tile < ntiles; tile += stride) {
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
     KeyTile<D / 16> kt;
     load_tile<D>(kt, K, tile * QM_KEYS, n, r, h);
-    process_tile<D, M>(kt, sS, tile * QM_KEYS, n, lane, r, h, norms, bits);
+    process_tile<D, M, DEFER>(kt, sS, tile * QM_KEYS, n, lane, r, h, norms, bits);
   }
-#endif
 }
 
+// Launch shape per sketch size (measured on MI355X): up to m = 256 two
+// 4-wave workgroups share a CU, each with its own copy of S, and packing is
+// deferred; at m = 512 S takes 128 KB of LDS, so one 8-wave workgroup per CU
+// packs each pass as it ends to stay within two waves' registers per SIMD.
 template <int D, int M>
 hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, float *norms,
                      uint32_t *bits, hipStream_t st) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
+  constexpr int WAVES = M <= 256 ? 4 : 8;
+  constexpr bool DEFER = M <= 256;
+  auto kern = quantize_mfma_kernel<D, M, WAVES, DEFER>;
+  static int resident = 0;  // workgroups resident on the whole device
+  if (resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
     (void)hipGetDevice(&dev);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WAVES, 0) !=
+            hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    resident = cus * per_cu;
   }
-  const size_t lds = (size_t)M * D * 2;
-  int per_cu = (int)((160 * 1024) / lds);                          // LDS limit
-  const int by_waves = (4 * QJL_QM_MINWAVES) / QM_WAVES;          // register limit
-  per_cu = per_cu < by_waves ? per_cu : by_waves;
-  per_cu = per_cu < 1 ? 1 : per_cu;
   const int64_t ntiles = (n + QM_KEYS - 1) / QM_KEYS;
-  const int64_t want = (ntiles + QM_WAVES - 1) / QM_WAVES;
-  const int grid = (int)(want < (int64_t)cus * per_cu ? want : (int64_t)cus * per_cu);
-  hipLaunchKernelGGL((quantize_mfma_kernel<D, M>), dim3(grid), dim3(QM_THREADS), 0, st, K,
-                     sk->S16mfma, n, norms, bits);
+  const int64_t want = (ntiles + WAVES - 1) / WAVES;
+  const int grid = (int)(want < resident ? want : resident);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->S16mfma, n, norms, bits);
   return hipGetLastError();
 }
 
