@@ -138,7 +138,6 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
   constexpr int W = M / 32;
   constexpr int NF = W * T;    // S fragments per tile walk
   constexpr int R = QM_RING;
-  constexpr int PER = 16 / T;  // deferred packing steps per MFMA step
   // The S reads below must stay inside the tile loop: hoisted out of it, all
   // m*d/512 fragments would be held in registers.
   asm volatile("" ::: "memory");
@@ -146,29 +145,10 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
 #pragma unroll
   for (int g = 0; g < R; ++g) ring[g] = s_fragment<T>(sS, g, lane);
 
+  // Squared norms: each lane sums its half of the key, one chunk per MFMA
+  // step of the first pass, in increasing chunk order.
+  float ss[QM_RT] = {};
   uint32_t zm[QM_RT];
-  float nrm[QM_RT];
-#pragma unroll
-  for (int rt = 0; rt < QM_RT; ++rt) {
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const uint4 v = __builtin_bit_cast(uint4, kt.a[rt][t]);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w[q]);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
-      }
-    }
-    const float tot = acc + __shfl_xor(acc, 32);
-    zm[rt] = tot > 0.f ? 0u : 0xFFFFFFFFu;
-    nrm[rt] = sqrtf(tot);
-  }
-  {
-    const int64_t key = k0 + 32 * h + r;
-    if (key < n) __builtin_nontemporal_store(h ? nrm[1] : nrm[0], norms + key);
-  }
 
   uint32_t Wd[QM_RT][W / 2];
   uint32_t x[QM_RT] = {};
@@ -186,17 +166,45 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
       for (int rt = 0; rt < QM_RT; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kt.a[rt][t], acc[rt], 0, 0, 0);
       if (g + R < NF) ring[g % R] = s_fragment<T>(sS, g + R, lane);
-      if (DEFER && q > 0) {
+      if (q == 0) {
+#pragma unroll
+        for (int rt = 0; rt < QM_RT; ++rt) {
+          const uint4 v = __builtin_bit_cast(uint4, kt.a[rt][t]);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2_t kx = __builtin_bit_cast(bf16x2_t, w[e]);
+            ss[rt] = __builtin_amdgcn_fdot2_f32_bf16(kx, kx, ss[rt], false);
+          }
+        }
+      }
+      if (DEFER && q > 0 && t > 0) {
+        // Steps 1..T-1 pack the previous pass, registers 15 down to 0; step 0
+        // would wait for that pass's last MFMA to finish writing them.
+        constexpr int hi = 15;  // register packed first
+        const int v1 = hi - (16 * (t - 1)) / (T - 1), v0 = hi + 1 - (16 * t) / (T - 1);
 #pragma unroll
         for (int rt = 0; rt < QM_RT; ++rt) {
 #pragma unroll
-          for (int k = 0; k < PER; ++k)
-            x[rt] = __builtin_amdgcn_alignbit(x[rt], __float_as_uint(prev[rt][15 - PER * t - k]), 31);
+          for (int v = 15; v >= 0; --v)
+            if (v <= v1 && v >= v0)
+              x[rt] = __builtin_amdgcn_alignbit(x[rt], __float_as_uint(prev[rt][v]), 31);
           asm volatile("" : "+v"(x[rt]));
         }
       }
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (q == 0) {
+      float nrm[QM_RT];
+#pragma unroll
+      for (int rt = 0; rt < QM_RT; ++rt) {
+        const float tot = ss[rt] + __shfl_xor(ss[rt], 32);
+        zm[rt] = tot > 0.f ? 0u : 0xFFFFFFFFu;
+        nrm[rt] = sqrtf(tot);
+      }
+      const int64_t key = k0 + 32 * h + r;
+      if (key < n) __builtin_nontemporal_store(h ? nrm[1] : nrm[0], norms + key);
     }
     if (DEFER) {
       if (q > 0 && (q - 1) % 2 == 1) {  // pass q - 1 completed word (q - 1) / 2
