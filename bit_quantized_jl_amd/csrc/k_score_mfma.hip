@@ -23,7 +23,14 @@
 //     products and partial sums are integers below 2^24, so each row of the
 //     accumulator is exactly  R_c = sum_j (2 b_j - 1) L_c(j).
 //   * The epilogue forms sum_c 32^(4-c) R_c (rows of one query sit in lane
-//     groups 0 and 1, or 2 and 3), scales by c ||k|| 2^-F and stores.
+//     groups 0 and 1, or 2 and 3), scales by c ||k|| 2^-F and stores with
+//     non-temporal stores (the scores are not read again by this kernel).
+//
+// Set-up per workgroup and query pass: each wave loads the query values,
+// starts its key stream, then computes F and the digit sums for the whole
+// query itself and writes the operand bytes of a quarter of the coordinates
+// into one shared LDS image; a single LDS barrier later every wave reads its
+// operand registers.  No wave waits for the key stream during the set-up.
 //
 // Operand layout (16x16x128, measured on gfx950): lane l holds row/column
 // l % 16.  An fp4 operand (4 registers) holds contraction indices
@@ -46,14 +53,13 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int SM_THREADS = 256;
 constexpr int SM_WAVES = 4;
 
-// e4m3 bit pattern of an integer |v| <= 64 with at most 4 significant bits.
+// e4m3 bit pattern of an integer |v| <= 64 with at most 4 significant bits:
+// such a value is exact in float32, whose sign, exponent (rebased from 127 to
+// 7) and top three mantissa bits are the e4m3 fields.
 __device__ __forceinline__ uint32_t e4m3_of_int(int v) {
-  if (v == 0) return 0u;
-  const uint32_t s = v < 0 ? 0x80u : 0u;
-  const int a = v < 0 ? -v : v;
-  const int e = 31 - __clz(a);
-  const int man = e >= 3 ? (a >> (e - 3)) & 7 : (a << (3 - e)) & 7;
-  return s | (uint32_t)((e + 7) << 3) | (uint32_t)man;
+  const uint32_t f = __float_as_uint((float)v);
+  const uint32_t mag = ((f >> 20) & 0x7FFu) - (120u << 3);
+  return v == 0 ? 0u : (((f >> 24) & 0x80u) | (mag & 0x7Fu));
 }
 
 // Balanced base-32 digit c (0 = most significant) of X, |X| <= 2^23.
@@ -102,9 +108,6 @@ typedef __attribute__((address_space(1))) void gbl_void_t;
 // gfx950 direct HBM -> LDS path): no registers are held by loads in flight,
 // so a wave keeps R - 1 stages of 64 keys outstanding while it computes one.
 constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
-#ifndef QJL_SM_EARLY_DMA
-#define QJL_SM_EARLY_DMA 0      // issue the first ring stages before the query set-up
-#endif
 // The first R - 1 stages are issued unconditionally (a stage past the wave's
 // range re-reads clamped, valid keys and is never consumed), so the number of
 // loads in flight is static when the loop starts.
@@ -278,10 +281,9 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
   constexpr int NQ = 2 * QP;       // queries per pass
   constexpr int R = Ring<T>::R;
   constexpr int SB = Ring<T>::STAGE_BYTES;
-  __shared__ int sX[NQ][m];
-  __shared__ uint4 sA[QP][T][64][2];
-  __shared__ int sF[NQ];
-  __shared__ int sC[NQ][5];
+  constexpr int JL = (m + 63) / 64;            // query coordinates per lane
+  constexpr int A_BYTES = QP * T * 64 * 32;    // the fp8 operand image
+  __shared__ __attribute__((aligned(16))) unsigned char sAimg[A_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sRing[SM_WAVES][R][SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -298,124 +300,134 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
     const float *gnorm = norms + g * nk;
     for (int64_t q0 = 0; q0 < nq; q0 += NQ) {
       const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
-      // ---- query values to registers first, then start the key DMA so it
-      // overlaps the query set-up (register loads complete before the DMA).
-      constexpr int JL = (m + 63) / 64;
-      float sv[(NQ + SM_WAVES - 1) / SM_WAVES][JL];
+      // ---- query values first (plain loads), then the first key stages
+      // (LDS DMA), so the query set-up below overlaps the stream's latency.
+      // (m is a multiple of 128 here, so every lane's coordinates exist; the
+      // loads are unconditional so the compiler can count them past the DMA.)
+      static_assert(m % 64 == 0, "whole coordinate blocks per lane");
+      float sv[NQ][JL];
 #pragma unroll
-      for (int a = 0; a < (NQ + SM_WAVES - 1) / SM_WAVES; ++a) {
-        const int qi = wave + SM_WAVES * a;
-        const bool qv = qi < nqp;
-        const float *s = Sq + (g * nq + q0 + (qv ? qi : 0)) * (int64_t)m;
+      for (int qi = 0; qi < NQ; ++qi) {
+        const float *src = Sq + (g * nq + q0 + (qi < nqp ? qi : 0)) * (int64_t)m;
 #pragma unroll
         for (int b = 0; b < JL; ++b) {
-          const int j = lane + 64 * b;
-          sv[a][b] = (qv && j < m) ? s[j] : 0.f;
+          const float v = src[lane + 64 * b];
+          sv[qi][b] = qi < nqp ? v : 0.f;
         }
       }
-#if QJL_SM_EARLY_DMA
-      // Start the key stream together with the query loads: the compiler waits
-      // for every outstanding load before the query values are used, so the
-      // first stages land within the same memory latency.  Each wave's ring is
-      // its own and its previous pass is fully consumed, so this is safe
-      // before the barrier.
 #pragma unroll
       for (int j = 0; j < R - 1; ++j)
         issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
                        kend, lane);
-#endif
-      lds_barrier();  // previous pass done with sX / sA
-      // ---- per query: exponent F, fixed-point values, digit sums C_c
+      // The query loads are the oldest in flight: wait for them alone.  (The
+      // compiler cannot count past LDS DMA and would wait for the stages too.)
+      wait_vmcnt<(R - 1) * Ring<T>::L>();
+      if (q0 > 0) lds_barrier();  // every wave has read the previous pass's image
+      // ---- per query: exponent F, fixed-point values X_j = rint(Sq_j 2^F),
+      // balanced base-32 digits, digit sums C_c (every wave computes these for
+      // the whole query) and the operand image (each wave writes the bytes of
+      // coordinate blocks j / 64 = wave mod 4).  A query slot past nqp only
+      // zeroes its bytes.
+      int Fq[NQ];
+      int Cq[NQ][5];
 #pragma unroll
-      for (int a = 0; a < (NQ + SM_WAVES - 1) / SM_WAVES; ++a) {
-        const int qi = wave + SM_WAVES * a;
-        if (qi >= NQ) continue;
+      for (int qi = 0; qi < NQ; ++qi) {
+        Fq[qi] = 0;
+#pragma unroll
+        for (int c = 0; c < 5; ++c) Cq[qi][c] = 0;
+        if (qi >= nqp) {  // empty slot: zero bytes at this wave's coordinates
+#pragma unroll
+          for (int b = 0; b < JL; ++b) {
+            if ((b & 3) != (wave & 3)) continue;
+            const int j = lane + 64 * b;
+            const int wi = j >> 5, jj = j & 31, sreg = jj & 3;
+            const int k = 32 * (wi / T) + 8 * sreg + (jj >> 2);
+            const int grp = (k & 63) >> 4, e = (k >> 6) * 16 + (k & 15);
+            const uint32_t dst = lds_address(
+                sAimg + (((qi >> 1) * T + wi % T) * 64 + 16 * grp + 8 * (qi & 1)) * 32 + e);
+            asm volatile(
+                "ds_write_b8 %0, %1\n\tds_write_b8 %0, %1 offset:32\n\t"
+                "ds_write_b8 %0, %1 offset:64\n\tds_write_b8 %0, %1 offset:96\n\t"
+                "ds_write_b8 %0, %1 offset:128\n\tds_write_b8 %0, %1 offset:160\n\t"
+                "ds_write_b8 %0, %1 offset:192\n\tds_write_b8 %0, %1 offset:224"
+                :
+                : "v"(dst), "v"(0u)
+                : "memory");
+          }
+          continue;
+        }
         float amax = 0.f;
 #pragma unroll
-        for (int b = 0; b < JL; ++b) amax = fmaxf(amax, fabsf(sv[a][b]));
+        for (int b = 0; b < JL; ++b) amax = fmaxf(amax, fabsf(sv[qi][b]));
         amax = wave_max_nonneg(amax);
         int e2 = 0;
         (void)frexpf(amax, &e2);
         const int F = amax > 0.f ? 23 - e2 : 0;
+        const int qp = qi >> 1, qq = qi & 1;
         int C[5] = {0, 0, 0, 0, 0};
 #pragma unroll
         for (int b = 0; b < JL; ++b) {
           const int j = lane + 64 * b;
-          if (j >= m) continue;
-          const int X = (int)rintf(ldexpf(sv[a][b], F));
-          sX[qi][j] = X;
-          const int wj = (j & 3) == 0 ? 5 : ((j & 3) == 3 ? 0 : 1);
+          const int X = (int)rintf(ldexpf(sv[qi][b], F));
+          int L[5];
           int rem = X;
 #pragma unroll
-          for (int k = 4; k >= 0; --k) {
-            const int d = ((rem + 16) & 31) - 16;
-            C[k] += wj * d;
-            rem = (rem - d) >> 5;
+          for (int c = 4; c >= 0; --c) {
+            L[c] = ((rem + 16) & 31) - 16;
+            rem = (rem - L[c]) >> 5;
+          }
+          // coordinate j -> (MFMA t, lane group, byte e) of the fp8 operand:
+          // word wi = j / 32 is fp4 register sreg = j % 4, element eb of lane
+          // group gb = wi / T in MFMA t = wi % T; contraction index
+          // k = 32 gb + eb sits in fp8 byte e of lane group (k % 64) / 16.
+          const int wi = j >> 5, jj = j & 31, sreg = jj & 3;
+          const int wj = sreg == 0 ? 5 : (sreg == 3 ? 0 : 1);
+#pragma unroll
+          for (int c = 0; c < 5; ++c) C[c] += wj * L[c];
+          if ((b & 3) == (wave & 3)) {
+            const int eb = 8 * sreg + (jj >> 2);
+            const int k = 32 * (wi / T) + eb;
+            const int t = wi % T;
+            const int grp = (k & 63) >> 4, e = (k >> 6) * 16 + (k & 15);
+            const int f = sreg == 0 ? 4 : (sreg == 1 ? 2 : (sreg == 2 ? 1 : -1));
+            const uint32_t dst =
+                lds_address(sAimg + ((qp * T + t) * 64 + 16 * grp + 8 * qq) * 32 + e);
+            // Limb rows c = 0..4, zero rows 5..7.  Written in asm: as plain
+            // stores the compiler would first wait for the key DMA in flight.
+            asm volatile(
+                "ds_write_b8 %0, %1\n\tds_write_b8 %0, %2 offset:32\n\t"
+                "ds_write_b8 %0, %3 offset:64\n\tds_write_b8 %0, %4 offset:96\n\t"
+                "ds_write_b8 %0, %5 offset:128\n\tds_write_b8 %0, %6 offset:160\n\t"
+                "ds_write_b8 %0, %6 offset:192\n\tds_write_b8 %0, %6 offset:224"
+                :
+                : "v"(dst), "v"(e4m3_of_int(f * L[0])), "v"(e4m3_of_int(f * L[1])),
+                  "v"(e4m3_of_int(f * L[2])), "v"(e4m3_of_int(f * L[3])),
+                  "v"(e4m3_of_int(f * L[4])), "v"(0u)
+                : "memory");
           }
         }
+        Fq[qi] = F;
 #pragma unroll
-        for (int k = 0; k < 5; ++k) C[k] = wave_sum(C[k]);
-        if (lane == 0) {
-          sF[qi] = F;
-#pragma unroll
-          for (int k = 0; k < 5; ++k) sC[qi][k] = C[k];
-        }
+        for (int c = 0; c < 5; ++c) Cq[qi][c] = wave_sum(C[c]);
       }
-      // ---- A operand (limb rows) in MFMA order: zero, then one task per
-      // (pair, slot, lane group, pair member, byte) writes its five limb bytes.
-      {
-        uint4 *z = &sA[0][0][0][0];
-        for (int i = tid; i < QP * T * 64 * 2; i += SM_THREADS) z[i] = make_uint4(0, 0, 0, 0);
-      }
-      lds_barrier();
-#if !QJL_SM_EARLY_DMA
-      // Start the key stream now: the limb build below touches only LDS.
-#pragma unroll
-      for (int j = 0; j < R - 1; ++j)
-        issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
-                       kend, lane);
-#endif
-      unsigned char *sAb = reinterpret_cast<unsigned char *>(&sA[0][0][0][0]);
-      for (int idx = tid; idx < QP * T * 4 * 2 * 32; idx += SM_THREADS) {
-        const int e = idx & 31;
-        const int qq = (idx >> 5) & 1;
-        const int grp = (idx >> 6) & 3;
-        const int t = (idx >> 8) % T;
-        const int qp = idx / (256 * T);
-        const int qi = 2 * qp + qq;
-        if (qi >= nqp) continue;
-        // fp8 byte e of lane group grp is contraction index k; the fp4 bits
-        // operand holds k as element k % 32 of lane group k / 32.
-        const int k = e < 16 ? 16 * grp + e : 64 + 16 * grp + (e - 16);
-        const int gb = k >> 5, eb = k & 31;
-        const int wi = T * gb + t;
-        const int sreg = eb >> 3;
-        const int j = 32 * wi + 4 * (eb & 7) + sreg;
-        const int f = sreg == 0 ? 4 : (sreg == 1 ? 2 : (sreg == 2 ? 1 : -1));
-        int rem = sX[qi][j];
-        int L[5];
-#pragma unroll
-        for (int c = 4; c >= 0; --c) {
-          L[c] = ((rem + 16) & 31) - 16;
-          rem = (rem - L[c]) >> 5;
-        }
-#pragma unroll
-        for (int c = 0; c < 5; ++c) {
-          const int l = (8 * qq + c) + 16 * grp;
-          sAb[(((qp * T + t) * 64 + l) * 32) + e] = (unsigned char)e4m3_of_int(f * L[c]);
-        }
-      }
-      lds_barrier();
+      lds_barrier();  // the image is complete
+      // The reads wait for themselves, not for the key DMA in flight.
       v8i_t A[QP][T];
 #pragma unroll
       for (int qp = 0; qp < QP; ++qp)
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          const uint4 a0 = sA[qp][t][lane][0], a1 = sA[qp][t][lane][1];
+          u32x4_t a0, a1;
+          asm volatile(
+              "ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+              : "=&v"(a0), "=&v"(a1)
+              : "v"(lds_address(sAimg + ((qp * T + t) * 64 + lane) * 32))
+              : "memory");
           A[qp][t] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
         }
-      // per-lane epilogue constants: rows 4 gq + v
+      // per-lane epilogue constants: accumulator rows 4 gq + v hold limb
+      // c = (4 gq + v) % 8 of query member gq / 2
       float wgt[4];
       v4f_t cinit[QP];
       float qscale[QP];
@@ -426,14 +438,18 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       }
 #pragma unroll
       for (int qp = 0; qp < QP; ++qp) {
-        const int qi = 2 * qp + (gq >> 1);
-        const bool qv = qi < nqp;
+        const bool hi = (gq >> 1) != 0;
+        const int qi0 = 2 * qp, qi1 = 2 * qp + 1;
+        const bool qv = (hi ? qi1 : qi0) < nqp;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int c = (4 * gq + v) & 7;
-          cinit[qp][v] = (qv && c < 5) ? -(float)sC[qi][c] : 0.f;
+          // limb c = v in even lane groups, c = 4 + v (a limb only for v = 0) in odd ones
+          const int lo = hi ? Cq[qi1][v] : Cq[qi0][v];
+          const int up = v == 0 ? (hi ? Cq[qi1][4] : Cq[qi0][4]) : 0;
+          cinit[qp][v] = qv ? -(float)((gq & 1) ? up : lo) : 0.f;
         }
-        qscale[qp] = qv ? ldexpf(cscale, -sF[qi]) : 0.f;
+        const int F = hi ? Fq[qi1] : Fq[qi0];
+        qscale[qp] = qv ? ldexpf(cscale, -F) : 0.f;
       }
       // ---- stream this wave's stages through the ring
       for (int j = 0; j < ns; ++j) {
@@ -478,7 +494,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
             e += __shfl_xor(e, 16);
             const int qi = 2 * qp + (gq >> 1);
             if ((gq & 1) == 0 && key < kend && qi < nqp)
-              out[(g * nq + q0 + qi) * nk + key] = (e * qscale[qp]) * nrm;
+              __builtin_nontemporal_store((e * qscale[qp]) * nrm,
+                                          out + (g * nq + q0 + qi) * nk + key);
           }
         }
       }
