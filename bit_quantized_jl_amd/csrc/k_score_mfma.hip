@@ -271,6 +271,40 @@ struct StageRead<8> {
   }
 };
 
+// One 16-key tile: expand the bits to the fp4 operand, run the MFMAs against
+// the query limbs, combine the limb rows and store the scores of the tile.
+template <int T, int QP>
+__device__ __forceinline__ void score_tile(const uint32_t *wb, float nrm, const v8i_t (&A)[QP][T],
+                                           const v4f_t (&cinit)[QP], const float (&wgt)[4],
+                                           const float (&qscale)[QP], int64_t key, int64_t kend,
+                                           int gq, int nqp, float *__restrict__ outq, int64_t nk) {
+  v4f_t acc[QP];
+#pragma unroll
+  for (int qp = 0; qp < QP; ++qp) acc[qp] = cinit[qp];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint32_t w = wb[t];
+    const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
+                          (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
+                          0, 0, 0, 0};
+#pragma unroll
+    for (int qp = 0; qp < QP; ++qp)
+      acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qp][t], B, acc[qp], 0, 4, 0,
+                                                                  127, 0, 127);
+  }
+#pragma unroll
+  for (int qp = 0; qp < QP; ++qp) {
+    float e = acc[qp][0] * wgt[0];
+    e = fmaf(acc[qp][1], wgt[1], e);
+    e = fmaf(acc[qp][2], wgt[2], e);
+    e = fmaf(acc[qp][3], wgt[3], e);
+    e += __shfl_xor(e, 16);
+    const int qi = 2 * qp + (gq >> 1);
+    if ((gq & 1) == 0 && key < kend && qi < nqp)
+      __builtin_nontemporal_store((e * qscale[qp]) * nrm, outq + qi * nk + key);
+  }
+}
+
 template <int T, int QP>
 __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
@@ -466,41 +500,13 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         sr.read(lds_address(slot + ((lane & 15) * W + T * gq) * 4),
                 lds_address(slot + Ring<T>::BITS_BYTES + (lane & 15) * 4));
 #pragma unroll
-        for (int u = 0; u < SM_STAGE / 16; ++u) {
-          const int kl = 16 * u + (lane & 15);
-          const int64_t key = k0 + kl;
-          const uint32_t *wb = sr.w[u];
-          const float nrm = sr.n[u];
-          v4f_t acc[QP];
-#pragma unroll
-          for (int qp = 0; qp < QP; ++qp) acc[qp] = cinit[qp];
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const uint32_t w = wb[t];
-            const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
-                                  (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
-                                  0, 0, 0, 0};
-#pragma unroll
-            for (int qp = 0; qp < QP; ++qp)
-              acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qp][t], B, acc[qp], 0,
-                                                                          4, 0, 127, 0, 127);
-          }
-#pragma unroll
-          for (int qp = 0; qp < QP; ++qp) {
-            float e = acc[qp][0] * wgt[0];
-            e = fmaf(acc[qp][1], wgt[1], e);
-            e = fmaf(acc[qp][2], wgt[2], e);
-            e = fmaf(acc[qp][3], wgt[3], e);
-            e += __shfl_xor(e, 16);
-            const int qi = 2 * qp + (gq >> 1);
-            if ((gq & 1) == 0 && key < kend && qi < nqp)
-              __builtin_nontemporal_store((e * qscale[qp]) * nrm,
-                                          out + (g * nq + q0 + qi) * nk + key);
-          }
-        }
+        for (int u = 0; u < SM_STAGE / 16; ++u)
+          score_tile<T, QP>(sr.w[u], sr.n[u], A, cinit, wgt, qscale, k0 + 16 * u + (lane & 15),
+                            kend, gq, nqp, out + (g * nq + q0) * nk, nk);
       }
     }
   }
+  wait_vmcnt<0>();  // loads of clamped stages past the end must land before exit
 }
 
 template <int T, int QP>
