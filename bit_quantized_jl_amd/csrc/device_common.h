@@ -28,17 +28,20 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_
 // h = r(seed, 4, ctr) per pair; a = h >> 40 and b = (h >> 16) & 0xFFFFFF give
 // u1 = (a + 1) 2^-24 and u2 = b 2^-24 (exact in float32); Box-Muller returns
 // R cos(2 pi u2) for the even and R sin(2 pi u2) for the odd coordinate.
+// The gfx950 transcendental instructions evaluate it directly: v_log_f32 is
+// log2 (R^2 = -2 ln 2 log2 u1), v_sin_f32 / v_cos_f32 take their argument in
+// revolutions (sin(2 pi u2) = v_sin_f32(u2), u2 in [0, 1)).  Their float32
+// errors move a dither value by ~1e-6 of its size, far below the band of
+// coordinates whose sign is not compared bit for bit.
 __device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &xc, float &xs) {
   const uint64_t h = stream_draw(key, ctr);
   const uint32_t a = (uint32_t)(h >> 40);
   const uint32_t b = (uint32_t)(h >> 16) & 0xFFFFFFu;
   const float u1 = (float)(a + 1u) * 0x1p-24f;
   const float u2 = (float)b * 0x1p-24f;
-  const float r = sqrtf(-2.0f * logf(u1));
-  float sn, cs;
-  sincospif(2.0f * u2, &sn, &cs);
-  xc = r * cs;
-  xs = r * sn;
+  const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
+  xc = r * __builtin_amdgcn_cosf(u2);
+  xs = r * __builtin_amdgcn_sinf(u2);
 }
 
 __device__ __forceinline__ float dither_one(uint64_t key, uint64_t key_index, int m, int j) {

@@ -38,7 +38,38 @@ __device__ __forceinline__ void fwht_reg(float (&u)[D]) {
   }
 }
 
-template <int D, typename T, bool PROJECT, bool DITHER>
+// Row loads as 16-byte vectors (a 2-byte load per element leaves each load
+// instruction touching 64 cache lines for 128 bytes).
+template <int D, typename T>
+__device__ __forceinline__ void load_row_vec(const T *__restrict__ xr, bool valid, float (&x)[D]) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(xr);
+  constexpr int NV = D * (int)sizeof(T) / 16;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint4 q = src[v];
+    const uint32_t w[4] = {valid ? q.x : 0u, valid ? q.y : 0u, valid ? q.z : 0u, valid ? q.w : 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (sizeof(T) == 4) {
+        x[4 * v + e] = __uint_as_float(w[e]);
+      } else {
+        x[8 * v + 2 * e] = __uint_as_float(w[e] << 16);
+        x[8 * v + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// Sign bits of 32 consecutive coordinates, bit t = [u[t] >= 0]: adding +0
+// turns -0 into +0, then each v_alignbit_b32 shifts one sign bit in.
+__device__ __forceinline__ uint32_t pack_nonneg(const float *u) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int t = 31; t >= 0; --t) word = __builtin_amdgcn_alignbit(word, __float_as_uint(u[t] + 0.0f), 31);
+  return ~word;
+}
+
+template <int D, typename T, bool PROJECT, bool DITHER, bool VEC>
 __global__ __launch_bounds__(64) void fqjl_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
@@ -55,8 +86,12 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
     float x[HOLD ? D : 1];
     float nrm = 0.f;
     if (HOLD) {
+      if constexpr (VEC) {
+        load_row_vec<D, T>(xr, valid, x);
+      } else {
 #pragma unroll
-      for (int c = 0; c < D; ++c) x[c] = valid ? load_as_f32(xr, c) : 0.f;
+        for (int c = 0; c < D; ++c) x[c] = valid ? load_as_f32(xr, c) : 0.f;
+      }
     }
     if (!PROJECT) {
       float s = 0.f;
@@ -106,12 +141,7 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
         if (valid) {
           uint32_t *br = bits + row * (int64_t)W + b * (D / 32);
 #pragma unroll
-          for (int w = 0; w < D / 32; ++w) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int t = 0; t < 32; ++t) word |= (u[32 * w + t] >= 0.f ? 1u : 0u) << t;
-            br[w] = word;
-          }
+          for (int w = 0; w < D / 32; ++w) br[w] = pack_nonneg(&u[32 * w]);
         }
       }
     }
@@ -183,17 +213,24 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
   const int grid = (int)(tiles < 16384 ? tiles : 16384);
   const bool proj = Y != nullptr;
   const bool dith = !proj && h.rho > 0.f;
-#define QJL_FQJL_LAUNCH(KERNEL, PJ, DT)                                                        \
-  hipLaunchKernelGGL((KERNEL<D, T, PJ, DT>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign, \
+#define QJL_FQJL_LAUNCH(KERNEL, ...)                                                            \
+  hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign,  \
                      sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
-  if (D >= 32) {
-    if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, true, false);
-    else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, false, true);
-    else QJL_FQJL_LAUNCH(fqjl_kernel, false, false);
+  if constexpr (D >= 32) {
+    const bool vec = ((uintptr_t)X & 15) == 0;  // rows are whole 16-byte vectors then
+    if (vec) {
+      if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true);
+      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true);
+      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, true);
+    } else {
+      if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false);
+      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false);
+      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, false);
+    }
   } else {
-    if (proj) QJL_FQJL_LAUNCH(fqjl_small_kernel, true, false);
-    else if (dith) QJL_FQJL_LAUNCH(fqjl_small_kernel, false, true);
-    else QJL_FQJL_LAUNCH(fqjl_small_kernel, false, false);
+    if (proj) QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, true, false);
+    else if (dith) QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, false, true);
+    else QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, false, false);
   }
 #undef QJL_FQJL_LAUNCH
   return hipGetLastError();

@@ -79,23 +79,23 @@ namespace {
 #define QJL_QM_RING 4  // S fragments in flight from LDS
 #endif
 constexpr int QM_RING = QJL_QM_RING;
-constexpr int QM_RT = 2;     // 32-key column tiles per wave (each S fragment feeds 2 MFMAs)
-constexpr int QM_KEYS = 64;  // keys per wave tile
+// A wave tile is RT 32-key column tiles: each S fragment read from LDS feeds
+// RT MFMAs.
 
-template <int T>
+template <int T, int RT>
 struct KeyTile {
-  bf16x8_t a[QM_RT][T];
+  bf16x8_t a[RT][T];
 };
 
-// Load the B fragments of the 64 keys starting at k0.  Rows past n re-read
+// Load the B fragments of the 32 RT keys starting at k0.  Rows past n re-read
 // row n-1 (their results are never stored): the loads stay unconditional, so
 // the compiler can count them and wait only for the tile it needs.
-template <int D>
-__device__ __forceinline__ void load_tile(KeyTile<D / 16> &kt, const uint16_t *__restrict__ K,
+template <int D, int RT>
+__device__ __forceinline__ void load_tile(KeyTile<D / 16, RT> &kt, const uint16_t *__restrict__ K,
                                           int64_t k0, int64_t n, int r, int h) {
   constexpr int T = D / 16;
 #pragma unroll
-  for (int rt = 0; rt < QM_RT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     int64_t row = k0 + 32 * rt + r;
     row = row < n ? row : n - 1;
     const uint4 *src = reinterpret_cast<const uint4 *>(K + row * D);
@@ -123,14 +123,14 @@ __device__ __forceinline__ uint32_t pack_signs(uint32_t x, const floatx16_t &acc
   return x;
 }
 
-// Norms, projection, sign packing and stores for one 64-key tile.  With
+// Norms, projection, sign packing and stores for one wave tile of 32 RT keys.  With
 // DEFER the bits of pass q - 1 are packed during pass q (one more pair of
 // accumulators live); otherwise each pass is packed when it ends.  A
 // scheduling barrier closes every MFMA step: without it the scheduler hoists
-// all MFMAs of the tile and runs out of registers.  Norms of the two column
-// tiles leave in one 64-lane store (lane half h writes column tile h).
-template <int D, int M, bool DEFER>
-__device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const uint4 *sS,
+// all MFMAs of the tile and runs out of registers.  Norms of column tiles
+// 2i and 2i + 1 leave in one 64-lane store (lane half h writes tile 2i + h).
+template <int D, int M, int RT, bool DEFER>
+__device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, const uint4 *sS,
                                              int64_t k0, int64_t n, int lane, int r, int h,
                                              float *__restrict__ norms,
                                              uint32_t *__restrict__ bits) {
@@ -147,28 +147,28 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
 
   // Squared norms: each lane sums its half of the key, one chunk per MFMA
   // step of the first pass, in increasing chunk order.
-  float ss[QM_RT] = {};
-  uint32_t zm[QM_RT];
+  float ss[RT] = {};
+  uint32_t zm[RT];
 
-  uint32_t Wd[QM_RT][W / 2];
-  uint32_t x[QM_RT] = {};
-  floatx16_t prev[QM_RT];
+  uint32_t Wd[RT][W / 2];
+  uint32_t x[RT] = {};
+  floatx16_t prev[RT];
 #pragma unroll
   for (int q = 0; q < W; ++q) {
-    floatx16_t acc[QM_RT];
+    floatx16_t acc[RT];
 #pragma unroll
-    for (int rt = 0; rt < QM_RT; ++rt) acc[rt] = floatx16_t{};
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx16_t{};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int g = q * T + t;
       const bf16x8_t A = ring[g % R];
 #pragma unroll
-      for (int rt = 0; rt < QM_RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
         acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kt.a[rt][t], acc[rt], 0, 0, 0);
       if (g + R < NF) ring[g % R] = s_fragment<T>(sS, g + R, lane);
       if (q == 0) {
 #pragma unroll
-        for (int rt = 0; rt < QM_RT; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
           const uint4 v = __builtin_bit_cast(uint4, kt.a[rt][t]);
           const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -184,7 +184,7 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
         constexpr int hi = 15;  // register packed first
         const int v1 = hi - (16 * (t - 1)) / (T - 1), v0 = hi + 1 - (16 * t) / (T - 1);
 #pragma unroll
-        for (int rt = 0; rt < QM_RT; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
           for (int v = 15; v >= 0; --v)
             if (v <= v1 && v >= v0)
@@ -196,29 +196,32 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
       __builtin_amdgcn_sched_barrier(0);
     }
     if (q == 0) {
-      float nrm[QM_RT];
+      float nrm[RT];
 #pragma unroll
-      for (int rt = 0; rt < QM_RT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const float tot = ss[rt] + __shfl_xor(ss[rt], 32);
         zm[rt] = tot > 0.f ? 0u : 0xFFFFFFFFu;
         nrm[rt] = sqrtf(tot);
       }
-      const int64_t key = k0 + 32 * h + r;
-      if (key < n) __builtin_nontemporal_store(h ? nrm[1] : nrm[0], norms + key);
+#pragma unroll
+      for (int i = 0; i < RT / 2; ++i) {
+        const int64_t key = k0 + 32 * (2 * i + h) + r;
+        if (key < n) __builtin_nontemporal_store(h ? nrm[2 * i + 1] : nrm[2 * i], norms + key);
+      }
     }
     if (DEFER) {
       if (q > 0 && (q - 1) % 2 == 1) {  // pass q - 1 completed word (q - 1) / 2
 #pragma unroll
-        for (int rt = 0; rt < QM_RT; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
           Wd[rt][(q - 1) / 2] = ~x[rt] | zm[rt];
           x[rt] = 0;
         }
       }
 #pragma unroll
-      for (int rt = 0; rt < QM_RT; ++rt) prev[rt] = acc[rt];
+      for (int rt = 0; rt < RT; ++rt) prev[rt] = acc[rt];
     } else {
 #pragma unroll
-      for (int rt = 0; rt < QM_RT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         x[rt] = pack_signs<15, 0>(x[rt], acc[rt]);
         if (q % 2 == 1) {
           Wd[rt][q / 2] = ~x[rt] | zm[rt];
@@ -229,14 +232,14 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
   }
   if (DEFER) {
 #pragma unroll
-    for (int rt = 0; rt < QM_RT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       x[rt] = pack_signs<15, 0>(x[rt], prev[rt]);
       Wd[rt][W / 2 - 1] = ~x[rt] | zm[rt];
     }
   }
 
 #pragma unroll
-  for (int rt = 0; rt < QM_RT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int64_t key = k0 + 32 * rt + r;
     if (key < n) {
       if constexpr ((W / 2) % 4 == 0) {
@@ -259,7 +262,7 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16> &kt, const ui
 // Persistent kernel: each wave walks 64-key tiles with a stride of all waves
 // in the grid; the grid is sized to what is resident at once.  Two waves per
 // SIMD hide one another's HBM latency.
-template <int D, int M, int WAVES, bool DEFER>
+template <int D, int M, int WAVES, int RT, bool DEFER>
 __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int64_t n,
     float *__restrict__ norms, uint32_t *__restrict__ bits) {
@@ -274,12 +277,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int64_t ntiles = (n + QM_KEYS - 1) / QM_KEYS;
+  constexpr int KEYS = 32 * RT;
+  const int64_t ntiles = (n + KEYS - 1) / KEYS;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
   for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
-    KeyTile<D / 16> kt;
-    load_tile<D>(kt, K, tile * QM_KEYS, n, r, h);
-    process_tile<D, M, DEFER>(kt, sS, tile * QM_KEYS, n, lane, r, h, norms, bits);
+    KeyTile<D / 16, RT> kt;
+    load_tile<D, RT>(kt, K, tile * KEYS, n, r, h);
+    process_tile<D, M, RT, DEFER>(kt, sS, tile * KEYS, n, lane, r, h, norms, bits);
   }
 }
 
@@ -290,9 +294,12 @@ __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
 template <int D, int M>
 hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, float *norms,
                      uint32_t *bits, hipStream_t st) {
+  // Two column tiles per wave: four (halving the LDS reads of S) measured
+  // slower, with no room left to defer the packing.
+  constexpr int RT = 2;
   constexpr int WAVES = M <= 256 ? 4 : 8;
   constexpr bool DEFER = M <= 256;
-  auto kern = quantize_mfma_kernel<D, M, WAVES, DEFER>;
+  auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER>;
   static int resident = 0;  // workgroups resident on the whole device
   if (resident == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -306,7 +313,7 @@ hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, float *
       per_cu = 1;
     resident = cus * per_cu;
   }
-  const int64_t ntiles = (n + QM_KEYS - 1) / QM_KEYS;
+  const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)(want < resident ? want : resident);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->S16mfma, n, norms, bits);
