@@ -148,6 +148,125 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
   }
 }
 
+// d = 128 with two lanes per row (32 rows per wave): lane half s computes
+// output half s of each Walsh-Hadamard transform.  H_128 = [[H, H], [H, -H]]
+// with H = H_64, so half s of H_128 z is H_64 (z_lo + (-1)^s z_hi): each lane
+// folds the top butterfly stage into how it combines its inputs and runs a
+// 64-point transform, with no cross-lane exchange.  The permutation tile is
+// then 16 KB per wave (element c of row k at ((c ^ (c >> 6)) << 5) + k: the
+// two halves' writes land in disjoint banks, and every gather reads one index
+// for all lanes, so it is conflict free), which doubles the waves a CU holds.
+template <typename T, bool PROJECT, bool DITHER>
+__global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
+    const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
+    const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
+    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    float *__restrict__ Y) {
+  constexpr int D = 128, H = 64;
+  __shared__ float lds[D * 32];
+  const int lane = threadIdx.x;
+  const int k = lane & 31, sh = lane >> 5;
+  const float sgn = sh ? -1.f : 1.f;
+  const int W = m / 32;
+  auto idx = [](int c, int key) { return ((c ^ (c >> 6)) << 5) + key; };
+  for (int64_t r0 = (int64_t)blockIdx.x * 32; r0 < n; r0 += (int64_t)gridDim.x * 32) {
+    const int64_t row = r0 + k;
+    const bool valid = row < n;
+    const T *xr = X + (valid ? row : 0) * (int64_t)D;
+    // The row stays in registers as loaded (bf16 pairs or float words) and is
+    // widened where it is used: half the registers of a float copy for bf16.
+    constexpr int NW = D * (int)sizeof(T) / 4;
+    uint32_t xw[NW];
+    {
+      const uint4 *src = reinterpret_cast<const uint4 *>(xr);
+#pragma unroll
+      for (int v = 0; v < NW / 4; ++v) {  // a row past n re-reads row 0 and stores nothing
+        const uint4 q = src[v];
+        xw[4 * v] = q.x;
+        xw[4 * v + 1] = q.y;
+        xw[4 * v + 2] = q.z;
+        xw[4 * v + 3] = q.w;
+      }
+    }
+    auto elem = [&](int c) -> uint32_t {  // float bits of element c
+      if constexpr (sizeof(T) == 4) return xw[c];
+      else return (c & 1) ? (xw[c >> 1] & 0xFFFF0000u) : (xw[c >> 1] << 16);
+    };
+    float nrm = 0.f;
+    if (!PROJECT) {  // each lane half sums half the row
+      float ssq = 0.f;
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        const float v = __uint_as_float(sh ? elem(c + H) : elem(c));
+        ssq = fmaf(v, v, ssq);
+      }
+      nrm = sqrtf(ssq + __shfl_xor(ssq, 32));
+      if (valid && sh == 0) norms[row] = nrm;
+    }
+    for (int b = 0; b < nb; ++b) {
+      // Re-widen the row inside each block: hoisted out of this loop, the
+      // widened copy would sit in registers beside the packed one.
+#pragma unroll
+      for (int i = 0; i < NW; ++i) asm volatile("" : "+v"(xw[i]));
+      const uint32_t *ds = Dsign + b * D;
+      const int32_t *pb = P + b * D;
+      const float *gb = Gs + b * D;
+      float t[H];
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        const float lo = __uint_as_float(elem(c) ^ ds[c]);
+        const float hi = __uint_as_float(elem(c + H) ^ ds[c + H]);
+        t[c] = fmaf(sgn, hi, lo);
+      }
+      fwht_reg<H>(t);
+      {
+        // idx(c + 64 sh, k) = 32 (c ^ sh) + 2048 sh + k for c < 64: one lane base
+        // for even and one for odd c, plus an immediate offset 32 c.
+        float *we = lds + k + 2048 * sh + 32 * sh;
+        float *wo = lds + k + 2048 * sh - 32 * sh;
+#pragma unroll
+        for (int c = 0; c < H; ++c) ((c & 1) ? wo : we)[32 * c] = t[c];
+      }
+      // Gather in groups of 16: the barriers keep the compiler from hoisting
+      // all 128 reads (and their addresses) into registers at once.
+#pragma unroll
+      for (int c = 0; c < H; ++c) {
+        if (c % 16 == 0) asm volatile("" ::: "memory");
+        const float lo = lds[idx(pb[c], k)] * gb[c];
+        const float hi = lds[idx(pb[c + H], k)] * gb[c + H];
+        t[c] = fmaf(sgn, hi, lo);
+      }
+      fwht_reg<H>(t);
+      const int j0 = b * D + H * sh;  // sketch coordinate of t[0]
+      if (PROJECT) {
+        if (valid) {
+          float *yr = Y + row * (int64_t)m + j0;
+#pragma unroll
+          for (int c = 0; c < H; ++c) yr[c] = t[c];
+        }
+      } else {
+        if (DITHER) {
+          const float amp = rho * nrm;
+          const uint64_t pair0 =
+              (uint64_t)(base + (valid ? row : 0)) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
+#pragma unroll
+          for (int c = 0; c < H; c += 2) {
+            float xc, xs;
+            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            t[c] += amp * xc;
+            t[c + 1] += amp * xs;
+          }
+        }
+        if (valid) {
+          uint32_t *br = bits + row * (int64_t)W + j0 / 32;
+#pragma unroll
+          for (int w = 0; w < H / 32; ++w) br[w] = pack_nonneg(&t[32 * w]);
+        }
+      }
+    }
+  }
+}
+
 // d = 8 or 16: a block is narrower than one 32-bit word, so the bits of
 // consecutive blocks share words.  These small sizes exist so the GPU chain
 // can be checked against explicit matrices; they run a plain per-lane loop
@@ -216,6 +335,20 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
 #define QJL_FQJL_LAUNCH(KERNEL, ...)                                                            \
   hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign,  \
                      sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
+  if constexpr (D == 128) {
+    if (((uintptr_t)X & 15) == 0) {  // rows are whole 16-byte vectors
+      const int64_t tiles2 = (n + 31) / 32;
+      const int grid2 = (int)(tiles2 < 32768 ? tiles2 : 32768);
+#define QJL_FQJL128_LAUNCH(...)                                                                  \
+  hipLaunchKernelGGL((fqjl128_kernel<__VA_ARGS__>), dim3(grid2), dim3(64), 0, st, X, nb, h.m,    \
+                     sk->Dsign, sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
+      if (proj) QJL_FQJL128_LAUNCH(T, true, false);
+      else if (dith) QJL_FQJL128_LAUNCH(T, false, true);
+      else QJL_FQJL128_LAUNCH(T, false, false);
+#undef QJL_FQJL128_LAUNCH
+      return hipGetLastError();
+    }
+  }
   if constexpr (D >= 32) {
     const bool vec = ((uintptr_t)X & 15) == 0;  // rows are whole 16-byte vectors then
     if (vec) {
