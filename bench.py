@@ -48,6 +48,9 @@ def parse():
                    help="only the timed step (used under profilers)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
+                   help="run only the dense quantize launch back to back for SECONDS while "
+                        "sampling socket power and graphics clocks with amd-smi")
     return p.parse_args()
 
 
@@ -62,6 +65,64 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_read": a.numel() * 4,
                       "calibrate_copy_bytes_written": a.numel() * 4}), flush=True)
+
+
+def sustain(seconds: float):
+    """The dominant kernel under sustained load: the 7B-shape quantize launched
+    back to back for `seconds`, with amd-smi sampling socket power and the
+    graphics clocks of every XCD in a child process meanwhile.  Prints one JSON
+    line: mean launch time, mean power, mean clock (samples of the first
+    second, while the clocks settle, are dropped)."""
+    import re
+    import subprocess
+    import torch
+
+    import bit_quantized_jl_amd as qj
+    import workloads as wl
+
+    qj.load()
+    w = wl.DECODE_7B
+    dev = "cuda:0"
+    K = wl.make_keys(w, dev)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    norms = torch.empty(w.n_keys, dtype=torch.float32, device=dev)
+    bits = torch.empty((w.n_keys, w.m // 32), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    for _ in range(10):
+        qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+    torch.cuda.synchronize()
+    n_samples = max(1, int(seconds / 0.5) - 2)
+    sampler = subprocess.Popen(
+        ["bash", "-c", f"sleep 1; for i in $(seq {n_samples}); do amd-smi metric -p -c; sleep 0.3; done"],
+        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    a, b = HipEvent(), HipEvent()
+    launches = 0
+    t0 = time.time()
+    a.record(st)
+    while time.time() - t0 < seconds:
+        for _ in range(50):
+            qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+        launches += 50
+        torch.cuda.synchronize()
+    b.record(st)
+    torch.cuda.synchronize()
+    out = sampler.communicate()[0]
+    power = [float(x) for x in re.findall(r"SOCKET_POWER: (\d+(?:\.\d+)?)", out)]
+    clocks, section = [], ""
+    for line in out.splitlines():
+        head = re.match(r"\s*(\w+):\s*$", line)
+        if head:
+            section = head.group(1)
+            continue
+        clk = re.match(r"\s*CLK: (\d+) MHz", line)
+        if clk and section.startswith("GFX_"):  # graphics clock of one XCD
+            clocks.append(float(clk.group(1)))
+    print(json.dumps({"sustain_s": seconds, "launches": launches,
+                      "mean_launch_s": a.seconds_to(b) / launches,
+                      "socket_power_w_mean": sum(power) / len(power) if power else None,
+                      "socket_power_w_samples": len(power),
+                      "gfx_clock_mhz_mean": sum(clocks) / len(clocks) if clocks else None,
+                      "gfx_clock_samples": len(clocks)}), flush=True)
 
 
 def kernel_src_hash() -> str:
@@ -201,6 +262,33 @@ class HipEvent:
             self._lib.hipEventDestroy(self._ev)
 
 
+def time_quantize(qj, torch, w, reps: int = 10):
+    """One quantize configuration on its own: `reps` launches back to back
+    between two HIP events after two warm-up launches; returns seconds per
+    launch and the algorithmic bytes of one launch."""
+    import workloads as wl
+    dev = "cuda:0"
+    K = wl.make_keys(w, dev)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    norms = torch.empty(w.n_keys, dtype=torch.float32, device=dev)
+    bits = torch.empty((w.n_keys, w.m // 32), dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+    torch.cuda.synchronize()
+    a, b = HipEvent(), HipEvent()
+    a.record(st)
+    for _ in range(reps):
+        qj.quantize_keys(sk, K, norms_out=norms, bits_out=bits, stream=st)
+    b.record(st)
+    torch.cuda.synchronize()
+    t = a.seconds_to(b) / reps
+    sk.close()
+    del K, norms, bits
+    torch.cuda.empty_cache()
+    return t, quantize_bytes(w)
+
+
 def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
     """Score kernel alone over `n_sets` distinct (bits, norms, Sq) sets, so the
     working set exceeds the 256 MB Infinity Cache; returns mean seconds."""
@@ -240,6 +328,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sustain > 0:
+        sustain(args.sustain)
         return
     import torch
 
@@ -358,6 +449,14 @@ def main():
                                         "mean_s": s2_mean, "median_s": s2_med, "bytes": sb2,
                                         "rotation": "2 sets x 302 MB"}
         sk2.close()
+        # the other quantize configurations (same 2,097,152-key cache size)
+        for name, wq in (("quantize_prefill", wl.PREFILL), ("quantize_fqjl", wl.FQJL_7B),
+                         ("quantize_fqjl_dither", wl.FQJL_7B_DITHER)):
+            tq, bq = time_quantize(qj, torch, wq)
+            result[name] = {"workload": wq.name, "sketch": wq.variant, "rho": wq.rho,
+                            "mean_s": tq, "keys_per_s": wq.n_keys / tq, "GBps": bq / tq / 1e9,
+                            "bound": "hbm" if wq.variant == "dense" else "alu",
+                            "timing": "10 launches back to back"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     sk.close()
