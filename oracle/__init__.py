@@ -30,5 +30,9 @@ Parity status of each function:
                    Monte Carlo.
   FQJL distortion magnitude: no closed form on the pages -> "parity unpinned";
                    only its decrease with m is tested.
+  attention.softmax_rows / decode_attention
+                   pinned: scipy.special.softmax; a two-key closed form; zero
+                   scores and zero scale give the mean of the values; key
+                   permutation invariance; a dominant key returns its value row.
 """
-from . import rng, sketch, qjl  # noqa: F401
+from . import rng, sketch, qjl, attention  # noqa: F401
