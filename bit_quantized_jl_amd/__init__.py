@@ -1,8 +1,8 @@
 """bit_quantized_jl_amd: the QJL key-cache sketch on AMD MI355X (gfx950).
 
 A thin Python layer over libqjl (include/qjl.h): quantize keys to packed sign
-bits plus norms, project queries, and estimate attention scores, all in
-hand-written HIP kernels.
+bits plus norms, project queries, estimate attention scores and form the
+decode-step attention output on them, all in hand-written HIP kernels.
 """
 from ._lib import (  # noqa: F401
     DTYPE_BF16,
@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     OK,
     QJLError,
     Sketch,
+    decode_attention,
+    decode_attention_workspace_size,
     destroy_sketch,
     generate_sketch_host,
     load,

@@ -52,6 +52,10 @@ def _declare(lib: ctypes.CDLL) -> None:
         "qjl_quantize_keys": (c.c_int, [vp, vp, i32, i64, i64, vp, vp, vp]),
         "qjl_project_query": (c.c_int, [vp, vp, i32, i64, vp, vp]),
         "qjl_score": (c.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp]),
+        "qjl_decode_attention_workspace_size": (c.c_int, [vp, i64, i64, i64, i32,
+                                                          c.POINTER(c.c_size_t)]),
+        "qjl_decode_attention": (c.c_int, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, f32,
+                                           vp, c.c_size_t, vp, vp]),
         "qjl_status_string": (c.c_char_p, [c.c_int]),
         "qjl_version": (c.c_char_p, []),
     }
@@ -264,3 +268,51 @@ def score(sk: Sketch, Sq, bits, norms, n_groups: int, n_q: int, n_k: int, scores
                             int(n_q), int(n_k), _ptr(scores_out), _stream(stream)),
            "qjl_score")
     return scores_out
+
+
+def decode_attention_workspace_size(sk: Sketch, n_groups: int, n_q: int, n_k: int,
+                                    d_v: int) -> int:
+    """Bytes of device workspace qjl_decode_attention needs for these counts."""
+    out = ctypes.c_size_t(0)
+    _check(load().qjl_decode_attention_workspace_size(sk.handle, int(n_groups), int(n_q),
+                                                      int(n_k), int(d_v), ctypes.byref(out)),
+           "qjl_decode_attention_workspace_size")
+    return int(out.value)
+
+
+def decode_attention(sk: Sketch, Sq, bits, norms, V, n_groups: int, n_q: int, n_k: int,
+                     softmax_scale: float, workspace=None, out=None, stream=None):
+    """Attention outputs [n_groups, n_q, d_v] float32 from the QJL scores.
+
+    V is [n_groups, n_k, d_v] float32 or bfloat16.  The workspace (a uint8
+    GPU tensor) is allocated here when not given.
+    """
+    import torch
+    for t, nm in ((Sq, "Sq"), (bits, "bits"), (norms, "norms"), (V, "V")):
+        _dev_tensor(t, nm)
+    if Sq.dtype != torch.float32 or norms.dtype != torch.float32:
+        raise TypeError("Sq and norms must be float32")
+    if bits.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("bits must be int32 (uint32 words)")
+    if V.dim() < 1:
+        raise ValueError("V must have a last dimension d_v")
+    d_v = int(V.shape[-1])
+    if (Sq.numel() < n_groups * n_q * sk.m or bits.numel() < n_groups * n_k * (sk.m // 32)
+            or norms.numel() < n_groups * n_k or V.numel() < n_groups * n_k * d_v):
+        raise ValueError("input buffers too small for the given counts")
+    need = decode_attention_workspace_size(sk, n_groups, n_q, n_k, d_v)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Sq.device)
+    _dev_tensor(workspace, "workspace")
+    if out is None:
+        out = torch.empty((n_groups, n_q, d_v), dtype=torch.float32, device=Sq.device)
+    _dev_tensor(out, "out")
+    if out.dtype != torch.float32 or out.numel() < n_groups * n_q * d_v:
+        raise ValueError("out must be float32 with n_groups * n_q * d_v elements")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().qjl_decode_attention(sk.handle, _ptr(Sq), _ptr(bits), _ptr(norms), _ptr(V),
+                                       _dtype_code(V), d_v, int(n_groups), int(n_q), int(n_k),
+                                       float(softmax_scale), _ptr(workspace), nbytes,
+                                       _ptr(out), _stream(stream)),
+           "qjl_decode_attention")
+    return out

@@ -272,6 +272,53 @@ qjl_status qjl_score(const qjl_sketch *sk, const float *Sq, const uint32_t *bits
                                scores_out, static_cast<hipStream_t>(stream)));
 }
 
+qjl_status qjl_decode_attention_workspace_size(const qjl_sketch *sk, int64_t n_groups,
+                                               int64_t n_q_per_group, int64_t n_k_per_group,
+                                               int32_t d_v, size_t *bytes_out) {
+  if (!sk || !bytes_out || n_groups < 0 || n_q_per_group < 0 || n_k_per_group < 0 || d_v < 1)
+    return QJL_ERR_INVALID_ARGUMENT;
+  if (n_groups == 0 || n_q_per_group == 0 || n_k_per_group == 0) {
+    *bytes_out = 0;
+    return QJL_OK;
+  }
+  qjl_status st = check_device(sk);
+  if (st != QJL_OK) return st;
+  *bytes_out = attention_workspace_bytes(sk, n_groups, n_q_per_group, n_k_per_group, d_v);
+  return QJL_OK;
+}
+
+qjl_status qjl_decode_attention(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                                int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                                float softmax_scale, void *workspace, size_t workspace_bytes,
+                                float *out, void *stream) {
+  if (!sk || n_groups < 0 || n_q_per_group < 0 || n_k_per_group < 0 || d_v < 1)
+    return QJL_ERR_INVALID_ARGUMENT;
+  if (v_dtype != QJL_DTYPE_F32 && v_dtype != QJL_DTYPE_BF16) return QJL_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(softmax_scale)) return QJL_ERR_INVALID_ARGUMENT;
+  if (n_groups == 0 || n_q_per_group == 0) return QJL_OK;
+  if (n_k_per_group == 0) return QJL_ERR_INVALID_ARGUMENT;  // softmax over no keys
+  if (!Sq || !bits || !norms || !V || !workspace || !out) return QJL_ERR_INVALID_ARGUMENT;
+  const size_t vsz = v_dtype == QJL_DTYPE_F32 ? 4 : 2;
+  if (!aligned(Sq, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(V, vsz) ||
+      !aligned(out, 4) || !aligned(workspace, 16))
+    return QJL_ERR_INVALID_ARGUMENT;
+  qjl_status st = check_device(sk);
+  if (st != QJL_OK) return st;
+  if (workspace_bytes <
+      attention_workspace_bytes(sk, n_groups, n_q_per_group, n_k_per_group, d_v))
+    return QJL_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float *ws = static_cast<float *>(workspace);
+  if (attention_fused_supported(sk, bits, V, v_dtype, d_v, n_k_per_group))
+    return from_hip(launch_attention_fused(sk, Sq, bits, norms, V, n_groups, n_q_per_group,
+                                           n_k_per_group, softmax_scale, ws, out, s));
+  hipError_t e = launch_score(sk, Sq, bits, norms, n_groups, n_q_per_group, n_k_per_group, ws, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(launch_attention_softmax(ws, V, v_dtype, d_v, n_groups, n_q_per_group,
+                                           n_k_per_group, softmax_scale, out, s));
+}
+
 }  // extern "C"
 
 namespace qjl {

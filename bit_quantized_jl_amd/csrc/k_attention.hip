@@ -1,0 +1,467 @@
+// Fused decode-step attention on the QJL scores.
+//
+// For query i of group g (QJL abstract on Majid Daliri's scholarfeed page:
+// the sketched keys serve attention; the KIVI abstract on the same site: a
+// decoding step reads the whole KV cache once):
+//     out[g][i][:] = sum_t softmax_t(scale * s[g][i][t]) * V[g][t][:],
+// with s the QJL estimate of q.k (the score of k_score_mfma.hip).  The scores
+// never reach HBM: each wave scores a 16-key tile on the matrix cores (the
+// exact fp8-limb method of the score kernel, shared through score_common.h),
+// folds it into an online softmax (running maximum and sum, in the exp2
+// domain) and adds the weighted value rows.  Each wave writes one partial
+// (maximum, sum, d_v-float weighted sum) per query to the caller's workspace;
+// attn_combine_kernel merges the partials of a query.
+//
+// The stream uses plain loads into registers, two 32-key stages deep: the
+// bits and norms of a stage (as the score kernel loads them) and its value
+// rows, lane l holding bf16 dimensions [8 (l % 16), 8 (l % 16) + 8) of key
+// 4 j + l / 16 of each 16-key tile (one 16-byte load covers four rows).
+// (LDS DMA for the bits, as in the score kernel, would make the compiler wait
+// for every load before using the value registers.)
+//
+// Shapes the fast path does not cover (d_v != 128, float values, m other than
+// 128, 256, 512 or 1024, unaligned buffers, 2^22 keys or more per group) take
+// a plain path: the
+// score kernel writes the scores to the workspace and attn_softmax_kernel
+// forms the weighted sum.
+#include "score_common.h"
+
+namespace qjl {
+
+namespace {
+
+using namespace sc;
+
+constexpr int AT_TILES = 2;   // 16-key tiles per stage
+constexpr int AT_STAGE = 16 * AT_TILES;  // keys per stage
+constexpr int AT_DV = 128;    // value width of the fast path
+constexpr int AT_PART = AT_DV + 4;  // floats per partial: sum, M, L, padding to 16 bytes
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <int T>
+struct AttnStage {
+  uint32_t w[AT_TILES][T];  // bits: words [T g, T g + T) of key 16 u + lane % 16
+  float n;                  // norm of key lane % 32 of the stage
+  uint4 v[AT_TILES][4];     // values: tile u, row 4 j + lane / 16, dims 8 (lane % 16) ..
+};
+
+// Buffer descriptors over keys [kbeg, kend) of a group: a load past kend
+// returns zeros (the descriptor's range check), so a stage needs no per-lane
+// clamps and every address is a 32-bit offset from the descriptor's base.
+struct KeyRange {
+  __amdgpu_buffer_rsrc_t bits, norm, v;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_rsrc(const void *base, int kbeg, int kend,
+                                                           int bytes_per_key) {
+  const uint32_t n = kend > kbeg ? (uint32_t)(kend - kbeg) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(static_cast<const char *>(base) + (int64_t)kbeg * bytes_per_key),
+      (short)0, (int)(n * (uint32_t)bytes_per_key), 0x00020000);
+}
+
+template <int T>
+__device__ __forceinline__ KeyRange key_range(const uint32_t *gbits, const float *gnorm,
+                                              const uint16_t *gV, int kbeg, int kend) {
+  return KeyRange{key_rsrc(gbits, kbeg, kend, 16 * T), key_rsrc(gnorm, kbeg, kend, 4),
+                  key_rsrc(gV, kbeg, kend, 2 * AT_DV)};
+}
+
+// Stage of keys [k0, k0 + AT_STAGE), k0 relative to the range's first key.
+template <int T>
+__device__ __forceinline__ void load_attn_stage(AttnStage<T> &s, const KeyRange &kr, int k0,
+                                                int lane) {
+  constexpr int W = 4 * T;
+  const int r = lane & 15, gq = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < AT_TILES; ++u) {
+    const int off = (int)(((uint32_t)(k0 + 16 * u + r) * W + T * gq) * 4u);
+    if constexpr (T == 1) {
+      s.w[u][0] = __builtin_amdgcn_raw_buffer_load_b32(kr.bits, off, 0, 0);
+    } else if constexpr (T == 2) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(kr.bits, off, 0, 0);
+      s.w[u][0] = v.x;
+      s.w[u][1] = v.y;
+    } else {
+#pragma unroll
+      for (int h = 0; h < T / 4; ++h) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(kr.bits, off + 16 * h, 0, 0);
+        s.w[u][4 * h] = v.x;
+        s.w[u][4 * h + 1] = v.y;
+        s.w[u][4 * h + 2] = v.z;
+        s.w[u][4 * h + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          kr.v, (int)((uint32_t)(k0 + 16 * u + 4 * j + gq) * (2u * AT_DV) + 16u * r), 0, 0);
+      s.v[u][j] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
+  s.n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      kr.norm, (int)(4u * (uint32_t)(k0 + (lane & (AT_STAGE - 1)))), 0, 0));
+}
+
+// Maximum and sum over the 16 lanes of each row (lane i exchanges with
+// i ^ 1, i ^ 2, then the mirrored lane of its half-row and of its row), the
+// result in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false));
+  return v;
+}
+
+// exp2(x - m) with m = -inf (nothing seen yet) giving 0 instead of NaN.
+__device__ __forceinline__ float exp2_shift(float x, float m) {
+  return m == -INFINITY ? 0.f : exp2f(x - m);
+}
+
+// Running softmax state of the queries a lane serves: per query pair qp,
+// member A = 2 qp and B = 2 qp + 1; M and L are the same in every lane.
+template <int QP>
+struct SoftmaxState {
+  float M[QP][2], L[QP][2];
+  float acc[QP][2][8];
+};
+
+template <int T, int QP>
+__device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOperands<T, QP> &qo,
+                                           int k0, int kend, int lane, int nqp,
+                                           float sl2, SoftmaxState<QP> &st) {
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < AT_TILES; ++u) {
+    const int key = k0 + 16 * u + (lane & 15);
+    float e[QP];
+    tile_limb_sums<T, QP>(s.w[u], qo, e);
+    const float nrm = __shfl(s.n, 16 * u + (lane & 15));
+    float vals[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q[4] = {s.v[u][j].x, s.v[u][j].y, s.v[u][j].z, s.v[u][j].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        vals[j][2 * h] = __uint_as_float(q[h] << 16);
+        vals[j][2 * h + 1] = __uint_as_float(q[h] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int qp = 0; qp < QP; ++qp) {
+      if (2 * qp >= nqp) break;  // uniform
+      const int qi = 2 * qp + (gq >> 1);
+      // logit in the exp2 domain: scale * log2(e) * score
+      const float x = (key < kend && qi < nqp) ? (e[qp] * qo.qscale[qp]) * nrm * sl2 : -INFINITY;
+      const float rm = row16_max(x);
+      const float tA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rm), 0));
+      const float tB = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rm), 32));
+      const float nA = fmaxf(st.M[qp][0], tA), nB = fmaxf(st.M[qp][1], tB);
+      const float p = exp2_shift(x, (gq >> 1) ? nB : nA);
+      const float rs = row16_sum(p);
+      const float sA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 0));
+      const float sB = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 32));
+      const float aA = exp2_shift(st.M[qp][0], nA), aB = exp2_shift(st.M[qp][1], nB);
+      st.L[qp][0] = st.L[qp][0] * aA + sA;
+      st.L[qp][1] = st.L[qp][1] * aB + sB;
+      st.M[qp][0] = nA;
+      st.M[qp][1] = nB;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        st.acc[qp][0][d] *= aA;
+        st.acc[qp][1][d] *= aB;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 4 * j + gq;  // key of this lane's value row in the tile
+        const float pA = __shfl(p, t), pB = __shfl(p, 32 + t);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          st.acc[qp][0][d] = fmaf(pA, vals[j][d], st.acc[qp][0][d]);
+          st.acc[qp][1][d] = fmaf(pB, vals[j][d], st.acc[qp][1][d]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ws layout: [G * nq][P][AT_PART]: the weighted sum, then M and L (exp2 domain).
+template <int T, int QP>
+__global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
+    const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
+    const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
+    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws, int P) {
+  constexpr int W = 4 * T;
+  constexpr int m = 32 * W;
+  constexpr int NQ = 2 * QP;
+  constexpr int JL = m / 64;
+  __shared__ __attribute__((aligned(16))) unsigned char sAimg[QueryOperands<T, QP>::IMAGE_BYTES];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // key positions within a group fit an int, and byte offsets into a
+  // group's rows a uint32 (the fused path takes nk < 2^22)
+  const int kbeg = (int)blockIdx.x * chunk;
+  const int kend = (int64_t)kbeg + chunk < nk ? kbeg + chunk : (int)nk;
+  const int nkb = kend > kbeg ? kend - kbeg : 0;  // keys of this workgroup
+  const int nstage_blk = (nkb + AT_STAGE - 1) / AT_STAGE;
+  const int ns = (nstage_blk - wave + SM_WAVES - 1) / SM_WAVES;
+  const int nsr = (ns + 1) & ~1;  // whole double-stage rounds
+  const int part = blockIdx.x * SM_WAVES + wave;
+
+  for (int64_t g = blockIdx.y; g < G; g += gridDim.y) {
+    const KeyRange kr = key_range<T>(bits + g * nk * (int64_t)W, norms + g * nk,
+                                     V + g * nk * (int64_t)AT_DV, kbeg, kend);
+    for (int64_t q0 = 0; q0 < nq; q0 += NQ) {
+      const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
+      float sv[NQ][JL];
+      load_query_values<m, NQ>(Sq + (g * nq + q0) * (int64_t)m, nqp, lane, sv);
+      if (q0 > 0) lds_barrier();  // every wave has read the previous pass's image
+      QueryOperands<T, QP> qo;
+      build_query_operands<T, QP>(sv, nqp, wave, lane, sAimg, cscale, qo);
+      __builtin_amdgcn_sched_barrier(0);
+      AttnStage<T> b0, b1;
+      load_attn_stage<T>(b0, kr, AT_STAGE * wave, lane);
+      load_attn_stage<T>(b1, kr, AT_STAGE * (wave + SM_WAVES), lane);
+      SoftmaxState<QP> st;
+#pragma unroll
+      for (int qp = 0; qp < QP; ++qp)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          st.M[qp][h] = -INFINITY;
+          st.L[qp][h] = 0.f;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) st.acc[qp][h][d] = 0.f;
+        }
+      for (int j = 0; j < nsr; j += 2) {
+        const int k0 = AT_STAGE * (wave + SM_WAVES * j);
+        attn_stage<T, QP>(b0, qo, k0, nkb, lane, nqp, sl2, st);
+        load_attn_stage<T>(b0, kr, k0 + 2 * AT_STAGE * SM_WAVES, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        attn_stage<T, QP>(b1, qo, k0 + AT_STAGE * SM_WAVES, nkb, lane, nqp, sl2, st);
+        load_attn_stage<T>(b1, kr, k0 + 3 * AT_STAGE * SM_WAVES, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // ---- this wave's partials: sum the four lane groups (each saw every
+      // fourth value row), then lanes 0..15 hold dims 8 lane .. 8 lane + 7
+#pragma unroll
+      for (int qp = 0; qp < QP; ++qp) {
+        if (2 * qp >= nqp) break;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qi = 2 * qp + h;
+          float a[8];
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            a[d] = st.acc[qp][h][d];
+            a[d] += __shfl_xor(a[d], 16);
+            a[d] += __shfl_xor(a[d], 32);
+          }
+          if (qi < nqp) {
+            float *dst = ws + ((g * nq + q0 + qi) * (int64_t)P + part) * AT_PART;
+            if (lane < 16) {
+              reinterpret_cast<float4 *>(dst)[2 * lane] = make_float4(a[0], a[1], a[2], a[3]);
+              reinterpret_cast<float4 *>(dst)[2 * lane + 1] = make_float4(a[4], a[5], a[6], a[7]);
+            }
+            if (lane == 0) {
+              dst[AT_DV] = st.M[qp][h];
+              dst[AT_DV + 1] = st.L[qp][h];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Merge the P partials of each (group, query) row: M = max M_p,
+// out = sum_p 2^(M_p - M) acc_p / sum_p 2^(M_p - M) L_p.  One wave per row,
+// lane l owns dims l and l + 64.
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ ws,
+                                                          int64_t rows, int P,
+                                                          float *__restrict__ out) {
+  const int lane = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const float *base = ws + row * (int64_t)P * AT_PART;
+    float M = -INFINITY;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * AT_PART + AT_DV]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int p = 0; p < P; ++p) {
+      const float *e = base + p * AT_PART;
+      const float w = exp2_shift(e[AT_DV], M);
+      L = fmaf(w, e[AT_DV + 1], L);
+      o0 = fmaf(w, e[lane], o0);
+      o1 = fmaf(w, e[lane + 64], o1);
+    }
+    const float inv = 1.f / L;
+    out[row * AT_DV + lane] = o0 * inv;
+    out[row * AT_DV + lane + 64] = o1 * inv;
+  }
+}
+
+// Plain path: scores already in the workspace ([G * nq][nk]); one workgroup
+// per (group, query) row.  Pass 1 finds the maximum, pass 2 forms the weights
+// and the weighted sum, threads splitting the value dimensions.
+template <typename TV>
+__global__ __launch_bounds__(256) void attn_softmax_kernel(const float *__restrict__ scores,
+                                                           const TV *__restrict__ V, int64_t rows,
+                                                           int64_t nq, int64_t nk, int dv,
+                                                           float sl2, float *__restrict__ out) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int64_t g = row / nq;
+    const float *s = scores + row * nk;
+    const TV *gv = V + g * nk * (int64_t)dv;
+    float mx = -INFINITY;
+    for (int64_t t = tid; t < nk; t += 256) mx = fmaxf(mx, s[t] * sl2);
+    red[tid] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+      __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+    float l = 0.f;
+    for (int64_t t = tid; t < nk; t += 256) l += exp2f(s[t] * sl2 - mx);
+    red[tid] = l;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    const float inv = 1.f / red[0];
+    __syncthreads();
+    for (int d = tid; d < dv; d += 256) {
+      float o = 0.f;
+      for (int64_t t = 0; t < nk; ++t) o = fmaf(exp2f(s[t] * sl2 - mx), load_as_f32(gv, t * dv + d), o);
+      out[row * dv + d] = o * inv;
+    }
+  }
+}
+
+// The fast path's grid: one resident round of workgroups over the keys of
+// all groups (as the score kernel), at most 65535 groups per launch row.
+template <int T, int QP>
+void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
+  static int resident = 0;
+  if (resident == 0) {
+    int dev = 0, cus = 256, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_partial_kernel<T, QP>,
+                                                     SM_THREADS, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    resident = cus * per_cu;
+  }
+  int64_t chunk = (G * nk + resident - 1) / resident;
+  chunk = (chunk + 2 * AT_STAGE * SM_WAVES - 1) / (2 * AT_STAGE * SM_WAVES) *
+          (2 * AT_STAGE * SM_WAVES);
+  *chunk_out = chunk;
+  *gx_out = (int)((nk + chunk - 1) / chunk);
+}
+
+template <int T, int QP>
+hipError_t launch_attn_t(const float *Sq, const uint32_t *bits, const float *norms,
+                         const uint16_t *V, int64_t G, int64_t nq, int64_t nk, float c, float sl2,
+                         float *ws, float *out, hipStream_t st) {
+  int64_t chunk = 0;
+  int gx = 0;
+  attn_grid<T, QP>(G, nk, &chunk, &gx);
+  const int P = gx * SM_WAVES;
+  dim3 grid((unsigned)gx, (unsigned)(G < 65535 ? G : 65535));
+  hipLaunchKernelGGL((attn_partial_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms,
+                     V, G, nq, nk, (int)chunk, c, sl2, ws, P);
+  const int64_t rows = G * nq;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)), dim3(64),
+                     0, st, ws, rows, P, out);
+  return hipGetLastError();
+}
+
+template <int T>
+int attn_partials_t(int64_t G, int64_t nk) {
+  int64_t chunk = 0;
+  int gx = 0;
+  attn_grid<T, 1>(G, nk, &chunk, &gx);
+  return gx * SM_WAVES;
+}
+
+}  // namespace
+
+// Sketch sizes with a fused instantiation (T = m / 128 words per lane group).
+static bool fused_m(int m) { return m == 128 || m == 256 || m == 512 || m == 1024; }
+
+// Whether the fused path serves this call (the rest takes the plain path).
+bool attention_fused_supported(const qjl_sketch *sk, const uint32_t *bits, const void *V,
+                               int v_dtype, int dv, int64_t nk) {
+  const int m = sk->host.m;
+  return v_dtype == QJL_DTYPE_BF16 && dv == AT_DV && fused_m(m) &&
+         nk < (int64_t(1) << 22) && ((uintptr_t)bits & 15) == 0 && ((uintptr_t)V & 15) == 0;
+}
+
+size_t attention_workspace_bytes(const qjl_sketch *sk, int64_t G, int64_t nq, int64_t nk, int dv) {
+  const int m = sk->host.m;
+  size_t fused = 0;
+  if (dv == AT_DV && fused_m(m) && nk < (int64_t(1) << 22)) {
+    int P = 0;
+    switch (m / 128) {
+      case 1: P = attn_partials_t<1>(G, nk); break;
+      case 2: P = attn_partials_t<2>(G, nk); break;
+      case 4: P = attn_partials_t<4>(G, nk); break;
+      case 8: P = attn_partials_t<8>(G, nk); break;
+      default: P = 0;
+    }
+    fused = (size_t)G * nq * P * AT_PART * sizeof(float);
+  }
+  const size_t plain = (size_t)G * nq * nk * sizeof(float);
+  return fused > plain ? fused : plain;
+}
+
+hipError_t launch_attention_fused(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                  const float *norms, const void *V, int64_t G, int64_t nq,
+                                  int64_t nk, float scale, float *ws, float *out,
+                                  hipStream_t st) {
+  const HostSketch &h = sk->host;
+  const float c = estimator_scale(h.m, h.rho);
+  const float sl2 = scale * LOG2E;
+  const uint16_t *Vb = static_cast<const uint16_t *>(V);
+  // One query pair per pass: a second pair's accumulators would not fit the
+  // registers beside two stages of value rows.
+  switch (h.m / 128) {
+    case 1: return launch_attn_t<1, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 2: return launch_attn_t<2, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 4: return launch_attn_t<4, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 8: return launch_attn_t<8, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention_softmax(const float *scores, const void *V, int v_dtype, int dv,
+                                    int64_t G, int64_t nq, int64_t nk, float scale, float *out,
+                                    hipStream_t st) {
+  const int64_t rows = G * nq;
+  const unsigned grid = (unsigned)(rows < 65535 ? rows : 65535);
+  const float sl2 = scale * LOG2E;
+  if (v_dtype == QJL_DTYPE_F32)
+    hipLaunchKernelGGL(attn_softmax_kernel<float>, dim3(grid), dim3(256), 0, st, scores,
+                       static_cast<const float *>(V), rows, nq, nk, dv, sl2, out);
+  else
+    hipLaunchKernelGGL(attn_softmax_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, scores,
+                       static_cast<const uint16_t *>(V), rows, nq, nk, dv, sl2, out);
+  return hipGetLastError();
+}
+
+}  // namespace qjl

@@ -41,65 +41,13 @@
 // (key r, group g) takes words [T g, T g + T) of key r, one word per MFMA, so
 // bit p of word (T g + t) is fp4 element 8 (p % 4) + p / 4 of MFMA t; the A
 // operand builder maps each fp8 byte to that same contraction index.
-#include "device_common.h"
+#include "score_common.h"
 
 namespace qjl {
 
 namespace {
 
-typedef int v8i_t __attribute__((ext_vector_type(8)));
-typedef float v4f_t __attribute__((ext_vector_type(4)));
-
-constexpr int SM_THREADS = 256;
-constexpr int SM_WAVES = 4;
-
-// e4m3 bit pattern of an integer |v| <= 64 with at most 4 significant bits:
-// such a value is exact in float32, whose sign, exponent (rebased from 127 to
-// 7) and top three mantissa bits are the e4m3 fields.
-__device__ __forceinline__ uint32_t e4m3_of_int(int v) {
-  const uint32_t f = __float_as_uint((float)v);
-  const uint32_t mag = ((f >> 20) & 0x7FFu) - (120u << 3);
-  return v == 0 ? 0u : (((f >> 24) & 0x80u) | (mag & 0x7Fu));
-}
-
-// Balanced base-32 digit c (0 = most significant) of X, |X| <= 2^23.
-__device__ __forceinline__ int digit_of(int X, int c) {
-  int rem = X, L = 0;
-#pragma unroll
-  for (int k = 4; k >= 0; --k) {
-    const int d = ((rem + 16) & 31) - 16;
-    if (k == c) L = d;
-    rem = (rem - d) >> 5;
-  }
-  return L;
-}
-
-// Wavefront reductions with DPP: row_shr 1, 2, 4, 8 fold each 16-lane row
-// into its lane 15, row_bcast 15 and 31 fold the rows into lane 63, which is
-// then read as a scalar.  Lanes without a DPP source keep the identity.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ int dpp(int identity, int v) {
-  return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROWMASK, 0xf, false);
-}
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  int x = __float_as_int(v);  // v >= 0: max on floats, identity 0
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x111, 0xf>(0, x))));
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x112, 0xf>(0, x))));
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x114, 0xf>(0, x))));
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x118, 0xf>(0, x))));
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x142, 0xa>(0, x))));
-  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<0x143, 0xc>(0, x))));
-  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
-}
-__device__ __forceinline__ int wave_sum(int x) {
-  x += dpp<0x111, 0xf>(0, x);
-  x += dpp<0x112, 0xf>(0, x);
-  x += dpp<0x114, 0xf>(0, x);
-  x += dpp<0x118, 0xf>(0, x);
-  x += dpp<0x142, 0xa>(0, x);
-  x += dpp<0x143, 0xc>(0, x);
-  return __builtin_amdgcn_readlane(x, 63);
-}
+using namespace sc;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
@@ -119,14 +67,6 @@ struct Ring {
   static constexpr int STAGE_BYTES = BITS_BYTES + SM_STAGE * 4;
   static constexpr int L = T + 1;                          // DMA instructions per stage
 };
-
-// s_waitcnt vmcnt(n) leaving the other counters unconstrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int T>
 __device__ __forceinline__ void wait_stages(int pending) {
@@ -159,22 +99,6 @@ __device__ __forceinline__ void issue_stage(unsigned char *slot, const uint32_t 
   __builtin_amdgcn_global_load_lds((const gbl_void_t *)(gnorm + key),
                                    (lds_void_t *)(slot + Ring<T>::BITS_BYTES), 4, 0, 0);
 }
-
-// Workgroup barrier for LDS data only.  __syncthreads() also fences global
-// memory, which would wait for every ring DMA in flight; LDS writes of a wave
-// are complete once its lgkmcnt drains.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
-typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-  return (uint32_t)(uintptr_t)((const lds_u8_t *)p);
-}
-
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Read one ring stage for this lane: the T words of key 16 u + (lane % 16),
 // lane group lane / 16, for the 4 tiles u, and the 4 norms.  The reads are
@@ -271,37 +195,20 @@ struct StageRead<8> {
   }
 };
 
-// One 16-key tile: expand the bits to the fp4 operand, run the MFMAs against
-// the query limbs, combine the limb rows and store the scores of the tile.
+// One 16-key tile: the scores of its keys (tile_limb_sums) scaled by the
+// query's exponent and the key norm, stored by the lanes of lane groups 0 and 2.
 template <int T, int QP>
-__device__ __forceinline__ void score_tile(const uint32_t *wb, float nrm, const v8i_t (&A)[QP][T],
-                                           const v4f_t (&cinit)[QP], const float (&wgt)[4],
-                                           const float (&qscale)[QP], int64_t key, int64_t kend,
-                                           int gq, int nqp, float *__restrict__ outq, int64_t nk) {
-  v4f_t acc[QP];
-#pragma unroll
-  for (int qp = 0; qp < QP; ++qp) acc[qp] = cinit[qp];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const uint32_t w = wb[t];
-    const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
-                          (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
-                          0, 0, 0, 0};
-#pragma unroll
-    for (int qp = 0; qp < QP; ++qp)
-      acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[qp][t], B, acc[qp], 0, 4, 0,
-                                                                  127, 0, 127);
-  }
+__device__ __forceinline__ void score_tile(const uint32_t *wb, float nrm,
+                                           const QueryOperands<T, QP> &qo, int64_t key,
+                                           int64_t kend, int gq, int nqp,
+                                           float *__restrict__ outq, int64_t nk) {
+  float e[QP];
+  tile_limb_sums<T, QP>(wb, qo, e);
 #pragma unroll
   for (int qp = 0; qp < QP; ++qp) {
-    float e = acc[qp][0] * wgt[0];
-    e = fmaf(acc[qp][1], wgt[1], e);
-    e = fmaf(acc[qp][2], wgt[2], e);
-    e = fmaf(acc[qp][3], wgt[3], e);
-    e += __shfl_xor(e, 16);
     const int qi = 2 * qp + (gq >> 1);
     if ((gq & 1) == 0 && key < kend && qi < nqp)
-      __builtin_nontemporal_store((e * qscale[qp]) * nrm, outq + qi * nk + key);
+      __builtin_nontemporal_store((e[qp] * qo.qscale[qp]) * nrm, outq + qi * nk + key);
   }
 }
 
@@ -316,8 +223,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
   constexpr int R = Ring<T>::R;
   constexpr int SB = Ring<T>::STAGE_BYTES;
   constexpr int JL = (m + 63) / 64;            // query coordinates per lane
-  constexpr int A_BYTES = QP * T * 64 * 32;    // the fp8 operand image
-  __shared__ __attribute__((aligned(16))) unsigned char sAimg[A_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sAimg[QueryOperands<T, QP>::IMAGE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sRing[SM_WAVES][R][SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -336,19 +242,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
       // ---- query values first (plain loads), then the first key stages
       // (LDS DMA), so the query set-up below overlaps the stream's latency.
-      // (m is a multiple of 128 here, so every lane's coordinates exist; the
-      // loads are unconditional so the compiler can count them past the DMA.)
-      static_assert(m % 64 == 0, "whole coordinate blocks per lane");
       float sv[NQ][JL];
-#pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) {
-        const float *src = Sq + (g * nq + q0 + (qi < nqp ? qi : 0)) * (int64_t)m;
-#pragma unroll
-        for (int b = 0; b < JL; ++b) {
-          const float v = src[lane + 64 * b];
-          sv[qi][b] = qi < nqp ? v : 0.f;
-        }
-      }
+      load_query_values<m, NQ>(Sq + (g * nq + q0) * (int64_t)m, nqp, lane, sv);
 #pragma unroll
       for (int j = 0; j < R - 1; ++j)
         issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
@@ -357,134 +252,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       // compiler cannot count past LDS DMA and would wait for the stages too.)
       wait_vmcnt<(R - 1) * Ring<T>::L>();
       if (q0 > 0) lds_barrier();  // every wave has read the previous pass's image
-      // ---- per query: exponent F, fixed-point values X_j = rint(Sq_j 2^F),
-      // balanced base-32 digits, digit sums C_c (every wave computes these for
-      // the whole query) and the operand image (each wave writes the bytes of
-      // coordinate blocks j / 64 = wave mod 4).  A query slot past nqp only
-      // zeroes its bytes.
-      int Fq[NQ];
-      int Cq[NQ][5];
-#pragma unroll
-      for (int qi = 0; qi < NQ; ++qi) {
-        Fq[qi] = 0;
-#pragma unroll
-        for (int c = 0; c < 5; ++c) Cq[qi][c] = 0;
-        if (qi >= nqp) {  // empty slot: zero bytes at this wave's coordinates
-#pragma unroll
-          for (int b = 0; b < JL; ++b) {
-            if ((b & 3) != (wave & 3)) continue;
-            const int j = lane + 64 * b;
-            const int wi = j >> 5, jj = j & 31, sreg = jj & 3;
-            const int k = 32 * (wi / T) + 8 * sreg + (jj >> 2);
-            const int grp = (k & 63) >> 4, e = (k >> 6) * 16 + (k & 15);
-            const uint32_t dst = lds_address(
-                sAimg + (((qi >> 1) * T + wi % T) * 64 + 16 * grp + 8 * (qi & 1)) * 32 + e);
-            asm volatile(
-                "ds_write_b8 %0, %1\n\tds_write_b8 %0, %1 offset:32\n\t"
-                "ds_write_b8 %0, %1 offset:64\n\tds_write_b8 %0, %1 offset:96\n\t"
-                "ds_write_b8 %0, %1 offset:128\n\tds_write_b8 %0, %1 offset:160\n\t"
-                "ds_write_b8 %0, %1 offset:192\n\tds_write_b8 %0, %1 offset:224"
-                :
-                : "v"(dst), "v"(0u)
-                : "memory");
-          }
-          continue;
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int b = 0; b < JL; ++b) amax = fmaxf(amax, fabsf(sv[qi][b]));
-        amax = wave_max_nonneg(amax);
-        int e2 = 0;
-        (void)frexpf(amax, &e2);
-        const int F = amax > 0.f ? 23 - e2 : 0;
-        const int qp = qi >> 1, qq = qi & 1;
-        int C[5] = {0, 0, 0, 0, 0};
-#pragma unroll
-        for (int b = 0; b < JL; ++b) {
-          const int j = lane + 64 * b;
-          const int X = (int)rintf(ldexpf(sv[qi][b], F));
-          int L[5];
-          int rem = X;
-#pragma unroll
-          for (int c = 4; c >= 0; --c) {
-            L[c] = ((rem + 16) & 31) - 16;
-            rem = (rem - L[c]) >> 5;
-          }
-          // coordinate j -> (MFMA t, lane group, byte e) of the fp8 operand:
-          // word wi = j / 32 is fp4 register sreg = j % 4, element eb of lane
-          // group gb = wi / T in MFMA t = wi % T; contraction index
-          // k = 32 gb + eb sits in fp8 byte e of lane group (k % 64) / 16.
-          const int wi = j >> 5, jj = j & 31, sreg = jj & 3;
-          const int wj = sreg == 0 ? 5 : (sreg == 3 ? 0 : 1);
-#pragma unroll
-          for (int c = 0; c < 5; ++c) C[c] += wj * L[c];
-          if ((b & 3) == (wave & 3)) {
-            const int eb = 8 * sreg + (jj >> 2);
-            const int k = 32 * (wi / T) + eb;
-            const int t = wi % T;
-            const int grp = (k & 63) >> 4, e = (k >> 6) * 16 + (k & 15);
-            const int f = sreg == 0 ? 4 : (sreg == 1 ? 2 : (sreg == 2 ? 1 : -1));
-            const uint32_t dst =
-                lds_address(sAimg + ((qp * T + t) * 64 + 16 * grp + 8 * qq) * 32 + e);
-            // Limb rows c = 0..4, zero rows 5..7.  Written in asm: as plain
-            // stores the compiler would first wait for the key DMA in flight.
-            asm volatile(
-                "ds_write_b8 %0, %1\n\tds_write_b8 %0, %2 offset:32\n\t"
-                "ds_write_b8 %0, %3 offset:64\n\tds_write_b8 %0, %4 offset:96\n\t"
-                "ds_write_b8 %0, %5 offset:128\n\tds_write_b8 %0, %6 offset:160\n\t"
-                "ds_write_b8 %0, %6 offset:192\n\tds_write_b8 %0, %6 offset:224"
-                :
-                : "v"(dst), "v"(e4m3_of_int(f * L[0])), "v"(e4m3_of_int(f * L[1])),
-                  "v"(e4m3_of_int(f * L[2])), "v"(e4m3_of_int(f * L[3])),
-                  "v"(e4m3_of_int(f * L[4])), "v"(0u)
-                : "memory");
-          }
-        }
-        Fq[qi] = F;
-#pragma unroll
-        for (int c = 0; c < 5; ++c) Cq[qi][c] = wave_sum(C[c]);
-      }
-      lds_barrier();  // the image is complete
-      // The reads wait for themselves, not for the key DMA in flight.
-      v8i_t A[QP][T];
-#pragma unroll
-      for (int qp = 0; qp < QP; ++qp)
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-          u32x4_t a0, a1;
-          asm volatile(
-              "ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
-              : "=&v"(a0), "=&v"(a1)
-              : "v"(lds_address(sAimg + ((qp * T + t) * 64 + lane) * 32))
-              : "memory");
-          A[qp][t] = v8i_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-        }
-      // per-lane epilogue constants: accumulator rows 4 gq + v hold limb
-      // c = (4 gq + v) % 8 of query member gq / 2
-      float wgt[4];
-      v4f_t cinit[QP];
-      float qscale[QP];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = (4 * gq + v) & 7;
-        wgt[v] = c < 5 ? (float)(1 << (5 * (4 - c))) : 0.f;
-      }
-#pragma unroll
-      for (int qp = 0; qp < QP; ++qp) {
-        const bool hi = (gq >> 1) != 0;
-        const int qi0 = 2 * qp, qi1 = 2 * qp + 1;
-        const bool qv = (hi ? qi1 : qi0) < nqp;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          // limb c = v in even lane groups, c = 4 + v (a limb only for v = 0) in odd ones
-          const int lo = hi ? Cq[qi1][v] : Cq[qi0][v];
-          const int up = v == 0 ? (hi ? Cq[qi1][4] : Cq[qi0][4]) : 0;
-          cinit[qp][v] = qv ? -(float)((gq & 1) ? up : lo) : 0.f;
-        }
-        const int F = hi ? Fq[qi1] : Fq[qi0];
-        qscale[qp] = qv ? ldexpf(cscale, -F) : 0.f;
-      }
+      QueryOperands<T, QP> qo;
+      build_query_operands<T, QP>(sv, nqp, wave, lane, sAimg, cscale, qo);
       // ---- stream this wave's stages through the ring
       for (int j = 0; j < ns; ++j) {
         if (j + R - 1 < ns)
@@ -501,8 +270,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
                 lds_address(slot + Ring<T>::BITS_BYTES + (lane & 15) * 4));
 #pragma unroll
         for (int u = 0; u < SM_STAGE / 16; ++u)
-          score_tile<T, QP>(sr.w[u], sr.n[u], A, cinit, wgt, qscale, k0 + 16 * u + (lane & 15),
-                            kend, gq, nqp, out + (g * nq + q0) * nk, nk);
+          score_tile<T, QP>(sr.w[u], sr.n[u], qo, k0 + 16 * u + (lane & 15), kend, gq, nqp,
+                            out + (g * nq + q0) * nk, nk);
       }
     }
   }

@@ -89,6 +89,17 @@ hipError_t launch_score(const qjl_sketch *sk, const float *Sq, const uint32_t *b
                         const float *norms, int64_t G, int64_t nq, int64_t nk, float *scores,
                         hipStream_t st);
 
+// Decode attention (k_attention.hip).
+bool attention_fused_supported(const qjl_sketch *sk, const uint32_t *bits, const void *V,
+                               int v_dtype, int dv, int64_t nk);
+size_t attention_workspace_bytes(const qjl_sketch *sk, int64_t G, int64_t nq, int64_t nk, int dv);
+hipError_t launch_attention_fused(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                  const float *norms, const void *V, int64_t G, int64_t nq,
+                                  int64_t nk, float scale, float *ws, float *out, hipStream_t st);
+hipError_t launch_attention_softmax(const float *scores, const void *V, int v_dtype, int dv,
+                                    int64_t G, int64_t nq, int64_t nk, float scale, float *out,
+                                    hipStream_t st);
+
 // Host-computed data the score kernels take per launch.
 float estimator_scale(int m, float rho);
 

@@ -172,6 +172,41 @@ qjl_status qjl_score(const qjl_sketch *sk, const float *Sq, const uint32_t *bits
                      const float *norms, int64_t n_groups, int64_t n_q_per_group,
                      int64_t n_k_per_group, float *scores_out, void *stream);
 
+/*
+ * Workspace that qjl_decode_attention needs for these sizes, in bytes
+ * (*bytes_out; 0 when any count is 0).  The caller allocates it (device
+ * memory, 16-byte aligned) and may reuse it across calls on one stream.
+ * Errors: NULL sk or bytes_out, negative counts, d_v < 1 -> INVALID_ARGUMENT.
+ */
+qjl_status qjl_decode_attention_workspace_size(const qjl_sketch *sk, int64_t n_groups,
+                                               int64_t n_q_per_group, int64_t n_k_per_group,
+                                               int32_t d_v, size_t *bytes_out);
+
+/*
+ * Attention output of one decoding step on the estimated scores (the QJL
+ * abstract: the sketched keys serve the attention over the KV cache; the
+ * KIVI abstract: decoding reads the whole cache once per token):
+ *   out[g][i][:] = sum_t softmax_t(softmax_scale * s[g][i][t]) * V[g n_k + t][:]
+ * with s[g][i][t] the estimate of qjl_score (never written to memory on the
+ * fast path).  Pass softmax_scale = 1/sqrt(d) for the usual attention.
+ * Sq, bits, norms as for qjl_score; V: device [n_groups*n_k][d_v] in
+ * v_dtype (values are not sketched); out: device float[n_groups][n_q][d_v];
+ * workspace: device, 16-byte aligned, at least the size above (holds the
+ * per-wave softmax partials, or the scores on the plain path).  The fast
+ * path takes bf16 values with d_v = 128, m of 128, 256, 512 or 1024, fewer
+ * than 2^22 keys per group and 16-byte aligned bits and V; other shapes give
+ * the same result through a plain path.  Calls sharing one workspace must be ordered (one stream).
+ * n_groups == 0 or n_q == 0 -> no-op.  Errors: NULL pointers, negative
+ * counts, n_k == 0 with n_q > 0, d_v < 1, bad v_dtype, misalignment,
+ * workspace_bytes below the required size, softmax_scale not finite, sketch
+ * of another device -> INVALID_ARGUMENT; launch failure -> DEVICE.
+ */
+qjl_status qjl_decode_attention(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                                int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                                float softmax_scale, void *workspace, size_t workspace_bytes,
+                                float *out, void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *qjl_status_string(qjl_status s);
 

@@ -6,8 +6,17 @@ Tolerances:
     legitimately flip a sign; such coordinates are counted and reported;
   * norms: relative 1e-5;
   * projected queries: absolute 1e-5 * ||q|| * sqrt(m);
-  * scores (the oracle scoring the GPU's bits in float64):
-    |gpu - ref| <= 1e-3 |ref| + 1e-4.
+  * scores: |gpu - ref| <= 1e-3 |ref| + 1e-4, where ref is the oracle's
+    float64 score of the oracle's own bits, norms and projected query; a sign
+    bit that legitimately differs inside the band adds its whole effect on
+    the estimate, 2 c ||k|| |Sq_j| (c the estimator constant), to the bound;
+  * decode attention: a change dx_t in logit t moves a softmax-weighted mean
+    of the value rows by at most 2 max_t |dx_t| max|V| (first order), so
+    |gpu - ref| <= 2 dx max|V| + 1e-5 max|V| + 1e-5 |ref| per group, dx
+    bounding the float32 error of the logits: scale (8 eps |s| +
+    eps c ||k|| m max|Sq|) with eps = 2^-24 (the products that form a logit,
+    and the query's fixed-point digits), plus the in-band slack above; the
+    1e-5 terms cover the float32 weighted sums.
 """
 from __future__ import annotations
 
@@ -50,9 +59,23 @@ def check_norms(gpu: np.ndarray, ref: np.ndarray) -> None:
     assert np.all(err <= tol), f"norm error {np.max(err / np.maximum(ref, 1e-30))}"
 
 
-def check_scores(gpu: np.ndarray, ref: np.ndarray) -> None:
+def inband_slack(gpu_bits: np.ndarray, ref_bits: np.ndarray, Sq: np.ndarray,
+                 norms: np.ndarray, m: int, rho: float, G: int, nq: int, nk: int) -> np.ndarray:
+    """[G, nq, nk] bound on how much sign bits that differ from the oracle's
+    (only ever inside the band, which check_bits asserts) move each score."""
+    flip = (oq.unpack_bits(gpu_bits, m) != oq.unpack_bits(ref_bits, m)).astype(np.float64)
+    c = oq.estimator_constant(m, rho)
+    F = flip.reshape(G, nk, m)
+    A = np.abs(np.asarray(Sq, dtype=np.float64)).reshape(G, nq, m)
+    nr = np.asarray(norms, dtype=np.float64).reshape(G, 1, nk)
+    return 2.0 * c * nr * np.einsum("gij,gtj->git", A, F)
+
+
+def check_scores(gpu: np.ndarray, ref: np.ndarray, slack=None) -> None:
     err = np.abs(gpu - ref)
     tol = SCORE_RTOL * np.abs(ref) + SCORE_ATOL
+    if slack is not None:
+        tol = tol + np.reshape(slack, tol.shape)
     if not np.all(err <= tol):
         i = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"score mismatch at {i}: gpu {gpu[i]} ref {ref[i]} "
@@ -63,3 +86,32 @@ def check_projection(gpu: np.ndarray, ref: np.ndarray, q: np.ndarray, m: int) ->
     qn = np.sqrt((q * q).sum(axis=1))[:, None]
     err = np.abs(gpu - ref)
     assert np.all(err <= 1e-5 * qn * np.sqrt(m) + 1e-30), float(np.max(err / (qn * np.sqrt(m))))
+
+
+EPS32 = 2.0 ** -24
+
+
+def logit_error_bound(scores: np.ndarray, Sq: np.ndarray, norms: np.ndarray, m: int,
+                      rho: float, scale: float, G: int, nq: int, nk: int,
+                      slack=None) -> np.ndarray:
+    """[G, nq] bound on the float32 error of the logits scale * s of a row."""
+    s = np.abs(np.asarray(scores, dtype=np.float64)).reshape(G, nq, nk)
+    c = oq.estimator_constant(m, rho)
+    kmax = np.abs(np.asarray(norms, dtype=np.float64)).reshape(G, nk).max(axis=1)
+    qmax = np.abs(np.asarray(Sq, dtype=np.float64)).reshape(G, nq, m).max(axis=2)
+    dx = abs(scale) * (8 * EPS32 * s.max(axis=2) + EPS32 * c * kmax[:, None] * m * qmax)
+    if slack is not None:
+        dx = dx + abs(scale) * np.reshape(slack, (G, nq, nk)).max(axis=2)
+    return dx
+
+
+def check_attention(gpu: np.ndarray, ref: np.ndarray, V: np.ndarray, dx: np.ndarray) -> None:
+    """gpu, ref: [G, nq, d_v]; V: [G * nk, d_v]; dx: [G, nq]."""
+    G = ref.shape[0]
+    vmax = np.abs(np.asarray(V, dtype=np.float64)).reshape(G, -1).max(axis=1)
+    tol = ((2 * dx + 1e-5) * vmax[:, None])[:, :, None] + 1e-5 * np.abs(ref)
+    err = np.abs(gpu - ref)
+    if not np.all(err <= tol):
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"attention mismatch at {i}: gpu {gpu[i]} ref {ref[i]} tol {tol[i]} "
+                             f"({int((err > tol).sum())} of {err.size})")

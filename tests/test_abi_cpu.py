@@ -85,6 +85,10 @@ def test_null_handles_rejected():
     assert lib.qjl_quantize_keys(None, None, 1, 4, 0, None, None, None) == 1
     assert lib.qjl_project_query(None, None, 1, 4, None, None) == 1
     assert lib.qjl_score(None, None, None, None, 1, 1, 1, None, None) == 1
+    sz = ctypes.c_size_t(7)
+    assert lib.qjl_decode_attention_workspace_size(None, 1, 1, 1, 128, ctypes.byref(sz)) == 1
+    assert lib.qjl_decode_attention(None, None, None, None, None, 1, 128, 1, 1, 1, 1.0, None, 0,
+                                    None, None) == 1
 
 
 @pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (0, 128, 512), (7, 16, 32), (3, 100, 64)])

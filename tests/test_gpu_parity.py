@@ -15,7 +15,7 @@ import torch
 import bit_quantized_jl_amd as qj
 import workloads as wl
 from gpu_helpers import (bits_np, check_bits, check_norms, check_projection, check_scores,
-                         to_np_f64)
+                         inband_slack, to_np_f64)
 from oracle import qjl as oq
 from oracle import sketch as osk
 
@@ -49,7 +49,7 @@ def run_quantize_case(w: wl.Workload, n_k: int | None = None, base: int = 0):
     nband = check_bits(bits_np(bits), rb, mg, w.m)
     check_norms(to_np_f64(norms), rn)
     sk.close()
-    return nband, K, bits, norms
+    return nband, K, bits, norms, rb, rn
 
 
 QUANT_CASES = [
@@ -137,7 +137,7 @@ def test_score_dither_constant():
                          ids=lambda w: w.name)
 def test_end_to_end_scores(w):
     note("e2e", w.name)
-    _, K, bits, norms = run_quantize_case(w)
+    _, K, bits, norms, rb, rn = run_quantize_case(w)
     q = wl.make_queries(w, "cpu").to(DEV)
     sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
     Sq = qj.project_query(sk, q)
@@ -145,9 +145,10 @@ def test_end_to_end_scores(w):
     torch.cuda.synchronize()
     ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
     Sq_ref = oq.project(ref, to_np_f64(q), w.dtype)
-    _, rn, _, _ = oq.quantize(ref, to_np_f64(K[:1]), w.dtype)
-    s_ref = oq.score(Sq_ref, bits_np(bits), to_np_f64(norms), w.m, w.rho, w.groups, w.n_q, w.n_k)
-    check_scores(to_np_f64(out), s_ref)
+    # the oracle's own bits and norms; in-band sign differences widen the bound
+    s_ref = oq.score(Sq_ref, rb, rn, w.m, w.rho, w.groups, w.n_q, w.n_k)
+    slack = inband_slack(bits_np(bits), rb, Sq_ref, rn, w.m, w.rho, w.groups, w.n_q, w.n_k)
+    check_scores(to_np_f64(out), s_ref, slack)
     sk.close()
 
 
@@ -247,7 +248,7 @@ def full_size_quantize(w: wl.Workload, sample=3000):
     return sk, K, norms, bits
 
 
-def full_size_score(w: wl.Workload, sk, norms, bits, groups_checked=4):
+def full_size_score(w: wl.Workload, sk, K, norms, bits, groups_checked=4):
     q = wl.make_queries(w, DEV)
     Sq = qj.project_query(sk, q)
     out = qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k)
@@ -256,12 +257,19 @@ def full_size_score(w: wl.Workload, sk, norms, bits, groups_checked=4):
     rs = np.random.default_rng(2)
     gs = sorted(set([0, w.groups - 1] + rs.choice(w.groups, groups_checked, replace=False).tolist()))
     for g in gs:
+        note("full score group", g)
         sl = slice(g * w.n_k, (g + 1) * w.n_k)
         qd = to_np_f64(q[g * w.n_q:(g + 1) * w.n_q])
         Sq_ref = oq.project(ref, qd, w.dtype)
         check_projection(to_np_f64(Sq[g * w.n_q:(g + 1) * w.n_q]), Sq_ref, qd, w.m)
-        s_ref = oq.score(Sq_ref, bits_np(bits[sl]), to_np_f64(norms[sl]), w.m, w.rho, 1, w.n_q, w.n_k)
-        check_scores(to_np_f64(out[g]), s_ref[0])
+        # the oracle quantizes this group's keys itself
+        rb, rn, mg, _ = oq.quantize(ref, to_np_f64(K[sl]), w.dtype,
+                                    key_index=np.arange(sl.start, sl.stop))
+        gb = bits_np(bits[sl])
+        check_bits(gb, rb, mg, w.m)
+        s_ref = oq.score(Sq_ref, rb, rn, w.m, w.rho, 1, w.n_q, w.n_k)
+        slack = inband_slack(gb, rb, Sq_ref, rn, w.m, w.rho, 1, w.n_q, w.n_k)
+        check_scores(to_np_f64(out[g]), s_ref[0], slack[0])
     # every group: finite and zero exactly where the norm is zero
     assert torch.isfinite(out).all()
 
@@ -269,17 +277,14 @@ def full_size_score(w: wl.Workload, sk, norms, bits, groups_checked=4):
 def test_full_size_decode_7b():
     w = wl.DECODE_7B
     sk, K, norms, bits = full_size_quantize(w)
-    del K
-    full_size_score(w, sk, norms, bits)
+    full_size_score(w, sk, K, norms, bits)
     sk.close()
 
 
 def test_full_size_long_context():
     w = wl.LONG_CTX
     sk, K, norms, bits = full_size_quantize(w, sample=2000)
-    del K
-    torch.cuda.empty_cache()
-    full_size_score(w, sk, norms, bits, groups_checked=2)
+    full_size_score(w, sk, K, norms, bits, groups_checked=2)
     sk.close()
 
 
@@ -291,6 +296,5 @@ def test_full_size_prefill():
 @pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER], ids=lambda w: w.name)
 def test_full_size_fqjl(w):
     sk, K, norms, bits = full_size_quantize(w, sample=2000)
-    del K
-    full_size_score(w, sk, norms, bits, groups_checked=2)
+    full_size_score(w, sk, K, norms, bits, groups_checked=2)
     sk.close()

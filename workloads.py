@@ -10,7 +10,8 @@ describe: keys of Llama-2-7B-like models (32 heads, head dimension 128), with
 per-channel outliers, which KIVI reports for keys.  No dataset or weights are
 used; these tensors stand in for real caches.
 
-Seeds: keys 1, queries 2, outlier channels 3, Student-t channel scales 4.
+Seeds: keys 1, queries 2, outlier channels 3, Student-t channel scales 4,
+values 5.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ SEED_KEYS = 1
 SEED_QUERIES = 2
 SEED_OUTLIERS = 3
 SEED_TSCALE = 4
+SEED_VALUES = 5
 
 
 @dataclass(frozen=True)
@@ -129,6 +131,20 @@ def make_queries(w: Workload, device="cpu") -> torch.Tensor:
     g = _gen(SEED_QUERIES, device)
     x = torch.randn(w.groups * w.n_q, w.d, generator=g, dtype=torch.float32, device=device)
     return x.to(dt)
+
+
+def make_values(w: Workload, device="cpu", n_k: int | None = None, d_v: int | None = None,
+                dtype: str = "bf16") -> torch.Tensor:
+    """Cached value rows [batch*heads*n_k, d_v], standard normal, bf16 by
+    default (the value cache is not sketched; d_v defaults to the head dim)."""
+    n_k = w.n_k if n_k is None else n_k
+    d_v = w.d if d_v is None else d_v
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    g = _gen(SEED_VALUES, device)
+    out = torch.empty(w.groups, n_k, d_v, dtype=dt, device=device)
+    for i in range(w.groups):
+        out[i].copy_(torch.randn(n_k, d_v, generator=g, dtype=torch.float32, device=device).to(dt))
+    return out.reshape(-1, d_v)
 
 
 def make_random_bits(n_keys: int, m: int, seed: int, device="cpu") -> torch.Tensor:
