@@ -202,6 +202,13 @@ def project_bytes(w) -> float:
     return w.n_queries * (w.d * esz + w.m * 4)
 
 
+def attention_bytes(w, d_v: int = 128) -> float:
+    """Keys' bits and norms, bf16 value rows, projected queries in, outputs out
+    (the per-wave partials in the workspace, a few MB, are not counted)."""
+    return (w.groups * w.n_k * (w.m / 8 + 4 + 2 * d_v)
+            + w.groups * w.n_q * (w.m * 4 + d_v * 4))
+
+
 def step_bytes(w) -> float:
     return quantize_bytes(w) + project_bytes(w) + score_bytes(w)
 
@@ -315,6 +322,47 @@ def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
     torch.cuda.synchronize()
     ts = sorted(a.seconds_to(b) for a, b in evs)
     del sets
+    torch.cuda.empty_cache()
+    pct = lambda p: ts[min(len(ts) - 1, int(p * len(ts)))]
+    return sum(ts) / len(ts), ts[len(ts) // 2], pct(0.1), pct(0.9)
+
+
+def time_attention_rotating(qj, torch, w, sk, n_sets: int, iters: int, d_v: int = 128):
+    """Fused decode attention alone over `n_sets` distinct (bits, norms, V, Sq)
+    sets (each larger than the 256 MB Infinity Cache); returns mean, median,
+    p10 and p90 seconds per call."""
+    import math
+    import workloads as wl
+    dev = "cuda:0"
+    sets = []
+    for s in range(n_sets):
+        bits = wl.make_random_bits(w.groups * w.n_k, w.m, seed=200 + s, device=dev)
+        norms = torch.rand(w.groups * w.n_k, device=dev) * 10 + 1
+        Sq = torch.randn(w.groups * w.n_q, w.m, device=dev) * 11
+        V = torch.randn(w.groups * w.n_k, d_v, device=dev).to(torch.bfloat16)
+        out = torch.empty(w.groups, w.n_q, d_v, device=dev)
+        sets.append((Sq, bits, norms, V, out))
+    ws = torch.empty(qj.decode_attention_workspace_size(sk, w.groups, w.n_q, w.n_k, d_v),
+                     dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(w.d)
+    st = torch.cuda.current_stream()
+
+    def call(i):
+        Sq, bits, norms, V, out = sets[i % n_sets]
+        qj.decode_attention(sk, Sq, bits, norms, V, w.groups, w.n_q, w.n_k, scale,
+                            workspace=ws, out=out, stream=st)
+
+    for i in range(2 * n_sets):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
+    for i in range(iters):
+        evs[i][0].record(st)
+        call(i)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    ts = sorted(a.seconds_to(b) for a, b in evs)
+    del sets, ws
     torch.cuda.empty_cache()
     pct = lambda p: ts[min(len(ts) - 1, int(p * len(ts)))]
     return sum(ts) / len(ts), ts[len(ts) // 2], pct(0.1), pct(0.9)
@@ -452,6 +500,20 @@ def main():
                                         "mean_s": s2_mean, "median_s": s2_med,
                                         "p10_s": s2_p10, "p90_s": s2_p90, "bytes": sb2,
                                         "rotation": "2 sets x 302 MB"}
+        # decode-step attention on the scores (fused: the scores never reach HBM)
+        for name, wa, sk_a, n_sets in (("attention_decode7b", w, sk, 2),
+                                       ("attention_long_context", wl2, sk2, 2)):
+            ab = attention_bytes(wa)
+            a_mean, a_med, a_p10, a_p90 = time_attention_rotating(qj, torch, wa, sk_a, n_sets,
+                                                                  iters=50)
+            result[name] = {"workload": wa.name, "values": "bf16, d_v 128",
+                            "GBps": ab / a_mean / 1e9,
+                            "frac_hbm": ab / a_mean / 1e9 / HBM_PEAK_GBPS,
+                            "keys_per_s": wa.groups * wa.n_k / a_mean,
+                            "mean_s": a_mean, "median_s": a_med, "p10_s": a_p10,
+                            "p90_s": a_p90, "bytes": ab,
+                            "timing": "HIP events around each call (partials + combine), "
+                                      f"{n_sets} input sets rotated"}
         sk2.close()
         # the other quantize configurations (same 2,097,152-key cache size)
         for name, wq in (("quantize_prefill", wl.PREFILL), ("quantize_fqjl", wl.FQJL_7B),

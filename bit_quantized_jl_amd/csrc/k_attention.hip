@@ -8,11 +8,12 @@
 // never reach HBM: each wave scores a 16-key tile on the matrix cores (the
 // exact fp8-limb method of the score kernel, shared through score_common.h),
 // folds it into an online softmax (running maximum and sum, in the exp2
-// domain) and adds the weighted value rows.  Each wave writes one partial
-// (maximum, sum, d_v-float weighted sum) per query to the caller's workspace;
-// attn_combine_kernel merges the partials of a query.
+// domain) and adds the weighted value rows.  The four waves of a workgroup
+// merge their states through LDS into one partial (maximum, sum, d_v-float
+// weighted sum) per query in the caller's workspace; attn_combine_kernel
+// merges the partials of a query.
 //
-// The stream uses plain loads into registers, two 32-key stages deep: the
+// The stream uses plain loads into registers, a ring of three 16-key stages: the
 // bits and norms of a stage (as the score kernel loads them) and its value
 // rows, lane l holding bf16 dimensions [8 (l % 16), 8 (l % 16) + 8) of key
 // 4 j + l / 16 of each 16-key tile (one 16-byte load covers four rows).
@@ -32,7 +33,7 @@ namespace {
 
 using namespace sc;
 
-constexpr int AT_TILES = 2;   // 16-key tiles per stage
+constexpr int AT_TILES = 1;   // 16-key tiles per stage
 constexpr int AT_STAGE = 16 * AT_TILES;  // keys per stage
 constexpr int AT_DV = 128;    // value width of the fast path
 constexpr int AT_PART = AT_DV + 4;  // floats per partial: sum, M, L, padding to 16 bytes
@@ -134,7 +135,9 @@ struct SoftmaxState {
   float acc[QP][2][8];
 };
 
-template <int T, int QP>
+// PAIR: both members of the query pair exist (else only member A's weighted
+// sum is formed).
+template <int T, int QP, bool PAIR>
 __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOperands<T, QP> &qo,
                                            int k0, int kend, int lane, int nqp,
                                            float sl2, SoftmaxState<QP> &st) {
@@ -177,16 +180,17 @@ __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOpe
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         st.acc[qp][0][d] *= aA;
-        st.acc[qp][1][d] *= aB;
+        if (PAIR) st.acc[qp][1][d] *= aB;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 4 * j + gq;  // key of this lane's value row in the tile
-        const float pA = __shfl(p, t), pB = __shfl(p, 32 + t);
+        const float pA = __shfl(p, t);
+        const float pB = PAIR ? __shfl(p, 32 + t) : 0.f;
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           st.acc[qp][0][d] = fmaf(pA, vals[j][d], st.acc[qp][0][d]);
-          st.acc[qp][1][d] = fmaf(pB, vals[j][d], st.acc[qp][1][d]);
+          if (PAIR) st.acc[qp][1][d] = fmaf(pB, vals[j][d], st.acc[qp][1][d]);
         }
       }
     }
@@ -194,20 +198,49 @@ __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOpe
   }
 }
 
-// ws layout: [G * nq][P][AT_PART]: the weighted sum, then M and L (exp2 domain).
-template <int T, int QP>
+// Stages held in registers per wave: one is computed while the others load.
+template <int T>
+constexpr int attn_ring() {
+  return 3;
+}
+
+// The key stream of one wave: stages wave, wave + 4, ... of the workgroup's
+// keys through a ring of R register stages (stage i lives in b[i % R]).
+template <int T, int QP, bool PAIR, int R>
+__device__ __forceinline__ void stream_keys(AttnStage<T> (&b)[R], const KeyRange &kr,
+                                            const QueryOperands<T, QP> &qo, int wave, int lane,
+                                            int nsr, int nkb, int nqp, float sl2,
+                                            SoftmaxState<QP> &st) {
+  for (int j = 0; j < nsr; j += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int k0 = AT_STAGE * (wave + SM_WAVES * (j + r));
+      attn_stage<T, QP, PAIR>(b[r], qo, k0, nkb, lane, nqp, sl2, st);
+      load_attn_stage<T>(b[r], kr, k0 + R * AT_STAGE * SM_WAVES, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ws layout: [G * nq][P][AT_PART], one partial per workgroup along the keys
+// (P = gridDim.x): the weighted sum, then M and L (exp2 domain).  PAIR is
+// nq > 1 (with one query per group, member B's sums are never formed).
+template <int T, int QP, bool PAIR>
 __global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
-    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws, int P) {
+    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws) {
+  static_assert(QP == 1, "one query pair per pass");
   constexpr int W = 4 * T;
   constexpr int m = 32 * W;
   constexpr int NQ = 2 * QP;
   constexpr int JL = m / 64;
   __shared__ __attribute__((aligned(16))) unsigned char sAimg[QueryOperands<T, QP>::IMAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float sPart[SM_WAVES][NQ][AT_PART];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int P = gridDim.x;
   // key positions within a group fit an int, and byte offsets into a
   // group's rows a uint32 (the fused path takes nk < 2^22)
   const int kbeg = (int)blockIdx.x * chunk;
@@ -215,8 +248,8 @@ __global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
   const int nkb = kend > kbeg ? kend - kbeg : 0;  // keys of this workgroup
   const int nstage_blk = (nkb + AT_STAGE - 1) / AT_STAGE;
   const int ns = (nstage_blk - wave + SM_WAVES - 1) / SM_WAVES;
-  const int nsr = (ns + 1) & ~1;  // whole double-stage rounds
-  const int part = blockIdx.x * SM_WAVES + wave;
+  constexpr int R = attn_ring<T>();
+  const int nsr = (ns + R - 1) / R * R;  // whole rounds of the ring
 
   for (int64_t g = blockIdx.y; g < G; g += gridDim.y) {
     const KeyRange kr = key_range<T>(bits + g * nk * (int64_t)W, norms + g * nk,
@@ -225,67 +258,80 @@ __global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
       const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
       float sv[NQ][JL];
       load_query_values<m, NQ>(Sq + (g * nq + q0) * (int64_t)m, nqp, lane, sv);
-      if (q0 > 0) lds_barrier();  // every wave has read the previous pass's image
+      // (the previous pass's merge barrier orders its image reads before
+      // this image's writes)
       QueryOperands<T, QP> qo;
       build_query_operands<T, QP>(sv, nqp, wave, lane, sAimg, cscale, qo);
       __builtin_amdgcn_sched_barrier(0);
-      AttnStage<T> b0, b1;
-      load_attn_stage<T>(b0, kr, AT_STAGE * wave, lane);
-      load_attn_stage<T>(b1, kr, AT_STAGE * (wave + SM_WAVES), lane);
+      AttnStage<T> ring[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) load_attn_stage<T>(ring[r], kr, AT_STAGE * (wave + SM_WAVES * r), lane);
       SoftmaxState<QP> st;
 #pragma unroll
-      for (int qp = 0; qp < QP; ++qp)
+      for (int h = 0; h < 2; ++h) {
+        st.M[0][h] = -INFINITY;
+        st.L[0][h] = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          st.M[qp][h] = -INFINITY;
-          st.L[qp][h] = 0.f;
-#pragma unroll
-          for (int d = 0; d < 8; ++d) st.acc[qp][h][d] = 0.f;
-        }
-      for (int j = 0; j < nsr; j += 2) {
-        const int k0 = AT_STAGE * (wave + SM_WAVES * j);
-        attn_stage<T, QP>(b0, qo, k0, nkb, lane, nqp, sl2, st);
-        load_attn_stage<T>(b0, kr, k0 + 2 * AT_STAGE * SM_WAVES, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        attn_stage<T, QP>(b1, qo, k0 + AT_STAGE * SM_WAVES, nkb, lane, nqp, sl2, st);
-        load_attn_stage<T>(b1, kr, k0 + 3 * AT_STAGE * SM_WAVES, lane);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int d = 0; d < 8; ++d) st.acc[0][h][d] = 0.f;
       }
+      stream_keys<T, QP, PAIR, R>(ring, kr, qo, wave, lane, nsr, nkb, nqp, sl2, st);
       // ---- this wave's partials: sum the four lane groups (each saw every
-      // fourth value row), then lanes 0..15 hold dims 8 lane .. 8 lane + 7
+      // fourth value row); lanes 0..15 then hold dims 8 lane .. 8 lane + 7
 #pragma unroll
-      for (int qp = 0; qp < QP; ++qp) {
-        if (2 * qp >= nqp) break;
+      for (int h = 0; h < 2; ++h) {
+        if (h >= nqp) break;
+        float a[8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int qi = 2 * qp + h;
-          float a[8];
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            a[d] = st.acc[qp][h][d];
-            a[d] += __shfl_xor(a[d], 16);
-            a[d] += __shfl_xor(a[d], 32);
-          }
-          if (qi < nqp) {
-            float *dst = ws + ((g * nq + q0 + qi) * (int64_t)P + part) * AT_PART;
-            if (lane < 16) {
-              reinterpret_cast<float4 *>(dst)[2 * lane] = make_float4(a[0], a[1], a[2], a[3]);
-              reinterpret_cast<float4 *>(dst)[2 * lane + 1] = make_float4(a[4], a[5], a[6], a[7]);
-            }
-            if (lane == 0) {
-              dst[AT_DV] = st.M[qp][h];
-              dst[AT_DV + 1] = st.L[qp][h];
-            }
-          }
+        for (int d = 0; d < 8; ++d) {
+          a[d] = st.acc[0][h][d];
+          a[d] += __shfl_xor(a[d], 16);
+          a[d] += __shfl_xor(a[d], 32);
+        }
+        float *dst = sPart[wave][h];
+        if (lane < 16) {
+          reinterpret_cast<float4 *>(dst)[2 * lane] = make_float4(a[0], a[1], a[2], a[3]);
+          reinterpret_cast<float4 *>(dst)[2 * lane + 1] = make_float4(a[4], a[5], a[6], a[7]);
+        }
+        if (lane == 0) {
+          dst[AT_DV] = st.M[0][h];
+          dst[AT_DV + 1] = st.L[0][h];
         }
       }
+      __syncthreads();
+      // ---- the workgroup's partial of query h, merged by wave h
+      if (wave < nqp) {
+        const int h = wave;
+        float Mw[SM_WAVES], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < SM_WAVES; ++w) {
+          Mw[w] = sPart[w][h][AT_DV];
+          M = fmaxf(M, Mw[w]);
+        }
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < SM_WAVES; ++w) {
+          const float f = exp2_shift(Mw[w], M);
+          L = fmaf(f, sPart[w][h][AT_DV + 1], L);
+          o0 = fmaf(f, sPart[w][h][lane], o0);
+          o1 = fmaf(f, sPart[w][h][lane + 64], o1);
+        }
+        float *dst = ws + ((g * nq + q0 + h) * (int64_t)P + blockIdx.x) * AT_PART;
+        dst[lane] = o0;
+        dst[lane + 64] = o1;
+        if (lane == 0) {
+          dst[AT_DV] = M;
+          dst[AT_DV + 1] = L;
+        }
+      }
+      __syncthreads();  // sPart and the query image are free again
     }
   }
 }
 
 // Merge the P partials of each (group, query) row: M = max M_p,
-// out = sum_p 2^(M_p - M) acc_p / sum_p 2^(M_p - M) L_p.  One wave per row,
-// lane l owns dims l and l + 64.
+// out = sum_p 2^(M_p - M) acc_p / sum_p 2^(M_p - M) L_p.  One wave per row:
+// lane p reads the maximum and sum of partial p (64 partials per round),
+// lane l sums dims l and l + 64 over the partials.
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restrict__ ws,
                                                           int64_t rows, int P,
                                                           float *__restrict__ out) {
@@ -293,15 +339,40 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float *__restric
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const float *base = ws + row * (int64_t)P * AT_PART;
     float M = -INFINITY;
-    for (int p = 0; p < P; ++p) M = fmaxf(M, base[p * AT_PART + AT_DV]);
+    for (int p = lane; p < P; p += 64) M = fmaxf(M, base[p * AT_PART + AT_DV]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int p = 0; p < P; ++p) {
-      const float *e = base + p * AT_PART;
-      const float w = exp2_shift(e[AT_DV], M);
-      L = fmaf(w, e[AT_DV + 1], L);
-      o0 = fmaf(w, e[lane], o0);
-      o1 = fmaf(w, e[lane + 64], o1);
+    for (int p0 = 0; p0 < P; p0 += 64) {
+      const int p = p0 + lane;
+      const float f = p < P ? exp2_shift(base[p * AT_PART + AT_DV], M) : 0.f;
+      L += p < P ? f * base[p * AT_PART + AT_DV + 1] : 0.f;
+      const int n = P - p0 < 64 ? P - p0 : 64;
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {  // four partials' loads in flight
+        float a0[4], a1[4], fi[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float *e = base + (p0 + i + u) * AT_PART;
+          a0[u] = e[lane];
+          a1[u] = e[lane + 64];
+          fi[u] = __shfl(f, i + u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          o0 = fmaf(fi[u], a0[u], o0);
+          o1 = fmaf(fi[u], a1[u], o1);
+        }
+      }
+      for (; i < n; ++i) {
+        const float fi = __shfl(f, i);
+        const float *e = base + (p0 + i) * AT_PART;
+        o0 = fmaf(fi, e[lane], o0);
+        o1 = fmaf(fi, e[lane + 64], o1);
+      }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
     const float inv = 1.f / L;
     out[row * AT_DV + lane] = o0 * inv;
     out[row * AT_DV + lane + 64] = o1 * inv;
@@ -361,15 +432,15 @@ void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_partial_kernel<T, QP>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_partial_kernel<T, QP, true>,
                                                      SM_THREADS, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     resident = cus * per_cu;
   }
   int64_t chunk = (G * nk + resident - 1) / resident;
-  chunk = (chunk + 2 * AT_STAGE * SM_WAVES - 1) / (2 * AT_STAGE * SM_WAVES) *
-          (2 * AT_STAGE * SM_WAVES);
+  constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
+  chunk = (chunk + round - 1) / round * round;
   *chunk_out = chunk;
   *gx_out = (int)((nk + chunk - 1) / chunk);
 }
@@ -381,10 +452,14 @@ hipError_t launch_attn_t(const float *Sq, const uint32_t *bits, const float *nor
   int64_t chunk = 0;
   int gx = 0;
   attn_grid<T, QP>(G, nk, &chunk, &gx);
-  const int P = gx * SM_WAVES;
+  const int P = gx;
   dim3 grid((unsigned)gx, (unsigned)(G < 65535 ? G : 65535));
-  hipLaunchKernelGGL((attn_partial_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms,
-                     V, G, nq, nk, (int)chunk, c, sl2, ws, P);
+  if (nq > 1)
+    hipLaunchKernelGGL((attn_partial_kernel<T, QP, true>), grid, dim3(SM_THREADS), 0, st, Sq,
+                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
+  else
+    hipLaunchKernelGGL((attn_partial_kernel<T, QP, false>), grid, dim3(SM_THREADS), 0, st, Sq,
+                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
   const int64_t rows = G * nq;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)), dim3(64),
                      0, st, ws, rows, P, out);
@@ -396,7 +471,7 @@ int attn_partials_t(int64_t G, int64_t nk) {
   int64_t chunk = 0;
   int gx = 0;
   attn_grid<T, 1>(G, nk, &chunk, &gx);
-  return gx * SM_WAVES;
+  return gx;
 }
 
 }  // namespace
