@@ -517,7 +517,8 @@ def main():
         sk2.close()
         # the other quantize configurations (same 2,097,152-key cache size)
         for name, wq in (("quantize_prefill", wl.PREFILL), ("quantize_fqjl", wl.FQJL_7B),
-                         ("quantize_fqjl_dither", wl.FQJL_7B_DITHER)):
+                         ("quantize_fqjl_dither", wl.FQJL_7B_DITHER),
+                         ("quantize_dfqjl", wl.DFQJL_7B), ("quantize_pfqjl", wl.PFQJL_7B)):
             tq, bq = time_quantize(qj, torch, wq)
             result[name] = {"workload": wq.name, "sketch": wq.variant, "rho": wq.rho,
                             "mean_s": tq, "keys_per_s": wq.n_keys / tq, "GBps": bq / tq / 1e9,

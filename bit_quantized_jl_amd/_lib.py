@@ -26,7 +26,7 @@ ERR_UNSUPPORTED = 2
 ERR_OUT_OF_MEMORY = 3
 ERR_DEVICE = 4
 
-VARIANTS = {"dense": 0, "fqjl": 1}
+VARIANTS = {"dense": 0, "fqjl": 1, "dfqjl": 2, "pfqjl": 3}
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 

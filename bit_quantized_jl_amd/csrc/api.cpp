@@ -46,7 +46,7 @@ const char *qjl_version(void) { return "qjl 0.1.0 gfx950"; }
 qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t variant,
                                     float *S_f32, uint16_t *S_bf16, int8_t *D_signs,
                                     int32_t *perm, float *G) {
-  qjl_status st = validate_sketch_params(d, m, variant, 0.f);
+  qjl_status st = validate_sketch_params(d, m, variant, 0.f, /*check_rho=*/false);
   if (st != QJL_OK) return st;
   HostSketch hs;
   hs.seed = seed;
@@ -232,7 +232,7 @@ qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype,
   qjl_status st = check_device(sk);
   if (st != QJL_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sk->host.variant == QJL_VARIANT_FQJL)
+  if (sk->host.variant != QJL_VARIANT_DENSE)
     return from_hip(launch_fqjl(sk, K, dtype, n_keys, key_index_base, norms_out, bits_out,
                                 nullptr, s));
   if (quantize_mfma_supported(sk, K, dtype, bits_out))
@@ -252,7 +252,7 @@ qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
   qjl_status st = check_device(sk);
   if (st != QJL_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sk->host.variant == QJL_VARIANT_FQJL)
+  if (sk->host.variant != QJL_VARIANT_DENSE)
     return from_hip(launch_fqjl(sk, q, dtype, n_queries, 0, nullptr, nullptr, Sq_out, s));
   return from_hip(launch_project_dense(sk, q, dtype, n_queries, Sq_out, s));
 }

@@ -69,7 +69,9 @@ __device__ __forceinline__ uint32_t pack_nonneg(const float *u) {
   return ~word;
 }
 
-template <int D, typename T, bool PROJECT, bool DITHER, bool VEC>
+// PERM = false: the block has no permutation (D-FQJL), so the transformed
+// row is scaled by G in place and the LDS round trip is skipped.
+template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
 __global__ __launch_bounds__(64) void fqjl_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
@@ -112,12 +114,17 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
         u[c] = __uint_as_float(__float_as_uint(v) ^ ds[c]);
       }
       fwht_reg<D>(u);
-#pragma unroll
-      for (int c = 0; c < D; ++c) lds[c * 64 + lane] = u[c];
       const int32_t *pb = P + b * D;
       const float *gb = Gs + b * D;
+      if constexpr (PERM) {
 #pragma unroll
-      for (int c = 0; c < D; ++c) u[c] = lds[pb[c] * 64 + lane] * gb[c];
+        for (int c = 0; c < D; ++c) lds[c * 64 + lane] = u[c];
+#pragma unroll
+        for (int c = 0; c < D; ++c) u[c] = lds[pb[c] * 64 + lane] * gb[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < D; ++c) u[c] *= gb[c];
+      }
       fwht_reg<D>(u);
       if (PROJECT) {
         if (valid) {
@@ -156,7 +163,10 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
 // then 16 KB per wave (element c of row k at ((c ^ (c >> 6)) << 5) + k: the
 // two halves' writes land in disjoint banks, and every gather reads one index
 // for all lanes, so it is conflict free), which doubles the waves a CU holds.
-template <typename T, bool PROJECT, bool DITHER>
+// Without a permutation (PERM = false, D-FQJL) each lane needs coordinate c
+// of both halves, which v_permlane32_swap exchanges between lanes k and
+// k + 32 in registers: no LDS at all.
+template <typename T, bool PROJECT, bool DITHER, bool PERM>
 __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
@@ -219,22 +229,35 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
         t[c] = fmaf(sgn, hi, lo);
       }
       fwht_reg<H>(t);
-      {
-        // idx(c + 64 sh, k) = 32 (c ^ sh) + 2048 sh + k for c < 64: one lane base
-        // for even and one for odd c, plus an immediate offset 32 c.
-        float *we = lds + k + 2048 * sh + 32 * sh;
-        float *wo = lds + k + 2048 * sh - 32 * sh;
+      if constexpr (PERM) {
+        {
+          // idx(c + 64 sh, k) = 32 (c ^ sh) + 2048 sh + k for c < 64: one lane base
+          // for even and one for odd c, plus an immediate offset 32 c.
+          float *we = lds + k + 2048 * sh + 32 * sh;
+          float *wo = lds + k + 2048 * sh - 32 * sh;
 #pragma unroll
-        for (int c = 0; c < H; ++c) ((c & 1) ? wo : we)[32 * c] = t[c];
-      }
-      // Gather in groups of 16: the barriers keep the compiler from hoisting
-      // all 128 reads (and their addresses) into registers at once.
+          for (int c = 0; c < H; ++c) ((c & 1) ? wo : we)[32 * c] = t[c];
+        }
+        // Gather in groups of 16: the barriers keep the compiler from hoisting
+        // all 128 reads (and their addresses) into registers at once.
 #pragma unroll
-      for (int c = 0; c < H; ++c) {
-        if (c % 16 == 0) asm volatile("" ::: "memory");
-        const float lo = lds[idx(pb[c], k)] * gb[c];
-        const float hi = lds[idx(pb[c + H], k)] * gb[c + H];
-        t[c] = fmaf(sgn, hi, lo);
+        for (int c = 0; c < H; ++c) {
+          if (c % 16 == 0) asm volatile("" ::: "memory");
+          const float lo = lds[idx(pb[c], k)] * gb[c];
+          const float hi = lds[idx(pb[c + H], k)] * gb[c + H];
+          t[c] = fmaf(sgn, hi, lo);
+        }
+      } else {
+        // t[c] is coordinate c + 64 sh of the transformed row; after the swap
+        // every lane holds coordinate c of half 0 (first) and half 1 (second)
+#pragma unroll
+        for (int c = 0; c < H; ++c) {
+          const uint32_t v = __float_as_uint(t[c]);
+          const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+          const float lo = __uint_as_float(sw[0]) * gb[c];
+          const float hi = __uint_as_float(sw[1]) * gb[c + H];
+          t[c] = fmaf(sgn, hi, lo);
+        }
       }
       fwht_reg<H>(t);
       const int j0 = b * D + H * sh;  // sketch coordinate of t[0]
@@ -332,6 +355,9 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
   const int grid = (int)(tiles < 16384 ? tiles : 16384);
   const bool proj = Y != nullptr;
   const bool dith = !proj && h.rho > 0.f;
+  // D-FQJL blocks have no permutation (P_b = I): the kernels skip the gather.
+  // Any other case (P-FQJL, the composition) gathers through LDS.
+  const bool perm = h.variant != QJL_VARIANT_DFQJL;
 #define QJL_FQJL_LAUNCH(KERNEL, ...)                                                            \
   hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign,  \
                      sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
@@ -342,23 +368,30 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
 #define QJL_FQJL128_LAUNCH(...)                                                                  \
   hipLaunchKernelGGL((fqjl128_kernel<__VA_ARGS__>), dim3(grid2), dim3(64), 0, st, X, nb, h.m,    \
                      sk->Dsign, sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
-      if (proj) QJL_FQJL128_LAUNCH(T, true, false);
-      else if (dith) QJL_FQJL128_LAUNCH(T, false, true);
-      else QJL_FQJL128_LAUNCH(T, false, false);
+      if (!perm && proj) QJL_FQJL128_LAUNCH(T, true, false, false);
+      else if (!perm && dith) QJL_FQJL128_LAUNCH(T, false, true, false);
+      else if (proj) QJL_FQJL128_LAUNCH(T, true, false, true);
+      else if (dith) QJL_FQJL128_LAUNCH(T, false, true, true);
+      else QJL_FQJL128_LAUNCH(T, false, false, true);
 #undef QJL_FQJL128_LAUNCH
       return hipGetLastError();
     }
   }
   if constexpr (D >= 32) {
     const bool vec = ((uintptr_t)X & 15) == 0;  // rows are whole 16-byte vectors then
+    // (a D-FQJL sketch always dithers its keys: rho > 0)
     if (vec) {
-      if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true);
-      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true);
-      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, true);
+      if (!perm && proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true, false);
+      else if (!perm && dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true, false);
+      else if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true, true);
+      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true, true);
+      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, true, true);
     } else {
-      if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false);
-      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false);
-      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, false);
+      if (!perm && proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false, false);
+      else if (!perm && dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false, false);
+      else if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false, true);
+      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false, true);
+      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, false, true);
     }
   } else {
     if (proj) QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, true, false);

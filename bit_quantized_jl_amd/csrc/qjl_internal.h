@@ -43,7 +43,8 @@ struct HostSketch {
   std::vector<float> G;        // FQJL: nb*d, float32 Gaussians
 };
 
-qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho);
+qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho,
+                                  bool check_rho = true);
 void generate_host_sketch(HostSketch &hs);
 uint16_t f32_to_bf16_rne(float x);
 // Explicit m x d FQJL matrix (double), for export.

@@ -41,11 +41,17 @@ uint16_t f32_to_bf16_rne(float x) {
 
 static bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
-qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho) {
-  if (variant != QJL_VARIANT_DENSE && variant != QJL_VARIANT_FQJL) return QJL_ERR_INVALID_ARGUMENT;
+qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho,
+                                  bool check_rho) {
+  if (variant < QJL_VARIANT_DENSE || variant > QJL_VARIANT_PFQJL) return QJL_ERR_INVALID_ARGUMENT;
   if (m < 32 || m % 32 != 0) return QJL_ERR_INVALID_ARGUMENT;
   if (d < 1) return QJL_ERR_INVALID_ARGUMENT;
-  if (!(rho >= 0.f) || !std::isfinite(rho)) return QJL_ERR_INVALID_ARGUMENT;
+  if (check_rho) {
+    if (!(rho >= 0.f) || !std::isfinite(rho)) return QJL_ERR_INVALID_ARGUMENT;
+    // D-FQJL is the dithered construction, P-FQJL the undithered one
+    if (variant == QJL_VARIANT_DFQJL && !(rho > 0.f)) return QJL_ERR_INVALID_ARGUMENT;
+    if (variant == QJL_VARIANT_PFQJL && rho != 0.f) return QJL_ERR_INVALID_ARGUMENT;
+  }
   if (m > QJL_MAX_M) return QJL_ERR_UNSUPPORTED;
   if (variant == QJL_VARIANT_DENSE) {
     if (d > QJL_MAX_D) return QJL_ERR_UNSUPPORTED;
@@ -84,6 +90,7 @@ void generate_host_sketch(HostSketch &hs) {
       P[c] = c;
       G[c] = (float)gaussian(kg, (uint64_t)b * d + c);
     }
+    if (hs.variant == QJL_VARIANT_DFQJL) continue;  // no permutation: P_b = I
     for (int i = d - 1; i >= 1; --i) {
       const double u = uniform53(stream_draw(kp, (uint64_t)b * d + i));
       const int t = (int)std::floor(u * (double)(i + 1));

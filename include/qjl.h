@@ -30,6 +30,14 @@
  *                      Dither (rho > 0) is the D-FQJL smoothing of the sign
  *                      quantizer on the same page, added after the transform
  *                      and before the sign.
+ *   QJL_VARIANT_DFQJL  the page's first construction alone (D-FQJL): the
+ *                      same blocks without the permutation, H diag(G_b)
+ *                      (H/sqrt d) diag(D_b), with Gaussian dither rho > 0.
+ *   QJL_VARIANT_PFQJL  the page's second construction alone (P-FQJL): the
+ *                      FQJL blocks with rho = 0 (bit-identical to
+ *                      QJL_VARIANT_FQJL at rho = 0 for the same seed).
+ *   All three FQJL variants draw D_b and G_b from the same streams, so for
+ *   one seed they differ only in the permutation and the dither.
  *
  * Every random quantity comes from SplitMix64 counter streams keyed by the
  * seed (stream 0: dense S, 1: D, 2: P, 3: G, 4: dither), so a sketch and its
@@ -82,7 +90,12 @@ typedef enum {
   QJL_ERR_DEVICE = 4            /* no usable GPU, or a HIP call / kernel launch failed */
 } qjl_status;
 
-typedef enum { QJL_VARIANT_DENSE = 0, QJL_VARIANT_FQJL = 1 } qjl_variant;
+typedef enum {
+  QJL_VARIANT_DENSE = 0,
+  QJL_VARIANT_FQJL = 1,  /* permutation, optional dither */
+  QJL_VARIANT_DFQJL = 2, /* no permutation (Pi_b = I), dither rho > 0 required */
+  QJL_VARIANT_PFQJL = 3  /* permutation, no dither (rho == 0 required) */
+} qjl_variant;
 typedef enum { QJL_DTYPE_F32 = 0, QJL_DTYPE_BF16 = 1 } qjl_dtype;
 
 typedef struct qjl_sketch qjl_sketch; /* opaque, library-owned */
@@ -97,8 +110,8 @@ typedef struct qjl_sketch qjl_sketch; /* opaque, library-owned */
  * composition) from `seed` on the host, upload it to the current HIP device
  * and return it in *out.  rho >= 0 is the dither level (0: none).
  * Errors: out == NULL, m % 32 != 0, m or d out of range, bad variant,
- * rho < 0 or not finite -> INVALID_ARGUMENT / UNSUPPORTED (per the limits
- * above); no GPU -> DEVICE; allocation failure -> OUT_OF_MEMORY.  On error
+ * rho < 0 or not finite, rho == 0 for DFQJL or rho != 0 for PFQJL ->
+ * INVALID_ARGUMENT / UNSUPPORTED (per the limits above); no GPU -> DEVICE; allocation failure -> OUT_OF_MEMORY.  On error
  * *out is set to NULL (when out is not NULL).
  */
 qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant, float rho,
@@ -124,8 +137,9 @@ qjl_status qjl_sketch_export(const qjl_sketch *sk, float *S_f32, uint16_t *S_bf1
 /*
  * Host-only: generate the random parameters of a sketch without a GPU, into
  * caller-owned host buffers (any may be NULL).  Dense: S_f32[m*d],
- * S_bf16[m*d].  FQJL: D_signs[(m/d)*d] (+1/-1), perm[(m/d)*d], G[(m/d)*d].
- * Same validation as qjl_make_sketch.
+ * S_bf16[m*d].  FQJL variants: D_signs[(m/d)*d] (+1/-1), perm[(m/d)*d]
+ * (the identity for DFQJL), G[(m/d)*d].  Same validation as
+ * qjl_make_sketch, except that there is no rho to check.
  */
 qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t variant,
                                     float *S_f32, uint16_t *S_bf16, int8_t *D_signs,

@@ -21,6 +21,13 @@ independent blocks are stacked; block b yields coordinates [b d, (b+1) d).
 The pages leave the Hadamard normalisation open; with 1/sqrt(d) on the
 first transform only, every coordinate of B_b k has variance ||k||^2 over
 G, exactly as a dense Gaussian row, so one estimator constant serves both.
+
+The same page names the two constructions the composition combines
+("Key concepts"): D-FQJL smooths the sign quantizer with Gaussian dither
+and has no permutation (Pi_b = I here), P-FQJL inserts the random
+permutation and has no dither.  "fqjl" is the composition with both
+(permutation, optional dither); "dfqjl" and "pfqjl" are the two
+constructions alone.
 """
 from __future__ import annotations
 
@@ -157,10 +164,12 @@ def fisher_yates(seed: int, block: int, d: int) -> np.ndarray:
     return P
 
 
-def make_fqjl(seed: int, d: int, m: int, rho: float = 0.0) -> FqjlSketch:
+def make_fqjl(seed: int, d: int, m: int, rho: float = 0.0, permute: bool = True,
+              variant: str = "fqjl") -> FqjlSketch:
     """Per block b < m/d: D_b from the top bit of r(seed, 1, b d + c)
-    (0 -> +1, 1 -> -1); P_b by Fisher-Yates on stream 2; G_b[c] =
-    fp32(N(b d + c)) on stream 3."""
+    (0 -> +1, 1 -> -1); P_b by Fisher-Yates on stream 2 (the identity when
+    ``permute`` is false: the D-FQJL construction has no permutation);
+    G_b[c] = fp32(N(b d + c)) on stream 3."""
     assert m % d == 0
     nb = m // d
     D = np.empty((nb, d))
@@ -169,16 +178,27 @@ def make_fqjl(seed: int, d: int, m: int, rho: float = 0.0) -> FqjlSketch:
     for b in range(nb):
         r = rng.draw(seed, rng.STREAM_D, np.arange(b * d, b * d + d, dtype=np.uint64))
         D[b] = np.where((r >> np.uint64(63)) == 0, 1.0, -1.0)
-        P[b] = fisher_yates(seed, b, d)
+        P[b] = fisher_yates(seed, b, d) if permute else np.arange(d)
         G[b] = round_to_f32(rng.gaussian_exact(seed, rng.STREAM_G, d, offset=b * d))
-    return FqjlSketch(seed, d, m, rho, D, P, G)
+    return FqjlSketch(seed, d, m, rho, D, P, G, variant)
 
 
 def make_sketch(seed: int, d: int, m: int, variant: str, rho: float = 0.0, exact: bool = True):
+    """variant: "dense"; "fqjl" (permutation, optional dither); "dfqjl" (the
+    FQJL page's D-FQJL: no permutation, dither rho > 0); "pfqjl" (its P-FQJL:
+    permutation, rho = 0)."""
     if variant == "dense":
         return make_dense(seed, d, m, rho, exact)
     if variant == "fqjl":
         return make_fqjl(seed, d, m, rho)
+    if variant == "dfqjl":
+        if not rho > 0:
+            raise ValueError("D-FQJL is the dithered construction: rho > 0")
+        return make_fqjl(seed, d, m, rho, permute=False, variant="dfqjl")
+    if variant == "pfqjl":
+        if rho != 0:
+            raise ValueError("P-FQJL is the undithered construction: rho = 0")
+        return make_fqjl(seed, d, m, 0.0, variant="pfqjl")
     raise ValueError(variant)
 
 

@@ -58,6 +58,10 @@ def test_status_strings_and_version():
     ((0, 128, 320, 1, 0.0), 2),      # FQJL m % d != 0
     ((0, 4, 32, 1, 0.0), 2),         # FQJL d < 8
     ((0, 256, 512, 1, 0.0), 2),      # FQJL d > 128
+    ((0, 128, 256, 4, 0.0), 1),      # no variant 4
+    ((0, 128, 256, 2, 0.0), 1),      # D-FQJL needs dither
+    ((0, 128, 256, 3, 0.1), 1),      # P-FQJL has none
+    ((0, 96, 192, 2, 0.1), 2),       # D-FQJL d not a power of two
 ])
 def test_make_sketch_validation(args, expect):
     lib = qj.load()
@@ -99,10 +103,11 @@ def test_host_dense_sketch_equals_oracle(seed, d, m):
     assert np.array_equal(got["S_bf16"], osk.bf16_bits(ref.S16))
 
 
+@pytest.mark.parametrize("variant", ["fqjl", "dfqjl", "pfqjl"])
 @pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (5, 8, 32), (9, 64, 192), (2, 128, 512)])
-def test_host_fqjl_params_equal_oracle(seed, d, m):
-    got = qj.generate_sketch_host(seed, d, m, "fqjl")
-    ref = osk.make_fqjl(seed, d, m)
+def test_host_fqjl_params_equal_oracle(seed, d, m, variant):
+    got = qj.generate_sketch_host(seed, d, m, variant)
+    ref = osk.make_sketch(seed, d, m, variant, 0.1 if variant == "dfqjl" else 0.0)
     assert np.array_equal(got["D"].astype(np.float64), ref.D)
     assert np.array_equal(got["P"].astype(np.int64), ref.P)
     assert np.array_equal(got["G"].astype(np.float64), ref.G)

@@ -59,6 +59,8 @@ QUANT_CASES = [
     wl.PREFILL.scaled(batch=1, heads=3, n_k=777),
     wl.FQJL_7B.scaled(batch=1, heads=2, n_k=1000),
     wl.FQJL_7B_DITHER.scaled(batch=1, heads=2, n_k=1000),
+    wl.DFQJL_7B.scaled(batch=1, heads=2, n_k=1000),
+    wl.PFQJL_7B.scaled(batch=1, heads=2, n_k=1000),
 ]
 
 
@@ -75,6 +77,10 @@ SHAPES = (
     + [("fqjl", d, m, dt, rho) for (d, m) in ((8, 32), (16, 32), (16, 64), (32, 32), (32, 96),
                                               (64, 64), (64, 256), (128, 128), (128, 512))
        for dt in ("f32", "bf16") for rho in (0.0, 0.3)]
+    + [("dfqjl", d, m, dt, 0.1) for (d, m) in ((8, 32), (16, 64), (32, 96), (64, 256), (128, 128),
+                                                (128, 512)) for dt in ("f32", "bf16")]
+    + [("pfqjl", d, m, dt, 0.0) for (d, m) in ((16, 32), (64, 192), (128, 256))
+       for dt in ("f32", "bf16")]
 )
 
 
@@ -88,15 +94,18 @@ def test_quantize_shapes(variant, d, m, dt, rho):
 @pytest.mark.parametrize("variant,d,m,dt", [("dense", 128, 256, "f32"), ("dense", 128, 256, "bf16"),
                                             ("dense", 100, 96, "bf16"), ("dense", 16, 512, "f32"),
                                             ("fqjl", 128, 256, "bf16"), ("fqjl", 8, 32, "f32"),
-                                            ("fqjl", 64, 192, "f32"), ("fqjl", 128, 512, "bf16")])
+                                            ("fqjl", 64, 192, "f32"), ("fqjl", 128, 512, "bf16"),
+                                            ("dfqjl", 128, 256, "bf16"), ("dfqjl", 16, 64, "f32"),
+                                            ("pfqjl", 128, 256, "bf16")])
 def test_project_query(variant, d, m, dt):
     note("project", variant, d, m, dt)
+    rho = 0.1 if variant == "dfqjl" else 0.0  # queries are never dithered
     w = wl.Workload("proj", d, m, variant, 1, 1, 1, 37, dt, seed=5)
     q = wl.make_queries(w, "cpu").to(DEV)
-    sk = qj.make_sketch(5, d, m, variant)
+    sk = qj.make_sketch(5, d, m, variant, rho)
     Sq = qj.project_query(sk, q)
     torch.cuda.synchronize()
-    ref = oracle_sketch(5, d, m, variant, 0.0)
+    ref = oracle_sketch(5, d, m, variant, rho)
     qd = to_np_f64(q)
     check_projection(to_np_f64(Sq), oq.project(ref, qd, dt), qd, m)
     sk.close()
@@ -133,7 +142,9 @@ def test_score_dither_constant():
 
 
 @pytest.mark.parametrize("w", [wl.TINY, wl.DECODE_7B.scaled(batch=1, heads=2, n_k=999),
-                               wl.FQJL_7B_DITHER.scaled(batch=1, heads=2, n_k=500)],
+                               wl.FQJL_7B_DITHER.scaled(batch=1, heads=2, n_k=500),
+                               wl.DFQJL_7B.scaled(batch=1, heads=2, n_k=500),
+                               wl.PFQJL_7B.scaled(batch=1, heads=2, n_k=500)],
                          ids=lambda w: w.name)
 def test_end_to_end_scores(w):
     note("e2e", w.name)
@@ -293,7 +304,7 @@ def test_full_size_prefill():
     sk.close()
 
 
-@pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER, wl.DFQJL_7B], ids=lambda w: w.name)
 def test_full_size_fqjl(w):
     sk, K, norms, bits = full_size_quantize(w, sample=2000)
     full_size_score(w, sk, K, norms, bits, groups_checked=2)

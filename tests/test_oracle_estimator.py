@@ -76,7 +76,8 @@ def _brute_estimate(S, q, k, rho=0.0, xi=None):
     return SQ * math.sqrt(1 + rho * rho) / m * nk * tot
 
 
-@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("dense", 0.5), ("fqjl", 0.0), ("fqjl", 0.3)])
+@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("dense", 0.5), ("fqjl", 0.0), ("fqjl", 0.3),
+                                         ("dfqjl", 0.3), ("pfqjl", 0.0)])
 def test_brute_force_tiny(variant, rho):
     d, m = 4, 32
     sk = sketch.make_sketch(3, d, m, variant, rho)
@@ -116,7 +117,8 @@ def _mc(variant, d, m, rho, seeds, q, k):
     return est
 
 
-@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("fqjl", 0.0), ("fqjl", 0.1), ("dense", 1.0)])
+@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("fqjl", 0.0), ("fqjl", 0.1), ("dense", 1.0),
+                                         ("dfqjl", 0.1), ("dfqjl", 1.0), ("pfqjl", 0.0)])
 def test_unbiased_over_seeds(variant, rho):
     d, m, N = 16, 64, 3000
     rs = np.random.default_rng(12)
@@ -150,8 +152,9 @@ def test_dense_variance_closed_form():
         assert abs(est.var(ddof=1) / var - 1) < 0.10
 
 
-@pytest.mark.parametrize("variant", ["dense", "fqjl"])
-def test_error_shrinks_like_inverse_sqrt_m(variant):
+@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("fqjl", 0.0), ("dfqjl", 0.1),
+                                         ("pfqjl", 0.0)])
+def test_error_shrinks_like_inverse_sqrt_m(variant, rho):
     d, N = 16, 300
     rs = np.random.default_rng(7)
     k = rs.standard_normal(d)
@@ -159,7 +162,7 @@ def test_error_shrinks_like_inverse_sqrt_m(variant):
     ms = [32, 64, 128, 256, 512, 1024]
     rms = []
     for m in ms:
-        est = _mc(variant, d, m, 0.0, range(1000, 1000 + N), q, k)
+        est = _mc(variant, d, m, rho, range(1000, 1000 + N), q, k)
         rms.append(math.sqrt(np.mean((est - q @ k) ** 2)))
     assert all(a > b for a, b in zip(rms, rms[1:]))
     slope = np.polyfit(np.log(ms), np.log(rms), 1)[0]
@@ -265,3 +268,51 @@ def test_unit_vector_special_case():
 def test_estimator_constant():
     assert qjl.estimator_constant(256, 0.0) == math.sqrt(math.pi / 2) / 256
     assert abs(qjl.estimator_constant(128, 0.1) - math.sqrt(math.pi / 2) * math.sqrt(1.01) / 128) < 1e-18
+
+
+# ---------------------------------------------------------------- D-FQJL / P-FQJL
+def test_dfqjl_block_is_the_unpermuted_composition():
+    # D-FQJL (the FQJL page's first construction) has no permutation: its
+    # block is H diag(G) (H / sqrt d) diag(D), built here from scipy's
+    # Hadamard matrix, while P-FQJL and the composition keep the permutation
+    from scipy.linalg import hadamard
+    d, m = 16, 64
+    dk = sketch.make_sketch(5, d, m, "dfqjl", 0.2)
+    pk = sketch.make_sketch(5, d, m, "pfqjl", 0.0)
+    fk = sketch.make_sketch(5, d, m, "fqjl", 0.0)
+    H = hadamard(d).astype(np.float64)
+    for b in range(m // d):
+        ref = H @ np.diag(dk.G[b]) @ (H / math.sqrt(d)) @ np.diag(dk.D[b])
+        assert np.allclose(dk.explicit()[b * d:(b + 1) * d], ref, rtol=0, atol=1e-12)
+        assert np.array_equal(dk.P[b], np.arange(d))
+    # same D and G streams for one seed; the permutation is the only difference
+    assert np.array_equal(dk.D, fk.D) and np.array_equal(dk.G, fk.G)
+    assert np.array_equal(pk.P, fk.P) and not np.array_equal(pk.P, dk.P)
+    assert np.array_equal(pk.explicit(), fk.explicit())
+    X = np.random.default_rng(0).standard_normal((5, d))
+    assert np.allclose(sketch.fqjl_apply(dk, X), X @ dk.explicit().T, rtol=0, atol=1e-10)
+
+
+def test_variant_rho_rules():
+    with pytest.raises(ValueError):
+        sketch.make_sketch(0, 16, 32, "dfqjl", 0.0)
+    with pytest.raises(ValueError):
+        sketch.make_sketch(0, 16, 32, "pfqjl", 0.1)
+
+
+def test_dfqjl_unbiased_conditional_on_D():
+    # with P = I the Gaussian second diagonal still makes every coordinate
+    # pair jointly Gaussian given D, so the dithered estimator with
+    # sqrt(1 + rho^2) is unbiased over G and the dither alone
+    d, m, N, rho = 16, 32, 6000, 0.5
+    base = sketch.make_sketch(0, d, m, "dfqjl", rho)
+    rs = np.random.default_rng(13)
+    k = rs.standard_normal(d)
+    q = 0.5 * k + rs.standard_normal(d)
+    est = np.empty(N)
+    for t in range(N):
+        G = rng.gaussian_fast(300 + t, rng.STREAM_G, np.arange(m)).reshape(m // d, d)
+        sk = sketch.FqjlSketch(0, d, m, rho, base.D, base.P, sketch.round_to_f32(G), "dfqjl")
+        est[t] = qjl.estimate_inner_product(sk, q, k, key_index=t)
+    se = est.std(ddof=1) / math.sqrt(N)
+    assert abs(est.mean() - q @ k) <= 3 * se

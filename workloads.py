@@ -33,7 +33,7 @@ class Workload:
     name: str
     d: int
     m: int
-    variant: str            # "dense" | "fqjl"
+    variant: str            # "dense" | "fqjl" | "dfqjl" | "pfqjl"
     batch: int
     heads: int
     n_k: int                # keys per (batch, head)
@@ -78,7 +78,12 @@ FQJL_7B = Workload("fqjl_llama7b_decode_b8_h32_ctx8192_m256", 128, 256, "fqjl",
 FQJL_7B_DITHER = FQJL_7B.scaled(name="fqjl_dither0.1_llama7b_decode_b8_h32_ctx8192_m256",
                                 rho=0.1)
 
-ALL = [TINY, DECODE_7B, LONG_CTX, PREFILL, FQJL_7B, FQJL_7B_DITHER]
+# the FQJL page's two constructions alone, on the same cache
+DFQJL_7B = FQJL_7B.scaled(name="dfqjl_dither0.1_llama7b_decode_b8_h32_ctx8192_m256",
+                          variant="dfqjl", rho=0.1)
+PFQJL_7B = FQJL_7B.scaled(name="pfqjl_llama7b_decode_b8_h32_ctx8192_m256", variant="pfqjl")
+
+ALL = [TINY, DECODE_7B, LONG_CTX, PREFILL, FQJL_7B, FQJL_7B_DITHER, DFQJL_7B, PFQJL_7B]
 
 
 def _gen(seed: int, device) -> torch.Generator:
