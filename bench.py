@@ -48,6 +48,9 @@ def parse():
                    help="only the timed step (used under profilers)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--attention-only", action="store_true",
+                   help="run only a few fused decode-attention calls at the 7B decode shape "
+                        "(for hardware-counter passes)")
     p.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                    help="run only the dense quantize launch back to back for SECONDS while "
                         "sampling socket power and graphics clocks with amd-smi")
@@ -368,6 +371,96 @@ def time_attention_rotating(qj, torch, w, sk, n_sets: int, iters: int, d_v: int 
     return sum(ts) / len(ts), ts[len(ts) // 2], pct(0.1), pct(0.9)
 
 
+def time_calls(torch, fn, iters: int):
+    """(mean seconds per call back to back, median of per-call event times)."""
+    st = torch.cuda.current_stream()
+    for _ in range(5):
+        fn(st)
+    torch.cuda.synchronize()
+    a, b = HipEvent(), HipEvent()
+    a.record(st)
+    for _ in range(iters):
+        fn(st)
+    b.record(st)
+    torch.cuda.synchronize()
+    b2b = a.seconds_to(b) / iters
+    evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record(st)
+        fn(st)
+        e1.record(st)
+    torch.cuda.synchronize()
+    ts = sorted(e0.seconds_to(e1) for e0, e1 in evs)
+    return b2b, ts[len(ts) // 2]
+
+
+def decode_time_extras(qj, torch, w, sk):
+    """The per-token path at the 7B decode shape: append one new key per
+    (batch, head) (256 keys), project the 256 new queries, and the fused
+    attention of each query over its head's 8192 cached keys; plus
+    multi-query scoring (n_q queries per cached head reuse one pass over
+    the bits)."""
+    import math
+    import workloads as wl
+    dev = "cuda:0"
+    out = {}
+    G = w.groups
+    one = w.scaled(n_k=1)
+    Knew = wl.make_keys(one, dev)                      # [256, 128] bf16
+    q = wl.make_queries(w, dev)
+    nb = torch.empty(G, dtype=torch.float32, device=dev)
+    bb = torch.empty((G, w.m // 32), dtype=torch.int32, device=dev)
+    Sq = torch.empty((w.n_queries, w.m), dtype=torch.float32, device=dev)
+    t_b2b, t_med = time_calls(torch, lambda st: qj.quantize_keys(sk, Knew, norms_out=nb,
+                                                                  bits_out=bb, stream=st), 200)
+    out["append_256_keys"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
+                              "keys": G, "sketch": "dense m=256"}
+    t_b2b, t_med = time_calls(torch, lambda st: qj.project_query(sk, q, Sq_out=Sq, stream=st), 200)
+    out["project_256_queries"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med}
+    skf = qj.make_sketch(w.seed, w.d, w.m, "fqjl")
+    t_b2b, t_med = time_calls(torch, lambda st: qj.project_query(skf, q, Sq_out=Sq, stream=st), 200)
+    out["project_256_queries_fqjl"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med}
+    t_b2b, t_med = time_calls(torch, lambda st: qj.quantize_keys(skf, Knew, norms_out=nb,
+                                                                  bits_out=bb, stream=st), 200)
+    out["append_256_keys_fqjl"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med}
+    skf.close()
+    # the whole per-token step on a resident cache: append + project + attention
+    bits = wl.make_random_bits(G * w.n_k, w.m, seed=300, device=dev)
+    norms = torch.rand(G * w.n_k, device=dev) * 10 + 1
+    V = torch.randn(G * w.n_k, 128, device=dev).to(torch.bfloat16)
+    att = torch.empty(G, w.n_q, 128, device=dev)
+    ws = torch.empty(qj.decode_attention_workspace_size(sk, G, w.n_q, w.n_k, 128),
+                     dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(w.d)
+
+    def step(st):
+        qj.quantize_keys(sk, Knew, norms_out=nb, bits_out=bb, stream=st)
+        qj.project_query(sk, q, Sq_out=Sq, stream=st)
+        qj.decode_attention(sk, Sq, bits, norms, V, G, w.n_q, w.n_k, scale, workspace=ws,
+                            out=att, stream=st)
+
+    t_b2b, t_med = time_calls(torch, step, 50)
+    out["decode_token_step"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
+                                "what": "append 256 keys + project 256 queries + fused "
+                                        "attention over 256 x 8192 cached keys (bf16 V)"}
+    del V, ws, att
+    # multi-query scoring: n_q queries per cached head (GQA-style)
+    mq = {}
+    for nq in (1, 2, 4, 8, 16):
+        Sqm = torch.randn(G * nq, w.m, device=dev) * 11
+        sc = torch.empty(G, nq, w.n_k, device=dev)
+        t_b2b, t_med = time_calls(torch, lambda st: qj.score(sk, Sqm, bits, norms, G, nq, w.n_k,
+                                                              scores_out=sc, stream=st), 50)
+        nbytes = G * w.n_k * (w.m / 8 + 4) + G * nq * w.n_k * 4 + G * nq * w.m * 4
+        mq[str(nq)] = {"median_s": t_med, "scores_per_s": G * nq * w.n_k / t_med,
+                       "GBps": nbytes / t_med / 1e9}
+        del Sqm, sc
+    out["score_multiquery"] = mq
+    del bits, norms
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -380,6 +473,17 @@ def main():
         return
     if args.sustain > 0:
         sustain(args.sustain)
+        return
+    if args.attention_only:
+        import torch
+
+        import bit_quantized_jl_amd as qj
+        import workloads as wl
+        w = wl.DECODE_7B
+        sk = qj.make_sketch(w.seed, w.d, w.m, w.variant)
+        t = time_attention_rotating(qj, torch, w, sk, n_sets=1, iters=5)
+        sk.close()
+        print(json.dumps({"attention_decode7b_mean_s": t[0]}), flush=True)
         return
     import torch
 
@@ -524,6 +628,7 @@ def main():
                             "mean_s": tq, "keys_per_s": wq.n_keys / tq, "GBps": bq / tq / 1e9,
                             "bound": "hbm" if wq.variant == "dense" else "alu",
                             "timing": "10 launches back to back"}
+        result["decode_time"] = decode_time_extras(qj, torch, w, sk)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     sk.close()
