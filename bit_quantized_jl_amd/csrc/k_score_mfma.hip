@@ -23,8 +23,11 @@
 //     products and partial sums are integers below 2^24, so each row of the
 //     accumulator is exactly  R_c = sum_j (2 b_j - 1) L_c(j).
 //   * The epilogue forms sum_c 32^(4-c) R_c (rows of one query sit in lane
-//     groups 0 and 1, or 2 and 3), scales by c ||k|| 2^-F and stores with
-//     non-temporal stores (the scores are not read again by this kernel).
+//     groups 0 and 1, or 2 and 3; v_permlane16_swap adds the two groups),
+//     moves the scores of a 64-key stage to one key per lane with
+//     v_permlane32_swap, scales by c ||k|| 2^-F and stores them with one
+//     non-temporal 256-byte store per query (the scores are not read again
+//     by this kernel).
 //
 // Set-up per workgroup and query pass: each wave loads the query values,
 // starts its key stream, then computes F and the digit sums for the whole
@@ -101,26 +104,25 @@ __device__ __forceinline__ void issue_stage(unsigned char *slot, const uint32_t 
 }
 
 // Read one ring stage for this lane: the T words of key 16 u + (lane % 16),
-// lane group lane / 16, for the 4 tiles u, and the 4 norms.  The reads are
-// inline asm that waits for its own results: the ring is written by DMA,
-// which the compiler would otherwise guard with a full vmcnt(0) before every
-// read (the explicit wait_stages() before this call is the real guard).
+// lane group lane / 16, for the 4 tiles u, and the norm of key `lane` of the
+// stage.  The reads are inline asm that waits for its own results: the ring
+// is written by DMA, which the compiler would otherwise guard with a full
+// vmcnt(0) before every read (the explicit wait_stages() before this call
+// is the real guard).
 template <int T>
 struct StageRead;
 
 template <>
 struct StageRead<1> {
   uint32_t w[4][1];
-  float n[4];
+  float n;
   __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
     asm volatile(
-        "ds_read_b32 %0, %8\n\tds_read_b32 %1, %8 offset:256\n\t"
-        "ds_read_b32 %2, %8 offset:512\n\tds_read_b32 %3, %8 offset:768\n\t"
-        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
-        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "ds_read_b32 %0, %5\n\tds_read_b32 %1, %5 offset:256\n\t"
+        "ds_read_b32 %2, %5 offset:512\n\tds_read_b32 %3, %5 offset:768\n\t"
+        "ds_read_b32 %4, %6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w[0][0]), "=&v"(w[1][0]), "=&v"(w[2][0]), "=&v"(w[3][0]), "=&v"(n[0]),
-          "=&v"(n[1]), "=&v"(n[2]), "=&v"(n[3])
+        : "=&v"(w[0][0]), "=&v"(w[1][0]), "=&v"(w[2][0]), "=&v"(w[3][0]), "=&v"(n)
         : "v"(aw), "v"(an));
   }
 };
@@ -128,17 +130,15 @@ struct StageRead<1> {
 template <>
 struct StageRead<2> {
   uint32_t w[4][2];
-  float n[4];
+  float n;
   __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
     u32x2_t a, b, c, d;
     asm volatile(
-        "ds_read_b64 %0, %8\n\tds_read_b64 %1, %8 offset:512\n\t"
-        "ds_read_b64 %2, %8 offset:1024\n\tds_read_b64 %3, %8 offset:1536\n\t"
-        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
-        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:512\n\t"
+        "ds_read_b64 %2, %5 offset:1024\n\tds_read_b64 %3, %5 offset:1536\n\t"
+        "ds_read_b32 %4, %6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]),
-          "=&v"(n[3])
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n)
         : "v"(aw), "v"(an));
     w[0][0] = a.x; w[0][1] = a.y; w[1][0] = b.x; w[1][1] = b.y;
     w[2][0] = c.x; w[2][1] = c.y; w[3][0] = d.x; w[3][1] = d.y;
@@ -148,17 +148,15 @@ struct StageRead<2> {
 template <>
 struct StageRead<4> {
   uint32_t w[4][4];
-  float n[4];
+  float n;
   __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
     u32x4_t a, b, c, d;
     asm volatile(
-        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b32 %4, %9\n\tds_read_b32 %5, %9 offset:64\n\t"
-        "ds_read_b32 %6, %9 offset:128\n\tds_read_b32 %7, %9 offset:192\n\t"
+        "ds_read_b128 %0, %5\n\tds_read_b128 %1, %5 offset:1024\n\t"
+        "ds_read_b128 %2, %5 offset:2048\n\tds_read_b128 %3, %5 offset:3072\n\t"
+        "ds_read_b32 %4, %6\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]),
-          "=&v"(n[3])
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(n)
         : "v"(aw), "v"(an));
     const u32x4_t v[4] = {a, b, c, d};
 #pragma unroll
@@ -171,19 +169,18 @@ struct StageRead<4> {
 template <>
 struct StageRead<8> {
   uint32_t w[4][8];
-  float n[4];
+  float n;
   __device__ __forceinline__ void read(uint32_t aw, uint32_t an) {
     u32x4_t a0, a1, b0, b1, c0, c1, d0, d1;
     asm volatile(
-        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:16\n\t"
-        "ds_read_b128 %2, %12 offset:2048\n\tds_read_b128 %3, %12 offset:2064\n\t"
-        "ds_read_b128 %4, %12 offset:4096\n\tds_read_b128 %5, %12 offset:4112\n\t"
-        "ds_read_b128 %6, %12 offset:6144\n\tds_read_b128 %7, %12 offset:6160\n\t"
-        "ds_read_b32 %8, %13\n\tds_read_b32 %9, %13 offset:64\n\t"
-        "ds_read_b32 %10, %13 offset:128\n\tds_read_b32 %11, %13 offset:192\n\t"
+        "ds_read_b128 %0, %9\n\tds_read_b128 %1, %9 offset:16\n\t"
+        "ds_read_b128 %2, %9 offset:2048\n\tds_read_b128 %3, %9 offset:2064\n\t"
+        "ds_read_b128 %4, %9 offset:4096\n\tds_read_b128 %5, %9 offset:4112\n\t"
+        "ds_read_b128 %6, %9 offset:6144\n\tds_read_b128 %7, %9 offset:6160\n\t"
+        "ds_read_b32 %8, %10\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1), "=&v"(c0), "=&v"(c1), "=&v"(d0),
-          "=&v"(d1), "=&v"(n[0]), "=&v"(n[1]), "=&v"(n[2]), "=&v"(n[3])
+          "=&v"(d1), "=&v"(n)
         : "v"(aw), "v"(an));
     const u32x4_t v[8] = {a0, a1, b0, b1, c0, c1, d0, d1};
 #pragma unroll
@@ -195,20 +192,38 @@ struct StageRead<8> {
   }
 };
 
-// One 16-key tile: the scores of its keys (tile_limb_sums) scaled by the
-// query's exponent and the key norm, stored by the lanes of lane groups 0 and 2.
+// One 64-key stage: the MFMAs of its four tiles first (independent
+// accumulators, so they issue back to back), then the limb combination, then
+// the scores move to one key per lane -- lane l gets key l of the stage,
+// member A of each query pair in one register and member B in the other --
+// by two selects and one v_permlane32_swap (tile u's keys sit in lane group
+// u % 2 of select source u / 2), and leave with one 256-byte store per query.
+// The query scale lives in the lane groups of its member (A: 0-1, B: 2-3),
+// so each member's is read from one of its lanes.
 template <int T, int QP>
-__device__ __forceinline__ void score_tile(const uint32_t *wb, float nrm,
-                                           const QueryOperands<T, QP> &qo, int64_t key,
-                                           int64_t kend, int gq, int nqp,
-                                           float *__restrict__ outq, int64_t nk) {
-  float e[QP];
-  tile_limb_sums<T, QP>(wb, qo, e);
+__device__ __forceinline__ void score_stage(const StageRead<T> &sr, const QueryOperands<T, QP> &qo,
+                                            int64_t key, int64_t kend, int gq, int nqp,
+                                            float *__restrict__ outq, int64_t nk) {
+  v4f_t acc[4][QP];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) tile_limb_acc<T, QP>(sr.w[u], qo, acc[u]);
+  const bool odd = gq & 1;
 #pragma unroll
   for (int qp = 0; qp < QP; ++qp) {
-    const int qi = 2 * qp + (gq >> 1);
-    if ((gq & 1) == 0 && key < kend && qi < nqp)
-      __builtin_nontemporal_store((e[qp] * qo.qscale[qp]) * nrm, outq + qi * nk + key);
+    float e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = limb_rows_combine(acc[u][qp], qo.wgt);
+    const uint32_t x = __float_as_uint(odd ? e[1] : e[0]);
+    const uint32_t y = __float_as_uint(odd ? e[3] : e[2]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    const uint32_t qs = __float_as_uint(qo.qscale[qp]);
+    const float sa = __uint_as_float(__builtin_amdgcn_readlane(qs, 0)) * sr.n;
+    const float sb = __uint_as_float(__builtin_amdgcn_readlane(qs, 32)) * sr.n;
+    if (key < kend) {
+      const int qa = 2 * qp, qb = 2 * qp + 1;
+      if (qa < nqp) __builtin_nontemporal_store(__uint_as_float(sw[0]) * sa, outq + qa * nk + key);
+      if (qb < nqp) __builtin_nontemporal_store(__uint_as_float(sw[1]) * sb, outq + qb * nk + key);
+    }
   }
 }
 
@@ -267,11 +282,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         const int64_t k0 = kbeg + SM_STAGE * (wave + SM_WAVES * j);
         StageRead<T> sr;
         sr.read(lds_address(slot + ((lane & 15) * W + T * gq) * 4),
-                lds_address(slot + Ring<T>::BITS_BYTES + (lane & 15) * 4));
-#pragma unroll
-        for (int u = 0; u < SM_STAGE / 16; ++u)
-          score_tile<T, QP>(sr.w[u], sr.n[u], qo, k0 + 16 * u + (lane & 15), kend, gq, nqp,
-                            out + (g * nq + q0) * nk, nk);
+                lds_address(slot + Ring<T>::BITS_BYTES + lane * 4));
+        score_stage<T, QP>(sr, qo, k0 + lane, kend, gq, nqp, out + (g * nq + q0) * nk, nk);
       }
     }
   }

@@ -241,14 +241,13 @@ __device__ __forceinline__ void build_query_operands(const float (&sv)[2 * QP][2
   }
 }
 
-// One 16-key tile: expand the bits to the fp4 operand, run the MFMAs against
-// the query limbs and combine the limb rows.  e[qp] is the exact sum
-// sum_j (2 b_j - 1) X_j of query 2 qp + (lane group / 2) against key
-// lane % 16 (in lane groups 0-1 and 2-3 alike).
+// One 16-key tile on the matrix cores: expand the bits to the fp4 operand
+// and run the MFMAs against the query limbs.  acc[qp] holds the limb rows
+// R_c of query pair qp (rows of member 2 qp in lane groups 0-1, of 2 qp + 1
+// in lane groups 2-3) for key lane % 16.
 template <int T, int QP>
-__device__ __forceinline__ void tile_limb_sums(const uint32_t *wb, const QueryOperands<T, QP> &qo,
-                                               float (&e)[QP]) {
-  v4f_t acc[QP];
+__device__ __forceinline__ void tile_limb_acc(const uint32_t *wb, const QueryOperands<T, QP> &qo,
+                                              v4f_t (&acc)[QP]) {
 #pragma unroll
   for (int qp = 0; qp < QP; ++qp) acc[qp] = qo.cinit[qp];
 #pragma unroll
@@ -262,14 +261,33 @@ __device__ __forceinline__ void tile_limb_sums(const uint32_t *wb, const QueryOp
       acc[qp] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qo.A[qp][t], B, acc[qp], 0, 4,
                                                                   0, 127, 0, 127);
   }
+}
+
+// Combine the limb rows a lane holds with those of lane group g ^ 1 (the
+// same key, the query's other rows): v_permlane16_swap of a value with
+// itself leaves rows (0, 0, 2, 2) in one result and (1, 1, 3, 3) in the
+// other, so their sum is v + v[lane ^ 16] with no LDS traffic.  The result
+// is the exact sum_j (2 b_j - 1) X_j (integers below 2^24 throughout).
+__device__ __forceinline__ float limb_rows_combine(const v4f_t &acc, const float (&wgt)[4]) {
+  float v = acc[0] * wgt[0];
+  v = fmaf(acc[1], wgt[1], v);
+  v = fmaf(acc[2], wgt[2], v);
+  v = fmaf(acc[3], wgt[3], v);
+  const uint32_t x = __float_as_uint(v);
+  const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// One 16-key tile: e[qp] is the exact sum_j (2 b_j - 1) X_j of query
+// 2 qp + (lane group / 2) against key lane % 16 (in lane groups 0-1 and 2-3
+// alike).
+template <int T, int QP>
+__device__ __forceinline__ void tile_limb_sums(const uint32_t *wb, const QueryOperands<T, QP> &qo,
+                                               float (&e)[QP]) {
+  v4f_t acc[QP];
+  tile_limb_acc<T, QP>(wb, qo, acc);
 #pragma unroll
-  for (int qp = 0; qp < QP; ++qp) {
-    float v = acc[qp][0] * qo.wgt[0];
-    v = fmaf(acc[qp][1], qo.wgt[1], v);
-    v = fmaf(acc[qp][2], qo.wgt[2], v);
-    v = fmaf(acc[qp][3], qo.wgt[3], v);
-    e[qp] = v + __shfl_xor(v, 16);
-  }
+  for (int qp = 0; qp < QP; ++qp) e[qp] = limb_rows_combine(acc[qp], qo.wgt);
 }
 
 }  // namespace sc
