@@ -53,15 +53,14 @@ namespace {
 using namespace sc;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// Keys stream through a per-wave LDS ring filled by global_load_lds (the
-// gfx950 direct HBM -> LDS path): no registers are held by loads in flight,
+// Keys stream through a per-wave LDS ring filled by buffer_load ... lds (the
+// direct HBM -> LDS path): no registers are held by loads in flight,
 // so a wave keeps R - 1 stages of 64 keys outstanding while it computes one.
 constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
-// The first R - 1 stages are issued unconditionally (a stage past the wave's
-// range re-reads clamped, valid keys and is never consumed), so the number of
-// loads in flight is static when the loop starts.
+// The first R - 1 stages are issued unconditionally (a stage past the
+// workgroup's keys reads zeros and is never consumed), so the number of loads
+// in flight is static when the loop starts.
 
 template <int T>
 struct Ring {
@@ -82,25 +81,42 @@ __device__ __forceinline__ void wait_stages(int pending) {
   }
 }
 
-// Issue the DMA of one stage: keys [k0, k0 + 64) of the group (keys past kend
-// re-read key kend - 1; their results are never stored).
+// Buffer descriptors over the workgroup's keys [kbeg, kend) of a group: a
+// DMA past kend reads zeros (the descriptor's range check), so no address is
+// clamped, and every offset is a 32-bit register.  The keys of one
+// workgroup span less than 4 GB (the whole cache fits in HBM and is split
+// over hundreds of workgroups).
+struct StageSrc {
+  __amdgpu_buffer_rsrc_t bits, norm;
+};
+
 template <int T>
-__device__ __forceinline__ void issue_stage(unsigned char *slot, const uint32_t *__restrict__ gbits,
-                                            const float *__restrict__ gnorm, int64_t k0,
-                                            int64_t kend, int lane) {
+__device__ __forceinline__ StageSrc stage_src(const uint32_t *gbits, const float *gnorm,
+                                              int64_t kbeg, int64_t kend) {
+  constexpr int W = 4 * T;
+  const uint32_t n = kend > kbeg ? (uint32_t)(kend - kbeg) : 0u;
+  return StageSrc{
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(gbits + kbeg * W), (short)0,
+                                        (int)(n * (uint32_t)(4 * W)), 0x00020000),
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(gnorm + kbeg), (short)0,
+                                        (int)(n * 4u), 0x00020000)};
+}
+
+// Issue the DMA of one stage: keys [k0, k0 + 64) of the workgroup (k0
+// relative to its first key; keys past its end land as zeros and their
+// results are never stored).  The stage's bits are one contiguous run of
+// 64 W words, so DMA instruction i moves bytes [1024 i, 1024 i + 1024).
+template <int T>
+__device__ __forceinline__ void issue_stage(unsigned char *slot, const StageSrc &src, uint32_t k0,
+                                            int lane) {
   constexpr int W = 4 * T;
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int off = i * 1024 + lane * 16;          // byte offset inside the stage
-    const int kl = off / (W * 4);
-    const int64_t key = (k0 + kl) < kend ? (k0 + kl) : (kend - 1);
-    const uint32_t *src = gbits + key * W + (off % (W * 4)) / 4;
-    __builtin_amdgcn_global_load_lds((const gbl_void_t *)src, (lds_void_t *)(slot + i * 1024), 16,
-                                     0, 0);
-  }
-  const int64_t key = (k0 + lane) < kend ? (k0 + lane) : (kend - 1);
-  __builtin_amdgcn_global_load_lds((const gbl_void_t *)(gnorm + key),
-                                   (lds_void_t *)(slot + Ring<T>::BITS_BYTES), 4, 0, 0);
+  for (int i = 0; i < T; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.bits, (lds_void_t *)(slot + i * 1024), 16,
+                                             (int)(k0 * (4u * W) + i * 1024u + lane * 16u), 0, 0,
+                                             0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.norm, (lds_void_t *)(slot + Ring<T>::BITS_BYTES), 4,
+                                           (int)((k0 + lane) * 4u), 0, 0, 0);
 }
 
 // Read one ring stage for this lane: the T words of key 16 u + (lane % 16),
@@ -251,8 +267,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
   const int ns = (int)((nstage_blk - wave + SM_WAVES - 1) / SM_WAVES);
 
   for (int64_t g = blockIdx.y; g < G; g += gridDim.y) {
-    const uint32_t *gbits = bits + g * nk * (int64_t)W;
-    const float *gnorm = norms + g * nk;
+    const StageSrc src = stage_src<T>(bits + g * nk * (int64_t)W, norms + g * nk, kbeg, kend);
     for (int64_t q0 = 0; q0 < nq; q0 += NQ) {
       const int nqp = (int)((nq - q0) < NQ ? (nq - q0) : NQ);
       // ---- query values first (plain loads), then the first key stages
@@ -261,8 +276,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       load_query_values<m, NQ>(Sq + (g * nq + q0) * (int64_t)m, nqp, lane, sv);
 #pragma unroll
       for (int j = 0; j < R - 1; ++j)
-        issue_stage<T>(&sRing[wave][j][0], gbits, gnorm, kbeg + SM_STAGE * (wave + SM_WAVES * j),
-                       kend, lane);
+        issue_stage<T>(&sRing[wave][j][0], src, SM_STAGE * (wave + SM_WAVES * j), lane);
       // The query loads are the oldest in flight: wait for them alone.  (The
       // compiler cannot count past LDS DMA and would wait for the stages too.)
       wait_vmcnt<(R - 1) * Ring<T>::L>();
@@ -272,8 +286,8 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       // ---- stream this wave's stages through the ring
       for (int j = 0; j < ns; ++j) {
         if (j + R - 1 < ns)
-          issue_stage<T>(&sRing[wave][(j + R - 1) % R][0], gbits, gnorm,
-                         kbeg + SM_STAGE * (wave + SM_WAVES * (j + R - 1)), kend, lane);
+          issue_stage<T>(&sRing[wave][(j + R - 1) % R][0], src,
+                         SM_STAGE * (wave + SM_WAVES * (j + R - 1)), lane);
         // stages issued after stage j: up to the last real one, and at least
         // the R - 2 issued before the loop
         const int last = (ns - 1) < (j + R - 1) ? (ns - 1) : (j + R - 1);
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
       }
     }
   }
-  wait_vmcnt<0>();  // loads of clamped stages past the end must land before exit
+  wait_vmcnt<0>();  // DMA of stages past the end must land before exit
 }
 
 template <int T, int QP>

@@ -241,6 +241,15 @@ __device__ __forceinline__ void build_query_operands(const float (&sv)[2 * QP][2
   }
 }
 
+// (m & w) | (~m & c) in one v_bfi_b32 (the compiler emits an AND and an OR
+// for a constant c): the mask comes from a scalar register, c from a vector
+// register, within the one scalar operand a VOP3 instruction may read.
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t w, uint32_t c) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(w), "v"(c));
+  return d;
+}
+
 // One 16-key tile on the matrix cores: expand the bits to the fp4 operand
 // and run the MFMAs against the query limbs.  acc[qp] holds the limb rows
 // R_c of query pair qp (rows of member 2 qp in lane groups 0-1, of 2 qp + 1
@@ -253,8 +262,8 @@ __device__ __forceinline__ void tile_limb_acc(const uint32_t *wb, const QueryOpe
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const uint32_t w = wb[t];
-    const v8i_t B = v8i_t{(int)((w & 0x11111111u) | 0x22222222u), (int)(w & 0x22222222u),
-                          (int)(w & 0x44444444u), (int)((w & 0x88888888u) | 0x22222222u),
+    const v8i_t B = v8i_t{(int)bfi(0x11111111u, w, 0x22222222u), (int)(w & 0x22222222u),
+                          (int)(w & 0x44444444u), (int)bfi(0x88888888u, w, 0x22222222u),
                           0, 0, 0, 0};
 #pragma unroll
     for (int qp = 0; qp < QP; ++qp)
