@@ -458,6 +458,15 @@ def decode_time_extras(qj, torch, w, sk):
     out["score_multiquery"] = mq
     del bits, norms
     torch.cuda.empty_cache()
+    # fused attention with several queries per cached head (grouped-query)
+    am = {}
+    for G2, nq in ((256, 1), (256, 4), (64, 8)):
+        w2 = w.scaled(batch=1, heads=G2, n_q=nq)
+        t_mean, t_med, _, _ = time_attention_rotating(qj, torch, w2, sk, n_sets=2, iters=30)
+        am[f"{G2}x{nq}"] = {"median_s": t_med, "queries": G2 * nq, "keys_per_group": w2.n_k,
+                            "GBps": attention_bytes(w2) / t_med / 1e9}
+    out["attention_multiquery"] = am
+    torch.cuda.empty_cache()
     return out
 
 

@@ -193,6 +193,7 @@ __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOpe
           if (PAIR) st.acc[qp][1][d] = fmaf(pB, vals[j][d], st.acc[qp][1][d]);
         }
       }
+      if (QP > 1) __builtin_amdgcn_sched_barrier(0);  // one pair's temporaries at a time
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -223,14 +224,15 @@ __device__ __forceinline__ void stream_keys(AttnStage<T> (&b)[R], const KeyRange
 }
 
 // ws layout: [G * nq][P][AT_PART], one partial per workgroup along the keys
-// (P = gridDim.x): the weighted sum, then M and L (exp2 domain).  PAIR is
+// (P = gridDim.x): the weighted sum, then M and L (exp2 domain).  A pass
+// serves QP query pairs (QP <= 2: one merging wave per query); PAIR is
 // nq > 1 (with one query per group, member B's sums are never formed).
 template <int T, int QP, bool PAIR>
-__global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
+__global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
     int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws) {
-  static_assert(QP == 1, "one query pair per pass");
+  static_assert(QP == 1 || QP == 2, "one or two query pairs per pass");
   constexpr int W = 4 * T;
   constexpr int m = 32 * W;
   constexpr int NQ = 2 * QP;
@@ -268,33 +270,36 @@ __global__ __launch_bounds__(SM_THREADS, 2) void attn_partial_kernel(
       for (int r = 0; r < R; ++r) load_attn_stage<T>(ring[r], kr, AT_STAGE * (wave + SM_WAVES * r), lane);
       SoftmaxState<QP> st;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        st.M[0][h] = -INFINITY;
-        st.L[0][h] = 0.f;
+      for (int qp = 0; qp < QP; ++qp)
 #pragma unroll
-        for (int d = 0; d < 8; ++d) st.acc[0][h][d] = 0.f;
-      }
+        for (int h = 0; h < 2; ++h) {
+          st.M[qp][h] = -INFINITY;
+          st.L[qp][h] = 0.f;
+#pragma unroll
+          for (int d = 0; d < 8; ++d) st.acc[qp][h][d] = 0.f;
+        }
       stream_keys<T, QP, PAIR, R>(ring, kr, qo, wave, lane, nsr, nkb, nqp, sl2, st);
       // ---- this wave's partials: sum the four lane groups (each saw every
       // fourth value row); lanes 0..15 then hold dims 8 lane .. 8 lane + 7
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (h >= nqp) break;
+      for (int qi = 0; qi < NQ; ++qi) {
+        if (qi >= nqp) break;
+        const int qp = qi >> 1, h = qi & 1;
         float a[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-          a[d] = st.acc[0][h][d];
+          a[d] = st.acc[qp][h][d];
           a[d] += __shfl_xor(a[d], 16);
           a[d] += __shfl_xor(a[d], 32);
         }
-        float *dst = sPart[wave][h];
+        float *dst = sPart[wave][qi];
         if (lane < 16) {
           reinterpret_cast<float4 *>(dst)[2 * lane] = make_float4(a[0], a[1], a[2], a[3]);
           reinterpret_cast<float4 *>(dst)[2 * lane + 1] = make_float4(a[4], a[5], a[6], a[7]);
         }
         if (lane == 0) {
-          dst[AT_DV] = st.M[0][h];
-          dst[AT_DV + 1] = st.L[0][h];
+          dst[AT_DV] = st.M[qp][h];
+          dst[AT_DV + 1] = st.L[qp][h];
         }
       }
       __syncthreads();
@@ -458,7 +463,7 @@ hipError_t launch_attn_t(const float *Sq, const uint32_t *bits, const float *nor
     hipLaunchKernelGGL((attn_partial_kernel<T, QP, true>), grid, dim3(SM_THREADS), 0, st, Sq,
                        bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
   else
-    hipLaunchKernelGGL((attn_partial_kernel<T, QP, false>), grid, dim3(SM_THREADS), 0, st, Sq,
+    hipLaunchKernelGGL((attn_partial_kernel<T, 1, false>), grid, dim3(SM_THREADS), 0, st, Sq,
                        bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
   const int64_t rows = G * nq;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)), dim3(64),
@@ -513,12 +518,19 @@ hipError_t launch_attention_fused(const qjl_sketch *sk, const float *Sq, const u
   const float c = estimator_scale(h.m, h.rho);
   const float sl2 = scale * LOG2E;
   const uint16_t *Vb = static_cast<const uint16_t *>(V);
-  // One query pair per pass: a second pair's accumulators would not fit the
-  // registers beside two stages of value rows.
+  // Three or more queries per group (grouped-query attention) take two
+  // query pairs per pass, so each pass over the values serves four queries.
+  const bool two = nq >= 3;
   switch (h.m / 128) {
-    case 1: return launch_attn_t<1, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
-    case 2: return launch_attn_t<2, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
-    case 4: return launch_attn_t<4, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 1:
+      return two ? launch_attn_t<1, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
+                 : launch_attn_t<1, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 2:
+      return two ? launch_attn_t<2, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
+                 : launch_attn_t<2, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 4:
+      return two ? launch_attn_t<4, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
+                 : launch_attn_t<4, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
     case 8: return launch_attn_t<8, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
     default: return hipErrorInvalidValue;
   }
