@@ -340,9 +340,6 @@ hipError_t launch_sm_t(int qp, const float *Sq, const uint32_t *bits, const floa
   if constexpr (T <= 4) {
     if (qp == 4) return launch_sm<T, 4>(Sq, bits, norms, m, G, nq, nk, c, scores, st);
   }
-  if constexpr (T <= 2) {
-    if (qp == 8) return launch_sm<T, 8>(Sq, bits, norms, m, G, nq, nk, c, scores, st);
-  }
   return hipErrorInvalidValue;
 }
 
@@ -357,7 +354,9 @@ hipError_t launch_score(const qjl_sketch *sk, const float *Sq, const uint32_t *b
     return launch_score_generic(sk, Sq, bits, norms, G, nq, nk, scores, st);
   const int W = m / 32;
   const int T = W / 4;
-  const int qp_max = T <= 2 ? 8 : (T <= 4 ? 4 : 2);
+  // up to four query pairs per pass (eight pairs measured slower: one
+  // workgroup per CU and spills; two passes of four re-read the bits instead)
+  const int qp_max = T <= 4 ? 4 : 2;
   int qp = 1;
   while (qp < qp_max && 2 * qp < nq) qp *= 2;
   const float c = estimator_scale(m, sk->host.rho);
