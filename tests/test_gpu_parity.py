@@ -128,6 +128,40 @@ def test_score_random_bits(m, G, nq, nk):
     sk.close()
 
 
+@pytest.mark.parametrize("variant,d,m,dt,rho", [
+    ("dense", 512, 64, "bf16", 0.0),      # largest dense d
+    ("dense", 1, 32, "f32", 0.0),         # smallest d and m
+    ("dense", 128, 8192, "bf16", 0.0),    # largest m
+    ("dense", 64, 8192, "f32", 0.2),
+    ("fqjl", 128, 8192, "bf16", 0.1),     # 64 stacked blocks
+    ("fqjl", 8, 8192, "f32", 0.0),
+    ("dfqjl", 128, 8192, "bf16", 0.1),
+    ("pfqjl", 16, 8192, "f32", 0.0),
+])
+def test_size_limits(variant, d, m, dt, rho):
+    w = wl.Workload(f"limit_{variant}_{d}_{m}", d, m, variant, 1, 3, 67, 3, dt, "normal", rho,
+                    seed=9)
+    note("limits", variant, d, m, dt, rho)
+    _, K, bits, norms, rb, rn = run_quantize_case(w)
+    q = wl.make_queries(w, "cpu").to(DEV)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    Sq = qj.project_query(sk, q)
+    out = qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
+    Sq_ref = oq.project(ref, to_np_f64(q), w.dtype)
+    check_projection(to_np_f64(Sq), Sq_ref, to_np_f64(q), w.m)
+    s_ref = oq.score(Sq_ref, rb, rn, w.m, w.rho, w.groups, w.n_q, w.n_k)
+    slack = inband_slack(bits_np(bits), rb, Sq_ref, rn, w.m, w.rho, w.groups, w.n_q, w.n_k)
+    # the GPU scores its own projected query: widen by the projection's
+    # difference, which moves a score by at most c ||k|| sum_j |dSq_j|
+    dsq = np.abs(to_np_f64(Sq) - Sq_ref).sum(axis=1).reshape(w.groups, w.n_q, 1)
+    c = oq.estimator_constant(w.m, w.rho)
+    slack = slack + c * rn.reshape(w.groups, 1, w.n_k) * dsq
+    check_scores(to_np_f64(out), s_ref, slack)
+    sk.close()
+
+
 def test_score_dither_constant():
     # rho enters the score only through sqrt(1 + rho^2)
     m, G, nq, nk = 256, 1, 2, 300
