@@ -211,9 +211,11 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
         ssq = fmaf(v, v, ssq);
       }
       nrm = sqrtf(ssq + __shfl_xor(ssq, 32));
-      if (valid && sh == 0) norms[row] = nrm;
+      if (valid && sh == 0 && blockIdx.y == 0) norms[row] = nrm;
     }
-    for (int b = 0; b < nb; ++b) {
+    // blocks b = blockIdx.y, blockIdx.y + gridDim.y, ...: a short call (few
+    // rows, e.g. one new key per head) spreads its blocks over workgroups
+    for (int b = blockIdx.y; b < nb; b += gridDim.y) {
       // Re-widen the row inside each block: hoisted out of this loop, the
       // widened copy would sit in registers beside the packed one.
 #pragma unroll
@@ -365,9 +367,12 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
     if (((uintptr_t)X & 15) == 0) {  // rows are whole 16-byte vectors
       const int64_t tiles2 = (n + 31) / 32;
       const int grid2 = (int)(tiles2 < 32768 ? tiles2 : 32768);
+      // Few rows: one workgroup per (row tile, block) so the blocks run side
+      // by side (a row is then loaded once per block instead of once).
+      const int gy = tiles2 * nb <= 4096 ? nb : 1;
 #define QJL_FQJL128_LAUNCH(...)                                                                  \
-  hipLaunchKernelGGL((fqjl128_kernel<__VA_ARGS__>), dim3(grid2), dim3(64), 0, st, X, nb, h.m,    \
-                     sk->Dsign, sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
+  hipLaunchKernelGGL((fqjl128_kernel<__VA_ARGS__>), dim3(grid2, gy), dim3(64), 0, st, X, nb,     \
+                     h.m, sk->Dsign, sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
       if (!perm && proj) QJL_FQJL128_LAUNCH(T, true, false, false);
       else if (!perm && dith) QJL_FQJL128_LAUNCH(T, false, true, false);
       else if (proj) QJL_FQJL128_LAUNCH(T, true, false, true);
