@@ -8,6 +8,24 @@
 
 namespace qjl {
 
+// Workgroups of `kernel` (launched with `threads` threads and no dynamic
+// LDS) that the current device holds at once: compute units times the
+// occupancy the runtime reports (fallbacks: 256 units, one workgroup each).
+// Callers cache it in a function-local static, whose initialization C++
+// makes thread safe.
+template <typename K>
+int resident_workgroups(K kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  return cus * per_cu;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }

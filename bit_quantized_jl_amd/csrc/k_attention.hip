@@ -430,19 +430,7 @@ __global__ __launch_bounds__(256) void attn_softmax_kernel(const float *__restri
 // all groups (as the score kernel), at most 65535 groups per launch row.
 template <int T, int QP>
 void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
-  static int resident = 0;
-  if (resident == 0) {
-    int dev = 0, cus = 256, per_cu = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_partial_kernel<T, QP, true>,
-                                                     SM_THREADS, 0) != hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-    resident = cus * per_cu;
-  }
+  static const int resident = resident_workgroups(attn_partial_kernel<T, QP, true>, SM_THREADS);
   int64_t chunk = (G * nk + resident - 1) / resident;
   constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
   chunk = (chunk + round - 1) / round * round;

@@ -300,19 +300,7 @@ hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, float *
   constexpr int WAVES = M <= 256 ? 4 : 8;
   constexpr bool DEFER = M <= 256;
   auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER>;
-  static int resident = 0;  // workgroups resident on the whole device
-  if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WAVES, 0) !=
-            hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-    resident = cus * per_cu;
-  }
+  static const int resident = resident_workgroups(kern, 64 * WAVES);  // on the whole device
   const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)(want < resident ? want : resident);

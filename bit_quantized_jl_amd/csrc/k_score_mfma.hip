@@ -310,19 +310,7 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   (void)m;
   // One resident round: size the chunks so the grid is (about) the number of
   // workgroups the chip holds at once, so no partial second round idles CUs.
-  static int resident = 0;
-  if (resident == 0) {
-    int dev = 0, cus = 256, per_cu = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_mfma_kernel<T, QP>,
-                                                     SM_THREADS, 0) != hipSuccess ||
-        per_cu <= 0)
-      per_cu = 1;
-    resident = cus * per_cu;
-  }
+  static const int resident = resident_workgroups(score_mfma_kernel<T, QP>, SM_THREADS);
   // chunk: a multiple of the 256 keys one block step covers
   int64_t chunk = (G * nk + resident - 1) / resident;
   chunk = (chunk + 255) / 256 * 256;
