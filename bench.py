@@ -48,8 +48,8 @@ def parse():
                    help="only the timed step (used under profilers)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
-    p.add_argument("--attention-only", action="store_true",
-                   help="run only a few fused decode-attention calls at the 7B decode shape "
+    p.add_argument("--only", choices=["quantize", "fqjl", "fqjl_dither", "score", "attention"],
+                   help="run only a few launches of one kernel on its 7B-decode-shape workload "
                         "(for hardware-counter passes)")
     p.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                    help="run only the dense quantize launch back to back for SECONDS while "
@@ -470,6 +470,29 @@ def decode_time_extras(qj, torch, w, sk):
     return out
 
 
+def run_only(kind: str):
+    """A few launches of one kernel (for rocprofv3 counter passes)."""
+    import torch
+
+    import bit_quantized_jl_amd as qj
+    import workloads as wl
+    if kind == "attention":
+        w = wl.DECODE_7B
+        sk = qj.make_sketch(w.seed, w.d, w.m, w.variant)
+        t = time_attention_rotating(qj, torch, w, sk, n_sets=1, iters=5)[0]
+    elif kind == "score":
+        w = wl.DECODE_7B
+        sk = qj.make_sketch(w.seed, w.d, w.m, w.variant)
+        t = time_score_rotating(qj, torch, w, sk, n_sets=1, iters=5)[0]
+    else:
+        w = {"quantize": wl.DECODE_7B, "fqjl": wl.FQJL_7B, "fqjl_dither": wl.FQJL_7B_DITHER}[kind]
+        sk = None
+        t = time_quantize(qj, torch, w, reps=3)[0]
+    if sk is not None:
+        sk.close()
+    print(json.dumps({"only": kind, "workload": w.name, "mean_s": t}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -483,16 +506,8 @@ def main():
     if args.sustain > 0:
         sustain(args.sustain)
         return
-    if args.attention_only:
-        import torch
-
-        import bit_quantized_jl_amd as qj
-        import workloads as wl
-        w = wl.DECODE_7B
-        sk = qj.make_sketch(w.seed, w.d, w.m, w.variant)
-        t = time_attention_rotating(qj, torch, w, sk, n_sets=1, iters=5)
-        sk.close()
-        print(json.dumps({"attention_decode7b_mean_s": t[0]}), flush=True)
+    if args.only:
+        run_only(args.only)
         return
     import torch
 
