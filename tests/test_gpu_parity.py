@@ -162,6 +162,37 @@ def test_size_limits(variant, d, m, dt, rho):
     sk.close()
 
 
+def test_one_sketch_two_streams_concurrently():
+    # a sketch is immutable: two streams quantizing and scoring different
+    # caches with it at once give each the results it gets alone
+    note("two streams")
+    w = wl.DECODE_7B.scaled(batch=1, heads=8, n_k=4096)
+    sk = qj.make_sketch(w.seed, w.d, w.m, w.variant)
+    K1 = wl.make_keys(w, DEV)
+    K2 = (K1.float() * -0.5 + 0.25).to(torch.bfloat16)
+    q = wl.make_queries(w, DEV)
+    ref = []
+    for K in (K1, K2):
+        n, b = qj.quantize_keys(sk, K)
+        Sq = qj.project_query(sk, q)
+        ref.append((n, b, qj.score(sk, Sq, b, n, w.groups, w.n_q, w.n_k)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(3):
+        outs.clear()
+        for K, st in zip((K1, K2), streams):
+            with torch.cuda.stream(st):
+                n, b = qj.quantize_keys(sk, K, stream=st)
+                Sq = qj.project_query(sk, q, stream=st)
+                outs.append((n, b, qj.score(sk, Sq, b, n, w.groups, w.n_q, w.n_k, stream=st)))
+        torch.cuda.synchronize()
+        for (n, b, s), (rn, rb, rs) in zip(outs, ref):
+            assert torch.equal(b, rb) and torch.equal(n, rn) and torch.equal(s, rs)
+    sk.close()
+
+
 def test_score_dither_constant():
     # rho enters the score only through sqrt(1 + rho^2)
     m, G, nq, nk = 256, 1, 2, 300
