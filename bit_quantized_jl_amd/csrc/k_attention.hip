@@ -25,19 +25,17 @@
 // a plain path: the
 // score kernel writes the scores to the workspace and attn_softmax_kernel
 // forms the weighted sum.
-#include "score_common.h"
+#include "attn_common.h"
 
 namespace qjl {
 
 namespace {
 
 using namespace sc;
+using namespace at;
 
 constexpr int AT_TILES = 1;   // 16-key tiles per stage
 constexpr int AT_STAGE = 16 * AT_TILES;  // keys per stage
-constexpr int AT_DV = 128;    // value width of the fast path
-constexpr int AT_PART = AT_DV + 4;  // floats per partial: sum, M, L, padding to 16 bytes
-constexpr float LOG2E = 1.4426950408889634f;
 
 template <int T>
 struct AttnStage {
@@ -102,29 +100,6 @@ __device__ __forceinline__ void load_attn_stage(AttnStage<T> &s, const KeyRange 
   }
   s.n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
       kr.norm, (int)(4u * (uint32_t)(k0 + (lane & (AT_STAGE - 1)))), 0, 0));
-}
-
-// Maximum and sum over the 16 lanes of each row (lane i exchanges with
-// i ^ 1, i ^ 2, then the mirrored lane of its half-row and of its row), the
-// result in every lane of the row.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false));
-  return v;
-}
-
-// exp2(x - m) with m = -inf (nothing seen yet) giving 0 instead of NaN.
-__device__ __forceinline__ float exp2_shift(float x, float m) {
-  return m == -INFINITY ? 0.f : exp2f(x - m);
 }
 
 // Running softmax state of the queries a lane serves: per query pair qp,
@@ -472,6 +447,12 @@ int attn_partials_t(int64_t G, int64_t nk) {
 // Sketch sizes with a fused instantiation (T = m / 128 words per lane group).
 static bool fused_m(int m) { return m == 128 || m == 256 || m == 512 || m == 1024; }
 
+hipError_t launch_attn_combine(const float *ws, int64_t rows, int P, float *out, hipStream_t st) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)), dim3(64),
+                     0, st, ws, rows, P, out);
+  return hipGetLastError();
+}
+
 // Whether the fused path serves this call (the rest takes the plain path).
 bool attention_fused_supported(const qjl_sketch *sk, const uint32_t *bits, const void *V,
                                int v_dtype, int dv, int64_t nk) {
@@ -492,6 +473,10 @@ size_t attention_workspace_bytes(const qjl_sketch *sk, int64_t G, int64_t nq, in
       case 8: P = attn_partials_t<8>(G, nk); break;
       default: P = 0;
     }
+    if (attn_mq_supported(m / 128)) {
+      const int Pm = attn_mq_partials(m / 128, G, nk);
+      P = P > Pm ? P : Pm;
+    }
     fused = (size_t)G * nq * P * AT_PART * sizeof(float);
   }
   const size_t plain = (size_t)G * nq * nk * sizeof(float);
@@ -506,19 +491,19 @@ hipError_t launch_attention_fused(const qjl_sketch *sk, const float *Sq, const u
   const float c = estimator_scale(h.m, h.rho);
   const float sl2 = scale * LOG2E;
   const uint16_t *Vb = static_cast<const uint16_t *>(V);
-  // Three or more queries per group (grouped-query attention) take two
-  // query pairs per pass, so each pass over the values serves four queries.
-  const bool two = nq >= 3;
-  switch (h.m / 128) {
-    case 1:
-      return two ? launch_attn_t<1, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
-                 : launch_attn_t<1, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
-    case 2:
-      return two ? launch_attn_t<2, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
-                 : launch_attn_t<2, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
-    case 4:
-      return two ? launch_attn_t<4, 2>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st)
-                 : launch_attn_t<4, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+  const int T = h.m / 128;
+  // Three or more queries per group (grouped-query attention): up to eight
+  // queries per pass, their weighted sums on the matrix cores.
+  if (nq >= 3 && attn_mq_supported(T)) {
+    int P = 0;
+    hipError_t e = launch_attn_mq_partials(T, Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, &P, st);
+    if (e != hipSuccess) return e;
+    return launch_attn_combine(ws, G * nq, P, out, st);
+  }
+  switch (T) {
+    case 1: return launch_attn_t<1, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 2: return launch_attn_t<2, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
+    case 4: return launch_attn_t<4, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
     case 8: return launch_attn_t<8, 1>(Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, st);
     default: return hipErrorInvalidValue;
   }

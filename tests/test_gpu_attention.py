@@ -69,7 +69,12 @@ def oracle_attention(Sq, bits, norms, V, m, rho, scale, G, nq, nk, slack=None):
 FUSED = [(128, 1, 1, 1, 128, "bf16"), (128, 2, 1, 17, 128, "bf16"),
          (256, 3, 1, 1000, 128, "bf16"), (512, 1, 3, 4096, 128, "bf16"),
          (1024, 2, 2, 2049, 128, "bf16"), (256, 1, 1, 50001, 128, "bf16"),
-         (256, 5, 4, 257, 128, "bf16")]
+         (256, 5, 4, 257, 128, "bf16"),
+         # three or more queries per group: the matrix-core weighted sums
+         (128, 2, 8, 1000, 128, "bf16"), (256, 3, 7, 513, 128, "bf16"),
+         (512, 2, 6, 2049, 128, "bf16"), (256, 1, 16, 4096, 128, "bf16"),
+         (128, 1, 3, 31, 128, "bf16"), (512, 4, 5, 20000, 128, "bf16"),
+         (1024, 1, 4, 300, 128, "bf16")]
 PLAIN = [(384, 1, 2, 300, 128, "bf16"), (256, 2, 1, 300, 128, "f32"),
          (256, 2, 2, 300, 64, "bf16"), (96, 1, 2, 130, 128, "bf16"),
          (2048, 1, 1, 64, 128, "bf16"), (32, 3, 3, 33, 7, "f32")]
