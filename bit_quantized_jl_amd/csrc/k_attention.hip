@@ -20,11 +20,12 @@
 // (LDS DMA for the bits, as in the score kernel, would make the compiler wait
 // for every load before using the value registers.)
 //
-// Shapes the fast path does not cover (d_v != 128, float values, m other than
-// 128, 256, 512 or 1024, unaligned buffers, 2^22 keys or more per group) take
-// a plain path: the
-// score kernel writes the scores to the workspace and attn_softmax_kernel
-// forms the weighted sum.
+// This kernel serves one or two queries per group (and m = 1024); three or
+// more take attn_mq_kernel (k_attention_mq.hip), whose weighted sums run on
+// the matrix cores.  Shapes neither fast path covers (d_v != 128, float
+// values, m other than 128, 256, 512 or 1024, unaligned buffers, 2^22 keys or
+// more per group) take a plain path: the score kernel writes the scores to
+// the workspace and attn_softmax_kernel forms the weighted sum.
 #include "attn_common.h"
 
 namespace qjl {
