@@ -207,9 +207,11 @@ qjl_status qjl_decode_attention_workspace_size(const qjl_sketch *sk, int64_t n_g
  * v_dtype (values are not sketched); out: device float[n_groups][n_q][d_v];
  * workspace: device, 16-byte aligned, at least the size above (holds the
  * per-workgroup softmax partials, or the scores on the plain path).  The fast
- * path takes bf16 values with d_v = 128, m of 128, 256, 512 or 1024, fewer
- * than 2^22 keys per group and 16-byte aligned bits and V; other shapes give
- * the same result through a plain path.  Calls sharing one workspace must be ordered (one stream).
+ * paths take bf16 values with d_v = 128, m of 128, 256, 512 or 1024, fewer
+ * than 2^22 keys per group and 16-byte aligned bits and V (three or more
+ * queries per group with m <= 512 form the weighted sums on the matrix
+ * cores); other shapes give the same result through a plain path.  Calls
+ * sharing one workspace must be ordered (one stream).
  * n_groups == 0 or n_q == 0 -> no-op.  Errors: NULL pointers, negative
  * counts, n_k == 0 with n_q > 0, d_v < 1, bad v_dtype, misalignment,
  * workspace_bytes below the required size, softmax_scale not finite, sketch
