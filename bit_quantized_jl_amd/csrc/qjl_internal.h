@@ -77,6 +77,10 @@ hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtyp
                                    int64_t base, float *norms, uint32_t *bits, hipStream_t st);
 hipError_t launch_project_dense(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
                                 float *Sq, hipStream_t st);
+bool project_mfma_supported(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
+                            const float *Sq);
+hipError_t launch_project_mfma(const qjl_sketch *sk, const void *q, int64_t n, float *Sq,
+                               hipStream_t st);
 bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
                              const uint32_t *bits);
 hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, float *norms,

@@ -166,7 +166,12 @@ qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype,
  * Project n_queries queries: Sq_out[i] = S q_i in float32, not quantized (the
  * "standard JL transform without quantization" of the QJL abstract; no
  * dither).  q: device [n_queries][d] in `dtype`; Sq_out: device
- * float[n_queries][m].  Errors as for qjl_quantize_keys.
+ * float[n_queries][m].  Errors as for qjl_quantize_keys.  For a dense sketch
+ * and bfloat16 queries with d % 16 == 0, m % 64 == 0 and 16-byte aligned q
+ * and Sq_out, the products run on the matrix cores exactly as in the
+ * quantizer (exact bf16 products, float32 sums), so projecting a key gives
+ * the very signs qjl_quantize_keys stores for it; other cases sum in
+ * float32 in increasing coordinate order.
  */
 qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
                              int64_t n_queries, float *Sq_out, void *stream);

@@ -91,16 +91,17 @@ def test_quantize_shapes(variant, d, m, dt, rho):
     run_quantize_case(w, base=11)
 
 
-@pytest.mark.parametrize("variant,d,m,dt", [("dense", 128, 256, "f32"), ("dense", 128, 256, "bf16"),
-                                            ("dense", 100, 96, "bf16"), ("dense", 16, 512, "f32"),
-                                            ("fqjl", 128, 256, "bf16"), ("fqjl", 8, 32, "f32"),
-                                            ("fqjl", 64, 192, "f32"), ("fqjl", 128, 512, "bf16"),
-                                            ("dfqjl", 128, 256, "bf16"), ("dfqjl", 16, 64, "f32"),
-                                            ("pfqjl", 128, 256, "bf16")])
-def test_project_query(variant, d, m, dt):
-    note("project", variant, d, m, dt)
+@pytest.mark.parametrize("variant,d,m,dt,nq", [
+    ("dense", 128, 256, "f32", 37), ("dense", 128, 256, "bf16", 37), ("dense", 100, 96, "bf16", 37),
+    ("dense", 16, 512, "f32", 37), ("dense", 128, 256, "bf16", 300), ("dense", 64, 128, "bf16", 33),
+    ("dense", 256, 64, "bf16", 65), ("dense", 48, 192, "bf16", 31), ("dense", 16, 64, "bf16", 1),
+    ("dense", 128, 512, "bf16", 70), ("fqjl", 128, 256, "bf16", 37), ("fqjl", 8, 32, "f32", 37),
+    ("fqjl", 64, 192, "f32", 37), ("fqjl", 128, 512, "bf16", 37), ("dfqjl", 128, 256, "bf16", 37),
+    ("dfqjl", 16, 64, "f32", 37), ("pfqjl", 128, 256, "bf16", 37)])
+def test_project_query(variant, d, m, dt, nq):
+    note("project", variant, d, m, dt, nq)
     rho = 0.1 if variant == "dfqjl" else 0.0  # queries are never dithered
-    w = wl.Workload("proj", d, m, variant, 1, 1, 1, 37, dt, seed=5)
+    w = wl.Workload("proj", d, m, variant, 1, 1, 1, nq, dt, seed=5)
     q = wl.make_queries(w, "cpu").to(DEV)
     sk = qj.make_sketch(5, d, m, variant, rho)
     Sq = qj.project_query(sk, q)
@@ -108,6 +109,24 @@ def test_project_query(variant, d, m, dt):
     ref = oracle_sketch(5, d, m, variant, rho)
     qd = to_np_f64(q)
     check_projection(to_np_f64(Sq), oq.project(ref, qd, dt), qd, m)
+    sk.close()
+
+
+@pytest.mark.parametrize("d,m", [(128, 256), (64, 512), (128, 128)])
+def test_projected_keys_reproduce_their_bits(d, m):
+    # Projecting bf16 keys as queries applies the same S as quantizing them
+    # (same bf16 sketch, same float32 matrix-core accumulation), so the signs
+    # of the projection are the quantized bits, bit for bit.
+    note("project-vs-quantize", d, m)
+    n = 333
+    K = torch.randn(n, d, generator=torch.Generator().manual_seed(d + m)).to(torch.bfloat16)
+    sk = qj.make_sketch(9, d, m, "dense", 0.0)
+    norms, bits = qj.quantize_keys(sk, K.to(DEV))
+    Sq = qj.project_query(sk, K.to(DEV))
+    torch.cuda.synchronize()
+    got = oq.unpack_bits(bits_np(bits), m).astype(bool)
+    want = to_np_f64(Sq) >= 0
+    assert got.shape == want.shape and np.array_equal(got, want)
     sk.close()
 
 
