@@ -198,17 +198,26 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
         xw[4 * v + 3] = q.w;
       }
     }
-    auto elem = [&](int c) -> uint32_t {  // float bits of element c
-      if constexpr (sizeof(T) == 4) return xw[c];
-      else return (c & 1) ? (xw[c >> 1] & 0xFFFF0000u) : (xw[c >> 1] << 16);
+    // Float bits of element c with its sign flipped by sm (0 or the sign
+    // bit).  For an even bf16 element the flip is an add, which carries out of
+    // bit 31 and so equals the xor: one v_lshl_add_u32 widens and flips.
+    auto elem_flip = [&](int c, uint32_t sm) -> uint32_t {
+      if constexpr (sizeof(T) == 4) return xw[c] ^ sm;
+      else return (c & 1) ? ((xw[c >> 1] & 0xFFFF0000u) ^ sm) : ((xw[c >> 1] << 16) + sm);
     };
     float nrm = 0.f;
-    if (!PROJECT) {  // each lane half sums half the row
+    if (!PROJECT) {  // each lane half sums half the row, one selected word at a time
       float ssq = 0.f;
 #pragma unroll
-      for (int c = 0; c < H; ++c) {
-        const float v = __uint_as_float(sh ? elem(c + H) : elem(c));
-        ssq = fmaf(v, v, ssq);
+      for (int i = 0; i < NW / 2; ++i) {
+        const uint32_t w = sh ? xw[i + NW / 2] : xw[i];
+        if constexpr (sizeof(T) == 4) {
+          ssq = fmaf(__uint_as_float(w), __uint_as_float(w), ssq);
+        } else {
+          const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+          ssq = fmaf(lo, lo, ssq);
+          ssq = fmaf(hi, hi, ssq);
+        }
       }
       nrm = sqrtf(ssq + __shfl_xor(ssq, 32));
       if (valid && sh == 0 && blockIdx.y == 0) norms[row] = nrm;
@@ -226,8 +235,8 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
       float t[H];
 #pragma unroll
       for (int c = 0; c < H; ++c) {
-        const float lo = __uint_as_float(elem(c) ^ ds[c]);
-        const float hi = __uint_as_float(elem(c + H) ^ ds[c + H]);
+        const float lo = __uint_as_float(elem_flip(c, ds[c]));
+        const float hi = __uint_as_float(elem_flip(c + H, ds[c + H]));
         t[c] = fmaf(sgn, hi, lo);
       }
       fwht_reg<H>(t);
