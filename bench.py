@@ -468,6 +468,16 @@ def decode_time_extras(qj, torch, w, sk):
     out["decode_token_step"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
                                 "what": "append 256 keys + project 256 queries + fused "
                                         "attention over 256 x 8192 cached keys (bf16 V)"}
+    # the same step captured once into a HIP graph and replayed per token
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    t_b2b, t_med = time_calls(torch, lambda st: graph.replay(), 50)
+    out["decode_token_step_graph"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
+                                      "what": "the decode_token_step launches replayed as one "
+                                              "HIP graph"}
+    del graph
     del V, ws, att
     # multi-query scoring: n_q queries per cached head (GQA-style)
     mq = {}
