@@ -458,16 +458,23 @@ def decode_time_extras(qj, torch, w, sk):
                      dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(w.d)
 
+    # each head's new key goes straight into its cache slot (the last of n_k rows)
+    t_b2b, t_med = time_calls(torch, lambda st: qj.quantize_keys_into(
+        sk, Knew, G, norms, bits, w.n_k, w.n_k - 1, stream=st), 200)
+    out["append_256_keys_into_cache"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
+                                         "keys": G, "cache_rows_per_head": w.n_k}
+
     def step(st):
-        qj.quantize_keys(sk, Knew, norms_out=nb, bits_out=bb, stream=st)
+        qj.quantize_keys_into(sk, Knew, G, norms, bits, w.n_k, w.n_k - 1, stream=st)
         qj.project_query(sk, q, Sq_out=Sq, stream=st)
         qj.decode_attention(sk, Sq, bits, norms, V, G, w.n_q, w.n_k, scale, workspace=ws,
                             out=att, stream=st)
 
     t_b2b, t_med = time_calls(torch, step, 50)
     out["decode_token_step"] = {"mean_s_back_to_back": t_b2b, "median_s": t_med,
-                                "what": "append 256 keys + project 256 queries + fused "
-                                        "attention over 256 x 8192 cached keys (bf16 V)"}
+                                "what": "append 256 keys into their cache rows + project "
+                                        "256 queries + fused attention over 256 x 8192 "
+                                        "cached keys (bf16 V), the new keys included"}
     # the same step captured once into a HIP graph and replayed per token
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     make_sketch,
     project_query,
     quantize_keys,
+    quantize_keys_into,
     score,
     sketch_export,
     status_string,

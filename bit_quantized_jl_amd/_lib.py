@@ -50,6 +50,7 @@ def _declare(lib: ctypes.CDLL) -> None:
         "qjl_sketch_export": (c.c_int, [vp, vp, vp]),
         "qjl_generate_sketch_host": (c.c_int, [u64, i32, i32, i32, vp, vp, vp, vp, vp]),
         "qjl_quantize_keys": (c.c_int, [vp, vp, i32, i64, i64, vp, vp, vp]),
+        "qjl_quantize_keys_into": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp]),
         "qjl_project_query": (c.c_int, [vp, vp, i32, i64, vp, vp]),
         "qjl_score": (c.c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp]),
         "qjl_decode_attention_workspace_size": (c.c_int, [vp, i64, i64, i64, i32,
@@ -227,6 +228,32 @@ def quantize_keys(sk: Sketch, K, key_index_base: int = 0, norms_out=None, bits_o
                                     _ptr(norms_out), _ptr(bits_out), _stream(stream)),
            "qjl_quantize_keys")
     return norms_out, bits_out
+
+
+def quantize_keys_into(sk: Sketch, K, n_groups: int, norms_cache, bits_cache,
+                       cache_rows_per_group: int, first_row: int, key_index_base: int = 0,
+                       stream=None):
+    """Quantize K [n_groups * keys_per_group, d] into a key cache laid out by
+    group: key i of group g goes to row g * cache_rows_per_group + first_row + i
+    of norms_cache [n_groups * cache_rows_per_group] (float32) and bits_cache
+    [n_groups * cache_rows_per_group, m/32] (int32 words).  Returns the cache."""
+    _dev_tensor(K, "K", 2)
+    if K.shape[1] != sk.d:
+        raise ValueError(f"K has {K.shape[1]} columns, sketch d = {sk.d}")
+    if n_groups <= 0 or K.shape[0] % n_groups != 0:
+        raise ValueError("K's rows must split evenly into n_groups groups")
+    kpg = K.shape[0] // n_groups
+    _dev_tensor(norms_cache, "norms_cache")
+    _dev_tensor(bits_cache, "bits_cache")
+    rows = n_groups * int(cache_rows_per_group)
+    if norms_cache.numel() < rows or bits_cache.numel() < rows * (sk.m // 32):
+        raise ValueError("cache buffers smaller than n_groups * cache_rows_per_group rows")
+    _check(load().qjl_quantize_keys_into(sk.handle, _ptr(K), _dtype_code(K), int(n_groups), kpg,
+                                         int(cache_rows_per_group), int(first_row),
+                                         int(key_index_base), _ptr(norms_cache),
+                                         _ptr(bits_cache), _stream(stream)),
+           "qjl_quantize_keys_into")
+    return norms_cache, bits_cache
 
 
 def project_query(sk: Sketch, q, Sq_out=None, stream=None):

@@ -1,4 +1,5 @@
 // extern "C" entry points of libqjl: validation, sketch lifetime, dispatch.
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -219,6 +220,25 @@ qjl_status qjl_sketch_export(const qjl_sketch *sk, float *S_f32, uint16_t *S_bf1
   return QJL_OK;
 }
 
+namespace {
+
+// Shared by qjl_quantize_keys and qjl_quantize_keys_into, after their own
+// argument checks: the device check and the kernel dispatch.
+qjl_status quantize_dispatch(const qjl_sketch *sk, const void *K, int32_t dtype, int64_t n,
+                             int64_t key_index_base, const RowMap &map, float *norms,
+                             uint32_t *bits, void *stream) {
+  qjl_status st = check_device(sk);
+  if (st != QJL_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sk->host.variant != QJL_VARIANT_DENSE)
+    return from_hip(launch_fqjl(sk, K, dtype, n, key_index_base, map, norms, bits, nullptr, s));
+  if (quantize_mfma_supported(sk, K, dtype, bits))
+    return from_hip(launch_quantize_mfma(sk, K, n, map, norms, bits, s));
+  return from_hip(launch_quantize_generic(sk, K, dtype, n, key_index_base, map, norms, bits, s));
+}
+
+}  // namespace
+
 qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype, int64_t n_keys,
                              int64_t key_index_base, float *norms_out, uint32_t *bits_out,
                              void *stream) {
@@ -229,16 +249,37 @@ qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype,
   const uintptr_t esz = dtype == QJL_DTYPE_F32 ? 4 : 2;
   if (!aligned(K, esz) || !aligned(norms_out, 4) || !aligned(bits_out, 4))
     return QJL_ERR_INVALID_ARGUMENT;
-  qjl_status st = check_device(sk);
-  if (st != QJL_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sk->host.variant != QJL_VARIANT_DENSE)
-    return from_hip(launch_fqjl(sk, K, dtype, n_keys, key_index_base, norms_out, bits_out,
-                                nullptr, s));
-  if (quantize_mfma_supported(sk, K, dtype, bits_out))
-    return from_hip(launch_quantize_mfma(sk, K, n_keys, norms_out, bits_out, s));
-  return from_hip(launch_quantize_generic(sk, K, dtype, n_keys, key_index_base, norms_out,
-                                          bits_out, s));
+  return quantize_dispatch(sk, K, dtype, n_keys, key_index_base, RowMap{}, norms_out, bits_out,
+                           stream);
+}
+
+qjl_status qjl_quantize_keys_into(const qjl_sketch *sk, const void *K, int32_t dtype,
+                                  int64_t n_groups, int64_t keys_per_group,
+                                  int64_t cache_rows_per_group, int64_t first_row,
+                                  int64_t key_index_base, float *norms_cache,
+                                  uint32_t *bits_cache, void *stream) {
+  if (!sk || n_groups < 0 || keys_per_group < 0 || cache_rows_per_group < 0 || first_row < 0 ||
+      key_index_base < 0)
+    return QJL_ERR_INVALID_ARGUMENT;
+  if (dtype != QJL_DTYPE_F32 && dtype != QJL_DTYPE_BF16) return QJL_ERR_INVALID_ARGUMENT;
+  // the new rows must lie inside each group's slice of the cache
+  if (first_row > cache_rows_per_group || keys_per_group > cache_rows_per_group - first_row)
+    return QJL_ERR_INVALID_ARGUMENT;
+  if (n_groups == 0 || keys_per_group == 0) return QJL_OK;
+  const int64_t big = INT64_MAX / 2;
+  if (n_groups > big / keys_per_group || n_groups > big / cache_rows_per_group)
+    return QJL_ERR_INVALID_ARGUMENT;  // key or cache row counts overflow
+  const int64_t n = n_groups * keys_per_group;
+  if (n >= ((int64_t)1 << 32)) return QJL_ERR_UNSUPPORTED;  // rows are mapped in 32 bits
+  if (!K || !norms_cache || !bits_cache) return QJL_ERR_INVALID_ARGUMENT;
+  const uintptr_t esz = dtype == QJL_DTYPE_F32 ? 4 : 2;
+  if (!aligned(K, esz) || !aligned(norms_cache, 4) || !aligned(bits_cache, 4))
+    return QJL_ERR_INVALID_ARGUMENT;
+  RowMap map;
+  map.per_group = keys_per_group;
+  map.stride = cache_rows_per_group;
+  map.first = first_row;
+  return quantize_dispatch(sk, K, dtype, n, key_index_base, map, norms_cache, bits_cache, stream);
 }
 
 qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
@@ -253,7 +294,7 @@ qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
   if (st != QJL_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (sk->host.variant != QJL_VARIANT_DENSE)
-    return from_hip(launch_fqjl(sk, q, dtype, n_queries, 0, nullptr, nullptr, Sq_out, s));
+    return from_hip(launch_fqjl(sk, q, dtype, n_queries, 0, RowMap{}, nullptr, nullptr, Sq_out, s));
   if (project_mfma_supported(sk, q, dtype, n_queries, Sq_out))
     return from_hip(launch_project_mfma(sk, q, n_queries, Sq_out, s));
   return from_hip(launch_project_dense(sk, q, dtype, n_queries, Sq_out, s));

@@ -71,11 +71,11 @@ __device__ __forceinline__ uint32_t pack_nonneg(const float *u) {
 
 // PERM = false: the block has no permutation (D-FQJL), so the transformed
 // row is scaled by G in place and the LDS round trip is skipped.
-template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
+template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM, bool MAPPED>
 __global__ __launch_bounds__(64) void fqjl_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   __shared__ float lds[D * 64];
   const int lane = threadIdx.x;
@@ -84,6 +84,7 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
   for (int64_t r0 = (int64_t)blockIdx.x * 64; r0 < n; r0 += (int64_t)gridDim.x * 64) {
     const int64_t row = r0 + lane;
     const bool valid = row < n;
+    const int64_t orow = MAPPED ? map_row(map, valid ? row : 0) : (valid ? row : 0);  // output row
     const T *xr = X + (valid ? row : 0) * (int64_t)D;
     float x[HOLD ? D : 1];
     float nrm = 0.f;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
         s = fmaf(v, v, s);
       }
       nrm = sqrtf(s);
-      if (valid) norms[row] = nrm;
+      if (valid) norms[orow] = nrm;
     }
     for (int b = 0; b < nb; ++b) {
       float u[D];
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
       } else {
         if (DITHER) {
           const float amp = rho * nrm;
-          const uint64_t pair0 = (uint64_t)(base + (valid ? row : 0)) * (uint64_t)(m / 2) +
+          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) +
                                  (uint64_t)(b * D / 2);
 #pragma unroll
           for (int c = 0; c < D; c += 2) {
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
           }
         }
         if (valid) {
-          uint32_t *br = bits + row * (int64_t)W + b * (D / 32);
+          uint32_t *br = bits + orow * (int64_t)W + b * (D / 32);
 #pragma unroll
           for (int w = 0; w < D / 32; ++w) br[w] = pack_nonneg(&u[32 * w]);
         }
@@ -166,11 +167,11 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
 // Without a permutation (PERM = false, D-FQJL) each lane needs coordinate c
 // of both halves, which v_permlane32_swap exchanges between lanes k and
 // k + 32 in registers: no LDS at all.
-template <typename T, bool PROJECT, bool DITHER, bool PERM>
+template <typename T, bool PROJECT, bool DITHER, bool PERM, bool MAPPED>
 __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   constexpr int D = 128, H = 64;
   __shared__ float lds[D * 32];
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
   for (int64_t r0 = (int64_t)blockIdx.x * 32; r0 < n; r0 += (int64_t)gridDim.x * 32) {
     const int64_t row = r0 + k;
     const bool valid = row < n;
+    const int64_t orow = MAPPED ? map_row(map, valid ? row : 0) : (valid ? row : 0);  // output row
     const T *xr = X + (valid ? row : 0) * (int64_t)D;
     // The row stays in registers as loaded (bf16 pairs or float words) and is
     // widened where it is used: half the registers of a float copy for bf16.
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
         }
       }
       nrm = sqrtf(ssq + __shfl_xor(ssq, 32));
-      if (valid && sh == 0 && blockIdx.y == 0) norms[row] = nrm;
+      if (valid && sh == 0 && blockIdx.y == 0) norms[orow] = nrm;
     }
     // blocks b = blockIdx.y, blockIdx.y + gridDim.y, ...: a short call (few
     // rows, e.g. one new key per head) spreads its blocks over workgroups
@@ -281,8 +283,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
       } else {
         if (DITHER) {
           const float amp = rho * nrm;
-          const uint64_t pair0 =
-              (uint64_t)(base + (valid ? row : 0)) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
+          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
 #pragma unroll
           for (int c = 0; c < H; c += 2) {
             float xc, xs;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
           }
         }
         if (valid) {
-          uint32_t *br = bits + row * (int64_t)W + j0 / 32;
+          uint32_t *br = bits + orow * (int64_t)W + j0 / 32;
 #pragma unroll
           for (int w = 0; w < H / 32; ++w) br[w] = pack_nonneg(&t[32 * w]);
         }
@@ -305,17 +306,18 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
 // consecutive blocks share words.  These small sizes exist so the GPU chain
 // can be checked against explicit matrices; they run a plain per-lane loop
 // that writes whole words after all blocks of a word are done.
-template <int D, typename T, bool PROJECT, bool DITHER>
+template <int D, typename T, bool PROJECT, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(64) void fqjl_small_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   const int lane = threadIdx.x;
   const int W = m / 32;
   for (int64_t r0 = (int64_t)blockIdx.x * 64; r0 < n; r0 += (int64_t)gridDim.x * 64) {
     const int64_t row = r0 + lane;
     if (row >= n) continue;
+    const int64_t orow = MAPPED ? map_row(map, row) : row;  // output row
     float x[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) x[c] = load_as_f32(X + row * (int64_t)D, c);
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(64) void fqjl_small_kernel(
 #pragma unroll
     for (int c = 0; c < D; ++c) s = fmaf(x[c], x[c], s);
     const float nrm = sqrtf(s);
-    if (!PROJECT) norms[row] = nrm;
+    if (!PROJECT) norms[orow] = nrm;
     uint32_t word = 0;
     for (int b = 0; b < nb; ++b) {
       float u[D], v[D];
@@ -346,10 +348,10 @@ __global__ __launch_bounds__(64) void fqjl_small_kernel(
           Y[row * (int64_t)m + j] = y;
           continue;
         }
-        if (DITHER) y += (rho * nrm) * dither_one(dkey, (uint64_t)(base + row), m, j);
+        if (DITHER) y += (rho * nrm) * dither_one(dkey, (uint64_t)(base + orow), m, j);
         word |= (y >= 0.f ? 1u : 0u) << (j & 31);
         if ((j & 31) == 31) {
-          bits[row * (int64_t)W + (j >> 5)] = word;
+          bits[orow * (int64_t)W + (j >> 5)] = word;
           word = 0;
         }
       }
@@ -357,11 +359,76 @@ __global__ __launch_bounds__(64) void fqjl_small_kernel(
   }
 }
 
+// Launch helpers: the boolean template arguments are chosen at run time.
+struct FqjlArgs {
+  int nb, m;
+  const uint32_t *Dsign;
+  const int32_t *P;
+  const float *Gs;
+  int64_t n, base;
+  RowMap map;
+  float rho;
+  uint64_t dkey;
+  float *norms;
+  uint32_t *bits;
+  float *Y;
+};
+
+template <typename T, bool PROJECT, bool DITHER, bool PERM>
+void launch_fqjl128(const T *X, const FqjlArgs &a, dim3 grid, hipStream_t st) {
+  if (!PROJECT && a.map.per_group != 0)
+    hipLaunchKernelGGL((fqjl128_kernel<T, PROJECT, DITHER, PERM, true>), grid, dim3(64), 0, st,
+                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+  else
+    hipLaunchKernelGGL((fqjl128_kernel<T, PROJECT, DITHER, PERM, false>), grid, dim3(64), 0, st,
+                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+}
+
+template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
+void launch_fqjl_row(const T *X, const FqjlArgs &a, int grid, hipStream_t st) {
+  if (!PROJECT && a.map.per_group != 0)
+    hipLaunchKernelGGL((fqjl_kernel<D, T, PROJECT, DITHER, VEC, PERM, true>), dim3(grid),
+                       dim3(64), 0, st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map,
+                       a.rho, a.dkey, a.norms, a.bits, a.Y);
+  else
+    hipLaunchKernelGGL((fqjl_kernel<D, T, PROJECT, DITHER, VEC, PERM, false>), dim3(grid),
+                       dim3(64), 0, st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map,
+                       a.rho, a.dkey, a.norms, a.bits, a.Y);
+}
+
+template <int D, typename T, bool PROJECT, bool DITHER>
+void launch_fqjl_small(const T *X, const FqjlArgs &a, int grid, hipStream_t st) {
+  if (!PROJECT && a.map.per_group != 0)
+    hipLaunchKernelGGL((fqjl_small_kernel<D, T, PROJECT, DITHER, true>), dim3(grid), dim3(64), 0,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+  else
+    hipLaunchKernelGGL((fqjl_small_kernel<D, T, PROJECT, DITHER, false>), dim3(grid), dim3(64), 0,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+}
+
+// The PROJECT / DITHER / PERM combinations that occur: a projection never
+// dithers, and a D-FQJL sketch (no permutation) always dithers its keys.
+template <int D, typename T, bool VEC>
+void launch_fqjl_rows(const T *X, const FqjlArgs &a, bool proj, bool dith, bool perm, int grid,
+                      hipStream_t st) {
+  if (!perm && proj) launch_fqjl_row<D, T, true, false, VEC, false>(X, a, grid, st);
+  else if (!perm && dith) launch_fqjl_row<D, T, false, true, VEC, false>(X, a, grid, st);
+  else if (proj) launch_fqjl_row<D, T, true, false, VEC, true>(X, a, grid, st);
+  else if (dith) launch_fqjl_row<D, T, false, true, VEC, true>(X, a, grid, st);
+  else launch_fqjl_row<D, T, false, false, VEC, true>(X, a, grid, st);
+}
+
 template <int D, typename T>
 hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t base,
-                         float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+                         const RowMap &map, float *norms, uint32_t *bits, float *Y,
+                         hipStream_t st) {
   const HostSketch &h = sk->host;
-  const int nb = h.m / D;
+  const FqjlArgs a{h.m / D, h.m, sk->Dsign, sk->P, sk->Gs, n, base, map, h.rho,
+                   sk->dither_key, norms, bits, Y};
   const int64_t tiles = (n + 63) / 64;
   const int grid = (int)(tiles < 16384 ? tiles : 16384);
   const bool proj = Y != nullptr;
@@ -369,62 +436,44 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
   // D-FQJL blocks have no permutation (P_b = I): the kernels skip the gather.
   // Any other case (P-FQJL, the composition) gathers through LDS.
   const bool perm = h.variant != QJL_VARIANT_DFQJL;
-#define QJL_FQJL_LAUNCH(KERNEL, ...)                                                            \
-  hipLaunchKernelGGL((KERNEL<__VA_ARGS__>), dim3(grid), dim3(64), 0, st, X, nb, h.m, sk->Dsign,  \
-                     sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
   if constexpr (D == 128) {
     if (((uintptr_t)X & 15) == 0) {  // rows are whole 16-byte vectors
       const int64_t tiles2 = (n + 31) / 32;
       const int grid2 = (int)(tiles2 < 32768 ? tiles2 : 32768);
       // Few rows: one workgroup per (row tile, block) so the blocks run side
       // by side (a row is then loaded once per block instead of once).
-      const int gy = tiles2 * nb <= 4096 ? nb : 1;
-#define QJL_FQJL128_LAUNCH(...)                                                                  \
-  hipLaunchKernelGGL((fqjl128_kernel<__VA_ARGS__>), dim3(grid2, gy), dim3(64), 0, st, X, nb,     \
-                     h.m, sk->Dsign, sk->P, sk->Gs, n, base, h.rho, sk->dither_key, norms, bits, Y)
-      if (!perm && proj) QJL_FQJL128_LAUNCH(T, true, false, false);
-      else if (!perm && dith) QJL_FQJL128_LAUNCH(T, false, true, false);
-      else if (proj) QJL_FQJL128_LAUNCH(T, true, false, true);
-      else if (dith) QJL_FQJL128_LAUNCH(T, false, true, true);
-      else QJL_FQJL128_LAUNCH(T, false, false, true);
-#undef QJL_FQJL128_LAUNCH
+      const dim3 g2(grid2, tiles2 * a.nb <= 4096 ? a.nb : 1);
+      if (!perm && proj) launch_fqjl128<T, true, false, false>(X, a, g2, st);
+      else if (!perm && dith) launch_fqjl128<T, false, true, false>(X, a, g2, st);
+      else if (proj) launch_fqjl128<T, true, false, true>(X, a, g2, st);
+      else if (dith) launch_fqjl128<T, false, true, true>(X, a, g2, st);
+      else launch_fqjl128<T, false, false, true>(X, a, g2, st);
       return hipGetLastError();
     }
   }
   if constexpr (D >= 32) {
-    const bool vec = ((uintptr_t)X & 15) == 0;  // rows are whole 16-byte vectors then
-    // (a D-FQJL sketch always dithers its keys: rho > 0)
-    if (vec) {
-      if (!perm && proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true, false);
-      else if (!perm && dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true, false);
-      else if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, true, true);
-      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, true, true);
-      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, true, true);
-    } else {
-      if (!perm && proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false, false);
-      else if (!perm && dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false, false);
-      else if (proj) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, true, false, false, true);
-      else if (dith) QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, true, false, true);
-      else QJL_FQJL_LAUNCH(fqjl_kernel, D, T, false, false, false, true);
-    }
+    if (((uintptr_t)X & 15) == 0)  // rows are whole 16-byte vectors
+      launch_fqjl_rows<D, T, true>(X, a, proj, dith, perm, grid, st);
+    else
+      launch_fqjl_rows<D, T, false>(X, a, proj, dith, perm, grid, st);
   } else {
-    if (proj) QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, true, false);
-    else if (dith) QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, false, true);
-    else QJL_FQJL_LAUNCH(fqjl_small_kernel, D, T, false, false);
+    if (proj) launch_fqjl_small<D, T, true, false>(X, a, grid, st);
+    else if (dith) launch_fqjl_small<D, T, false, true>(X, a, grid, st);
+    else launch_fqjl_small<D, T, false, false>(X, a, grid, st);
   }
-#undef QJL_FQJL_LAUNCH
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t base,
-                         float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+                         const RowMap &map, float *norms, uint32_t *bits, float *Y,
+                         hipStream_t st) {
   switch (sk->host.d) {
-    case 8: return launch_fqjl_t<8>(sk, X, n, base, norms, bits, Y, st);
-    case 16: return launch_fqjl_t<16>(sk, X, n, base, norms, bits, Y, st);
-    case 32: return launch_fqjl_t<32>(sk, X, n, base, norms, bits, Y, st);
-    case 64: return launch_fqjl_t<64>(sk, X, n, base, norms, bits, Y, st);
-    case 128: return launch_fqjl_t<128>(sk, X, n, base, norms, bits, Y, st);
+    case 8: return launch_fqjl_t<8>(sk, X, n, base, map, norms, bits, Y, st);
+    case 16: return launch_fqjl_t<16>(sk, X, n, base, map, norms, bits, Y, st);
+    case 32: return launch_fqjl_t<32>(sk, X, n, base, map, norms, bits, Y, st);
+    case 64: return launch_fqjl_t<64>(sk, X, n, base, map, norms, bits, Y, st);
+    case 128: return launch_fqjl_t<128>(sk, X, n, base, map, norms, bits, Y, st);
   }
   return hipErrorInvalidValue;
 }
@@ -432,10 +481,10 @@ hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
 }  // namespace
 
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
-                       float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+                       const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st) {
   if (dtype == QJL_DTYPE_F32)
-    return launch_fqjl_d(sk, static_cast<const float *>(X), n, base, norms, bits, Y, st);
-  return launch_fqjl_d(sk, static_cast<const uint16_t *>(X), n, base, norms, bits, Y, st);
+    return launch_fqjl_d(sk, static_cast<const float *>(X), n, base, map, norms, bits, Y, st);
+  return launch_fqjl_d(sk, static_cast<const uint16_t *>(X), n, base, map, norms, bits, Y, st);
 }
 
 }  // namespace qjl

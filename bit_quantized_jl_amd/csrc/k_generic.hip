@@ -17,10 +17,11 @@ namespace {
 constexpr int GEN_THREADS = 256;
 constexpr int GEN_KEYS = 16;  // rows per block tile
 
-template <typename T, bool DITHER>
+template <typename T, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
     const T *__restrict__ X, const float *__restrict__ S, int d, int m, int64_t n, int64_t base,
-    float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits) {
+    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits) {
+  auto out_row = [&](int64_t r) -> int64_t { return MAPPED ? map_row(map, r) : r; };
   extern __shared__ float smem[];
   float *sX = smem;                        // [GEN_KEYS][d]
   float *sNorm = smem + GEN_KEYS * d;      // [GEN_KEYS]
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
       for (int c = 0; c < d; ++c) s = fmaf(sX[tid * d + c], sX[tid * d + c], s);
       const float nrm = sqrtf(s);
       sNorm[tid] = nrm;
-      if (tid < nr) norms[r0 + tid] = nrm;
+      if (tid < nr) norms[out_row(r0 + tid)] = nrm;
     }
     __syncthreads();
     for (int jb = 0; jb < m; jb += GEN_THREADS) {
@@ -62,10 +63,11 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
 #pragma unroll
       for (int r = 0; r < GEN_KEYS; ++r) {
         float y = acc[r];
-        if (DITHER && valid) y += (rho * sNorm[r]) * dither_one(dkey, (uint64_t)(base + r0 + r), m, j);
+        if (DITHER && valid)
+          y += (rho * sNorm[r]) * dither_one(dkey, (uint64_t)(base + out_row(r0 + r)), m, j);
         const uint64_t msk = __ballot(valid && y >= 0.f);
         if (r < nr) {
-          uint32_t *brow = bits + (r0 + r) * (int64_t)W;
+          uint32_t *brow = bits + out_row(r0 + r) * (int64_t)W;
           if (lane == 0 && w0 < W) brow[w0] = (uint32_t)msk;
           if (lane == 32 && w0 + 1 < W) brow[w0 + 1] = (uint32_t)(msk >> 32);
         }
@@ -77,33 +79,38 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
 
 template <typename T, bool DITHER>
 hipError_t launch_generic_t(const T *X, const float *S, int d, int m, int64_t n, int64_t base,
-                            float rho, uint64_t dkey, float *norms, uint32_t *bits,
-                            hipStream_t st) {
+                            const RowMap &map, float rho, uint64_t dkey, float *norms,
+                            uint32_t *bits, hipStream_t st) {
   const int64_t tiles = (n + GEN_KEYS - 1) / GEN_KEYS;
   const int grid = (int)(tiles < 8192 ? tiles : 8192);
   const size_t shmem = (size_t)(GEN_KEYS * d + GEN_KEYS) * sizeof(float);
-  hipLaunchKernelGGL((dense_generic_kernel<T, DITHER>), dim3(grid), dim3(GEN_THREADS), shmem, st,
-                     X, S, d, m, n, base, rho, dkey, norms, bits);
+  if (map.per_group != 0)
+    hipLaunchKernelGGL((dense_generic_kernel<T, DITHER, true>), dim3(grid), dim3(GEN_THREADS),
+                       shmem, st, X, S, d, m, n, base, map, rho, dkey, norms, bits);
+  else
+    hipLaunchKernelGGL((dense_generic_kernel<T, DITHER, false>), dim3(grid), dim3(GEN_THREADS),
+                       shmem, st, X, S, d, m, n, base, map, rho, dkey, norms, bits);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtype, int64_t n,
-                                   int64_t base, float *norms, uint32_t *bits, hipStream_t st) {
+                                   int64_t base, const RowMap &map, float *norms, uint32_t *bits,
+                                   hipStream_t st) {
   const HostSketch &h = sk->host;
   const bool dith = h.rho > 0.f;
   if (dtype == QJL_DTYPE_F32) {
     const float *X = static_cast<const float *>(K);
-    return dith ? launch_generic_t<float, true>(X, sk->S32, h.d, h.m, n, base, h.rho,
+    return dith ? launch_generic_t<float, true>(X, sk->S32, h.d, h.m, n, base, map, h.rho,
                                                sk->dither_key, norms, bits, st)
-                : launch_generic_t<float, false>(X, sk->S32, h.d, h.m, n, base, h.rho,
+                : launch_generic_t<float, false>(X, sk->S32, h.d, h.m, n, base, map, h.rho,
                                                 sk->dither_key, norms, bits, st);
   }
   const uint16_t *X = static_cast<const uint16_t *>(K);
-  return dith ? launch_generic_t<uint16_t, true>(X, sk->S16f, h.d, h.m, n, base, h.rho,
+  return dith ? launch_generic_t<uint16_t, true>(X, sk->S16f, h.d, h.m, n, base, map, h.rho,
                                                 sk->dither_key, norms, bits, st)
-              : launch_generic_t<uint16_t, false>(X, sk->S16f, h.d, h.m, n, base, h.rho,
+              : launch_generic_t<uint16_t, false>(X, sk->S16f, h.d, h.m, n, base, map, h.rho,
                                                  sk->dither_key, norms, bits, st);
 }
 

@@ -118,10 +118,10 @@ __device__ __forceinline__ uint32_t pack_signs(uint32_t x, const floatx16_t &acc
 // scheduling barrier closes every MFMA step: without it the scheduler hoists
 // all MFMAs of the tile and runs out of registers.  Norms of column tiles
 // 2i and 2i + 1 leave in one 64-lane store (lane half h writes tile 2i + h).
-template <int D, int M, int RT, bool DEFER>
+template <int D, int M, int RT, bool DEFER, bool MAPPED>
 __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, const uint4 *sS,
                                              int64_t k0, int64_t n, int lane, int r, int h,
-                                             float *__restrict__ norms,
+                                             const RowMap &map, float *__restrict__ norms,
                                              uint32_t *__restrict__ bits) {
   constexpr int T = D / 16;
   constexpr int W = M / 32;
@@ -195,7 +195,9 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, cons
 #pragma unroll
       for (int i = 0; i < RT / 2; ++i) {
         const int64_t key = k0 + 32 * (2 * i + h) + r;
-        if (key < n) __builtin_nontemporal_store(h ? nrm[2 * i + 1] : nrm[2 * i], norms + key);
+        if (key < n)
+          __builtin_nontemporal_store(h ? nrm[2 * i + 1] : nrm[2 * i],
+                                      norms + (MAPPED ? map_row(map, key) : key));
       }
     }
     if (DEFER) {
@@ -231,15 +233,16 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, cons
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t key = k0 + 32 * rt + r;
     if (key < n) {
+      const int64_t row = MAPPED ? map_row(map, key) : key;
       if constexpr ((W / 2) % 4 == 0) {
-        u32x4_t *dst = reinterpret_cast<u32x4_t *>(bits + key * W + h * (W / 2));
+        u32x4_t *dst = reinterpret_cast<u32x4_t *>(bits + row * W + h * (W / 2));
 #pragma unroll
         for (int q = 0; q < W / 8; ++q)
           __builtin_nontemporal_store(
               u32x4_t{Wd[rt][4 * q], Wd[rt][4 * q + 1], Wd[rt][4 * q + 2], Wd[rt][4 * q + 3]},
               dst + q);
       } else {
-        u32x2_t *dst = reinterpret_cast<u32x2_t *>(bits + key * W + h * (W / 2));
+        u32x2_t *dst = reinterpret_cast<u32x2_t *>(bits + row * W + h * (W / 2));
 #pragma unroll
         for (int q = 0; q < W / 4; ++q)
           __builtin_nontemporal_store(u32x2_t{Wd[rt][2 * q], Wd[rt][2 * q + 1]}, dst + q);
@@ -251,9 +254,9 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, cons
 // Persistent kernel: each wave walks 64-key tiles with a stride of all waves
 // in the grid; the grid is sized to what is resident at once.  Two waves per
 // SIMD hide one another's HBM latency.
-template <int D, int M, int WAVES, int RT, bool DEFER>
+template <int D, int M, int WAVES, int RT, bool DEFER, bool MAPPED>
 __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
-    const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int64_t n,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int64_t n, RowMap map,
     float *__restrict__ norms, uint32_t *__restrict__ bits) {
   static_assert(M % 128 == 0, "each lane stores whole 8-byte groups of words");
   __shared__ uint4 sS[M * D / 8];
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
   for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
     KeyTile<D / 16, RT> kt;
     load_tile<D, RT>(kt, K, tile * KEYS, n, r, h);
-    process_tile<D, M, RT, DEFER>(kt, sS, tile * KEYS, n, lane, r, h, norms, bits);
+    process_tile<D, M, RT, DEFER, MAPPED>(kt, sS, tile * KEYS, n, lane, r, h, map, norms, bits);
   }
 }
 
@@ -280,21 +283,35 @@ __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
 // 4-wave workgroups share a CU, each with its own copy of S, and packing is
 // deferred; at m = 512 S takes 128 KB of LDS, so one 8-wave workgroup per CU
 // packs each pass as it ends to stay within two waves' registers per SIMD.
-template <int D, int M>
-hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, float *norms,
-                     uint32_t *bits, hipStream_t st) {
+template <int D, int M, bool MAPPED>
+hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
+                     float *norms, uint32_t *bits, hipStream_t st) {
   // Two column tiles per wave: four (halving the LDS reads of S) measured
   // slower, with no room left to defer the packing.
   constexpr int RT = 2;
   constexpr int WAVES = M <= 256 ? 4 : 8;
   constexpr bool DEFER = M <= 256;
-  auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER>;
+  auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER, MAPPED>;
   static const int resident = resident_workgroups(kern, 64 * WAVES);  // on the whole device
   const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)(want < resident ? want : resident);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->S16mfma, n, norms, bits);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->S16mfma, n, map, norms,
+                     bits);
   return hipGetLastError();
+}
+
+template <bool MAPPED>
+hipError_t launch_qm_dm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
+                        float *norms, uint32_t *bits, hipStream_t st) {
+  const int d = sk->host.d, m = sk->host.m;
+  if (d == 128 && m == 128) return launch_qm<128, 128, MAPPED>(sk, K, n, map, norms, bits, st);
+  if (d == 128 && m == 256) return launch_qm<128, 256, MAPPED>(sk, K, n, map, norms, bits, st);
+  if (d == 128 && m == 512) return launch_qm<128, 512, MAPPED>(sk, K, n, map, norms, bits, st);
+  if (d == 64 && m == 128) return launch_qm<64, 128, MAPPED>(sk, K, n, map, norms, bits, st);
+  if (d == 64 && m == 256) return launch_qm<64, 256, MAPPED>(sk, K, n, map, norms, bits, st);
+  if (d == 64 && m == 512) return launch_qm<64, 512, MAPPED>(sk, K, n, map, norms, bits, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -309,17 +326,11 @@ bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
   return false;
 }
 
-hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *Kv, int64_t n, float *norms,
-                                uint32_t *bits, hipStream_t st) {
+hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *Kv, int64_t n, const RowMap &map,
+                                float *norms, uint32_t *bits, hipStream_t st) {
   const uint16_t *K = static_cast<const uint16_t *>(Kv);
-  const int d = sk->host.d, m = sk->host.m;
-  if (d == 128 && m == 128) return launch_qm<128, 128>(sk, K, n, norms, bits, st);
-  if (d == 128 && m == 256) return launch_qm<128, 256>(sk, K, n, norms, bits, st);
-  if (d == 128 && m == 512) return launch_qm<128, 512>(sk, K, n, norms, bits, st);
-  if (d == 64 && m == 128) return launch_qm<64, 128>(sk, K, n, norms, bits, st);
-  if (d == 64 && m == 256) return launch_qm<64, 256>(sk, K, n, norms, bits, st);
-  if (d == 64 && m == 512) return launch_qm<64, 512>(sk, K, n, norms, bits, st);
-  return hipErrorInvalidValue;
+  if (map.per_group != 0) return launch_qm_dm<true>(sk, K, n, map, norms, bits, st);
+  return launch_qm_dm<false>(sk, K, n, map, norms, bits, st);
 }
 
 }  // namespace qjl

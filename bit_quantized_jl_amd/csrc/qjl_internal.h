@@ -31,6 +31,20 @@ __host__ __device__ inline uint64_t stream_draw(uint64_t key, uint64_t i) {
 
 enum : int { STREAM_DENSE = 0, STREAM_D = 1, STREAM_P = 2, STREAM_G = 3, STREAM_DITHER = 4 };
 
+// Output row of quantized key r in a cache laid out by group: key r is key
+// r % per_group of group r / per_group and goes to row
+// (r / per_group) * stride + first + r % per_group; its dither counter is
+// key_index_base plus that row.  per_group == 0 is the identity (row r).
+// The division is 32-bit: callers keep r below 2^32.
+struct RowMap {
+  int64_t per_group = 0, stride = 0, first = 0;
+};
+__host__ __device__ inline int64_t map_row(const RowMap &mp, int64_t r) {
+  if (mp.per_group == 1) return r * mp.stride + mp.first;
+  const uint32_t g = (uint32_t)r / (uint32_t)mp.per_group;
+  return (int64_t)g * mp.stride + mp.first + (r - (int64_t)g * mp.per_group);
+}
+
 // Host-side random parameters of one sketch (no device state).
 struct HostSketch {
   uint64_t seed = 0;
@@ -74,7 +88,8 @@ namespace qjl {
 
 // Kernel launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtype, int64_t n,
-                                   int64_t base, float *norms, uint32_t *bits, hipStream_t st);
+                                   int64_t base, const RowMap &map, float *norms, uint32_t *bits,
+                                   hipStream_t st);
 hipError_t launch_project_dense(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
                                 float *Sq, hipStream_t st);
 bool project_mfma_supported(const qjl_sketch *sk, const void *q, int dtype, int64_t n,
@@ -83,10 +98,10 @@ hipError_t launch_project_mfma(const qjl_sketch *sk, const void *q, int64_t n, f
                                hipStream_t st);
 bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
                              const uint32_t *bits);
-hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, float *norms,
-                                uint32_t *bits, hipStream_t st);
+hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, const RowMap &map,
+                                float *norms, uint32_t *bits, hipStream_t st);
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
-                       float *norms, uint32_t *bits, float *Y, hipStream_t st);
+                       const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st);
 hipError_t launch_score_generic(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
                                 const float *norms, int64_t G, int64_t nq, int64_t nk,
                                 float *scores, hipStream_t st);

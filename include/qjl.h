@@ -163,6 +163,31 @@ qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype,
                              void *stream);
 
 /*
+ * Quantize new keys straight into a key cache laid out by group (the
+ * decode-time append: the QJL abstract's cache of sign bits and norms grows
+ * by one key per head and token).  K: device [n_groups * keys_per_group][d]
+ * in `dtype`, the keys of group g in rows [g * keys_per_group,
+ * (g + 1) * keys_per_group).  Key i of group g is quantized exactly as by
+ * qjl_quantize_keys and written to cache row
+ *     g * cache_rows_per_group + first_row + i
+ * of norms_cache (device float[n_groups * cache_rows_per_group]) and
+ * bits_cache (device uint32[n_groups * cache_rows_per_group][m/32]); no
+ * other row is touched.  The dither counter of a key is key_index_base plus
+ * its cache row, so a cache filled by appends holds the same bits as one
+ * qjl_quantize_keys call over the whole cache with the same key_index_base.
+ * Errors: NULL pointers (with keys to write), negative counts or indices,
+ * first_row + keys_per_group > cache_rows_per_group, overflowing row counts,
+ * bad dtype, misalignment, sketch of another device -> INVALID_ARGUMENT;
+ * n_groups * keys_per_group >= 2^32 -> UNSUPPORTED; launch failure -> DEVICE.
+ * n_groups == 0 or keys_per_group == 0 is a no-op.
+ */
+qjl_status qjl_quantize_keys_into(const qjl_sketch *sk, const void *K, int32_t dtype,
+                                  int64_t n_groups, int64_t keys_per_group,
+                                  int64_t cache_rows_per_group, int64_t first_row,
+                                  int64_t key_index_base, float *norms_cache,
+                                  uint32_t *bits_cache, void *stream);
+
+/*
  * Project n_queries queries: Sq_out[i] = S q_i in float32, not quantized (the
  * "standard JL transform without quantization" of the QJL abstract; no
  * dither).  q: device [n_queries][d] in `dtype`; Sq_out: device

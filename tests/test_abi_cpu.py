@@ -87,6 +87,7 @@ def test_null_handles_rejected():
     assert lib.qjl_sketch_info(None, None, None, None, None, None, None) == 1
     assert lib.qjl_sketch_export(None, None, None) == 1
     assert lib.qjl_quantize_keys(None, None, 1, 4, 0, None, None, None) == 1
+    assert lib.qjl_quantize_keys_into(None, None, 1, 2, 1, 8, 7, 0, None, None, None) == 1
     assert lib.qjl_project_query(None, None, 1, 4, None, None) == 1
     assert lib.qjl_score(None, None, None, None, 1, 1, 1, None, None) == 1
     sz = ctypes.c_size_t(7)

@@ -112,6 +112,93 @@ def test_project_query(variant, d, m, dt, nq):
     sk.close()
 
 
+SENTINEL_BITS = 0x5A5A5A5A
+SENTINEL_NORM = -7.0
+
+
+@pytest.mark.parametrize("variant,d,m,dt,rho,G,kpg,cap,first", [
+    ("dense", 128, 256, "bf16", 0.0, 37, 1, 300, 299),    # decode append, matrix cores
+    ("dense", 128, 256, "bf16", 0.0, 5, 70, 200, 17),     # prefill into spare capacity
+    ("dense", 128, 512, "bf16", 0.0, 3, 129, 129, 0),     # whole groups
+    ("dense", 128, 256, "f32", 0.0, 9, 3, 11, 8),         # float32 keys (generic kernel)
+    ("dense", 96, 64, "bf16", 0.3, 4, 33, 40, 5),         # dithered dense (generic kernel)
+    ("fqjl", 128, 256, "bf16", 0.0, 64, 1, 50, 13),       # two lanes per row
+    ("fqjl", 128, 256, "bf16", 0.1, 6, 45, 64, 19),       # with dither
+    ("dfqjl", 128, 256, "bf16", 0.1, 7, 2, 9, 7),
+    ("fqjl", 64, 192, "f32", 0.2, 5, 17, 17, 0),          # one row per lane
+    ("fqjl", 16, 64, "f32", 0.0, 3, 5, 12, 2)])           # narrow blocks
+def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
+    # Rows g * cap + first + i get key i of group g, quantized as the oracle
+    # does with dither counter base + that row; every other row keeps its
+    # sentinel.
+    note("quantize into cache", variant, d, m, dt, rho, G, kpg, cap, first)
+    base = 1234
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    gen = torch.Generator().manual_seed(G * 7 + kpg + cap + first)
+    K = (torch.randn(G * kpg, d, generator=gen) * 2).to(tdt)
+    sk = qj.make_sketch(4, d, m, variant, rho)
+    W = m // 32
+    norms = torch.full((G * cap,), SENTINEL_NORM, dtype=torch.float32, device=DEV)
+    bits = torch.full((G * cap, W), SENTINEL_BITS, dtype=torch.int32, device=DEV)
+    qj.quantize_keys_into(sk, K.to(DEV), G, norms, bits, cap, first, key_index_base=base)
+    torch.cuda.synchronize()
+    rows = (np.arange(G)[:, None] * cap + first + np.arange(kpg)[None, :]).reshape(-1)
+    ref = oracle_sketch(4, d, m, variant, rho)
+    rb, rn, mg, _ = oq.quantize(ref, to_np_f64(K), dt, key_index=base + rows)
+    got_b, got_n = bits_np(bits), to_np_f64(norms)
+    check_bits(got_b[rows], rb, mg, m)
+    check_norms(got_n[rows], rn)
+    untouched = np.ones(G * cap, dtype=bool)
+    untouched[rows] = False
+    assert np.all(got_b[untouched] == np.uint32(SENTINEL_BITS))
+    assert np.all(got_n[untouched] == SENTINEL_NORM)
+    sk.close()
+
+
+@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("fqjl", 0.1)])
+def test_cache_built_by_appends_equals_whole(variant, rho):
+    # Appending one key per group per step, then a block of four, fills the
+    # cache exactly as one call over the whole cache (same kernels per key,
+    # dither counters given by the cache row).
+    note("appends vs whole", variant, rho)
+    d, m, G, T = 128, 256, 24, 9
+    gen = torch.Generator().manual_seed(5)
+    cache_keys = (torch.randn(G, T, d, generator=gen) * 1.5).to(torch.bfloat16).to(DEV)
+    sk = qj.make_sketch(2, d, m, variant, rho)
+    whole_n, whole_b = qj.quantize_keys(sk, cache_keys.reshape(G * T, d), key_index_base=77)
+    norms = torch.full((G * T,), SENTINEL_NORM, dtype=torch.float32, device=DEV)
+    bits = torch.full((G * T, m // 32), SENTINEL_BITS, dtype=torch.int32, device=DEV)
+    for t in range(T - 4):
+        qj.quantize_keys_into(sk, cache_keys[:, t].contiguous(), G, norms, bits, T, t,
+                              key_index_base=77)
+    qj.quantize_keys_into(sk, cache_keys[:, T - 4:].reshape(G * 4, d).contiguous(), G, norms, bits,
+                          T, T - 4, key_index_base=77)
+    torch.cuda.synchronize()
+    assert torch.equal(bits, whole_b)
+    assert torch.equal(norms, whole_n)
+    sk.close()
+
+
+def test_quantize_into_cache_errors():
+    note("quantize into cache errors")
+    sk = qj.make_sketch(0, 128, 256, "dense", 0.0)
+    lib = qj.load()
+    K = torch.randn(4, 128, device=DEV).to(torch.bfloat16)
+    nb = torch.empty(64, device=DEV)
+    bb = torch.empty((64, 8), dtype=torch.int32, device=DEV)
+    call = lambda G, kpg, cap, first, base=0: lib.qjl_quantize_keys_into(
+        sk.handle, K.data_ptr(), 1, G, kpg, cap, first, base, nb.data_ptr(), bb.data_ptr(), None)
+    assert call(2, 2, 8, 7) == qj.ERR_INVALID_ARGUMENT      # rows past the group's slice
+    assert call(2, 2, 8, -1) == qj.ERR_INVALID_ARGUMENT     # negative first row
+    assert call(-1, 2, 8, 0) == qj.ERR_INVALID_ARGUMENT
+    assert call(2, 2, 8, 0, -5) == qj.ERR_INVALID_ARGUMENT  # negative dither base
+    assert call(1 << 20, 1 << 13, 1 << 13, 0) == qj.ERR_UNSUPPORTED  # 2^33 keys
+    assert call(0, 2, 8, 0) == qj.OK and call(2, 0, 8, 8) == qj.OK  # nothing to write
+    assert lib.qjl_quantize_keys_into(sk.handle, None, 1, 2, 2, 8, 0, 0, None, None, None) == \
+        qj.ERR_INVALID_ARGUMENT
+    sk.close()
+
+
 @pytest.mark.parametrize("d,m", [(128, 256), (64, 512), (128, 128)])
 def test_projected_keys_reproduce_their_bits(d, m):
     # Projecting bf16 keys as queries applies the same S as quantizing them
