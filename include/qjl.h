@@ -154,6 +154,8 @@ qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t
  * same bits as one quantized whole.
  * K: device, [n_keys][d] in `dtype`, aligned to its element size.
  * norms_out: device float[n_keys]; bits_out: device uint32[n_keys][m/32].
+ * Keys are expected finite: the bits and norm of a row holding NaN or
+ * infinity are unspecified (no error is raised).
  * Errors: NULL pointers (n_keys > 0), n_keys < 0, key_index_base < 0, bad
  * dtype, misalignment, sketch of another device -> INVALID_ARGUMENT;
  * launch failure -> DEVICE.

@@ -74,6 +74,7 @@ SHAPES = (
     [("dense", d, m, dt, 0.0) for d in (16, 64, 100, 128, 256) for m in (32, 96, 512)
      for dt in ("f32", "bf16")]
     + [("dense", 128, 256, "bf16", 0.5), ("dense", 64, 128, "f32", 0.1)]
+    + [("dense", d, m, "bf16", 0.0) for (d, m) in ((64, 128), (64, 256), (128, 128))]  # MFMA
     + [("fqjl", d, m, dt, rho) for (d, m) in ((8, 32), (16, 32), (16, 64), (32, 32), (32, 96),
                                               (64, 64), (64, 256), (128, 128), (128, 512))
        for dt in ("f32", "bf16") for rho in (0.0, 0.3)]
