@@ -9,6 +9,8 @@
 
 namespace qjl {
 void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out);
+bool fqjl_mfma_image_shape(int d, int m);
+void build_fqjl_mfma_image(const HostSketch &hs, uint16_t *out);
 }
 
 using namespace qjl;
@@ -131,8 +133,11 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
       off_a = 0;                                  // Dsign u32[nbd]
       off_b = round_up(off_a + nbd * 4, 256);     // P     i32[nbd]
       off_c = round_up(off_b + nbd * 4, 256);     // Gs    f32[nbd]
-      total = round_up(off_c + nbd * 4, 256);
+      off_d = round_up(off_c + nbd * 4, 256);     // Fmfma u16[md] (matrix-core first stage)
+      total = round_up(off_d + (fqjl_mfma_image_shape(d, m) ? md * 2 : 0), 256);
       blob.assign(total, 0);
+      if (fqjl_mfma_image_shape(d, m))
+        build_fqjl_mfma_image(hs, reinterpret_cast<uint16_t *>(blob.data() + off_d));
       uint32_t *ds = reinterpret_cast<uint32_t *>(blob.data() + off_a);
       float *gs = reinterpret_cast<float *>(blob.data() + off_c);
       const float inv = (float)(1.0 / std::sqrt((double)d));
@@ -167,6 +172,7 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
     sk->Dsign = reinterpret_cast<const uint32_t *>(base + off_a);
     sk->P = reinterpret_cast<const int32_t *>(base + off_b);
     sk->Gs = reinterpret_cast<const float *>(base + off_c);
+    if (fqjl_mfma_image_shape(d, m)) sk->Fmfma = reinterpret_cast<const uint16_t *>(base + off_d);
   }
   *out = sk;
   return QJL_OK;

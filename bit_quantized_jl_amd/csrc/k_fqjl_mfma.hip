@@ -1,0 +1,293 @@
+// FQJL key quantization with its first stage on the gfx950 matrix cores
+// ("Fast Quantized Johnson-Lindenstrauss Transforms" page: block b of the
+// sketch is H diag(G_b) Pi_b (H/sqrt d) diag(D_b), optional Gaussian dither
+// before the sign).
+//
+// For bfloat16 keys, everything before the Gaussian diagonal is one matrix
+// with entries +-1:  M_b = Pi_b H diag(D_b), M_b[i][c] = H[P_b[i]][c] D_b[c]
+// (the 1/sqrt d lives in the stored G_b / sqrt d; the image also carries
+// the sign of G_b[i] in row i, and the kernel scales by |G_b[i]| / sqrt d,
+// which keeps -0 out of the rest of the chain).  Its products with bf16
+// key elements are exact and the matrix cores sum them in float32, so
+// u_b = M_b k comes out of v_mfma_f32_32x32x16_bf16 exactly as from the
+// butterfly network, up to the order of the float32 additions.  What
+// remains runs on the vector ALUs per key: z = (G_b / sqrt d) * u_b, the
+// second Walsh-Hadamard transform y = H z, the dither, the sign and the
+// packing -- half the vector work of the all-butterfly kernel.
+//
+// Layout.  The operand image of [M_0; M_1; ...] uses the dense quantizer's
+// order (mfma_image.h) with one difference in the row order: tile
+// tau = 4 b + p (block b, pass p) puts coordinate 64 h + 16 p + v of block b
+// in accumulator register v of lane half h.  So after the four passes of a
+// block, lane (key r, half h) holds u_b[64 h .. 64 h + 63] of its key, in
+// order, in its 64 accumulator registers.  The second transform splits as
+// H_128 = [[H_64, H_64], [H_64, -H_64]]: each lane half runs H_64 on its own
+// half (a_h), one v_permlane32_swap gives every lane a_0 and a_1, and lane
+// half h keeps y[64 h + i] = a_0[i] + (-1)^h a_1[i].  Coordinates
+// [128 b + 64 h, + 64) are two output words, stored as 8 bytes.
+//
+// Schedule as in the dense quantizer: S fragments stream from LDS through a
+// ring of registers, each feeding RT column tiles of 32 keys; the key tile is
+// loaded straight into MFMA operand registers; the norm is summed with
+// v_dot2c_f32_bf16 during the first pass.  Two waves per SIMD hide one
+// another's vector work behind the matrix cores.
+#include "device_common.h"
+#include "fwht_common.h"
+#include "mfma_image.h"
+
+namespace qjl {
+
+bool fqjl_mfma_image_shape(int d, int m) {
+  return d == 128 && (m == 128 || m == 256 || m == 512);
+}
+
+// Host: operand image of the blocks' first stage M_b = Pi_b H diag(D_b),
+// with row i negated where G_b[i] < 0 (the kernel then scales by |G_b[i]|).
+void build_fqjl_mfma_image(const HostSketch &hs, uint16_t *out) {
+  const int d = hs.d, m = hs.m;
+  if (!fqjl_mfma_image_shape(d, m)) return;
+  const int T = d / 16, NB = m / d;
+  for (int b = 0; b < NB; ++b)
+    for (int p = 0; p < 4; ++p) {
+      const int tau = 4 * b + p;
+      for (int t = 0; t < T; ++t)
+        for (int l = 0; l < 64; ++l) {
+          const int r = l & 31, hh = l >> 5;
+          const int a = r >> 3, h = (r >> 2) & 1, bb = r & 3;
+          const int i = 64 * h + 16 * p + 4 * a + bb;  // coordinate of block b
+          const int pi = hs.P[(size_t)b * d + i];      // row of H it takes
+          const int gneg = hs.G[(size_t)b * d + i] < 0.f ? 1 : 0;  // sign of G_b[i], see below
+          for (int e = 0; e < 8; ++e) {
+            const int c = 8 * qm_chunk(hh, t) + e;
+            const int neg = (__builtin_popcount((unsigned)(pi & c)) & 1) ^
+                            (hs.D[(size_t)b * d + c] < 0 ? 1 : 0) ^ gneg;
+            out[(((size_t)tau * T + t) * 64 + l) * 8 + e] = neg ? 0xBF80 : 0x3F80;  // -1, +1
+          }
+        }
+    }
+}
+
+namespace {
+
+// Sign bits of 32 consecutive coordinates, bit t = [u[t] >= 0], one
+// v_alignbit_b32 each.  No -0 reaches here, so the sign bit alone decides:
+// the matrix cores start from +0 and return +0 for an all-zero sum, the
+// Gaussian diagonal's signs sit in the image (|G| > 0 multiplies), so z has
+// no -0; and a butterfly or a dither add yields -0 only from -0 operands
+// (x + (-x) rounds to +0).  A zero key thus packs to all ones.
+__device__ __forceinline__ uint32_t pack_signs(const float *u) {
+  uint32_t word = 0;
+#pragma unroll
+  for (int t = 31; t >= 0; --t) word = __builtin_amdgcn_alignbit(word, __float_as_uint(u[t]), 31);
+  return ~word;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int FM_RING = 4;  // S fragments in flight from LDS
+
+template <int T, int RT>
+struct FmKeys {
+  bf16x8_t a[RT][T];
+};
+
+// The B fragments of the 32 RT keys from k0 (rows past n re-read row n - 1;
+// their results are never stored), as the dense quantizer loads them.
+template <int T, int RT>
+__device__ __forceinline__ void fm_load(FmKeys<T, RT> &kt, const uint16_t *__restrict__ K,
+                                        int64_t k0, int64_t n, int r, int h) {
+  constexpr int D = 16 * T;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    int64_t row = k0 + 32 * rt + r;
+    row = row < n ? row : n - 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(K + row * D);
+#pragma unroll
+    for (int t = 0; t < T; ++t) kt.a[rt][t] = __builtin_bit_cast(bf16x8_t, src[qm_chunk(h, t)]);
+  }
+}
+
+template <int M, int WAVES, int RT, bool DITHER, bool MAPPED>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ Fimg,
+    const float *__restrict__ Gs, int64_t n, int64_t base, RowMap map, float rho, uint64_t dkey,
+    float *__restrict__ norms, uint32_t *__restrict__ bits) {
+  constexpr int D = 128, T = D / 16, NB = M / D, W = M / 32;
+  constexpr int NF = NB * 4 * T;  // S fragments per tile walk
+  constexpr int R = FM_RING;
+  __shared__ uint4 sF[M * D / 8];
+  __shared__ float sG[M];
+  const int tid = threadIdx.x;
+  {
+    const uint4 *src = reinterpret_cast<const uint4 *>(Fimg);
+    for (int i = tid; i < M * D / 8; i += 64 * WAVES) sF[i] = src[i];
+    for (int i = tid; i < M; i += 64 * WAVES) sG[i] = fabsf(Gs[i]);
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  constexpr int KEYS = 32 * RT;
+  const int64_t ntiles = (n + KEYS - 1) / KEYS;
+  const int64_t stride = (int64_t)gridDim.x * WAVES;
+  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
+    const int64_t k0 = tile * KEYS;
+    FmKeys<T, RT> kt;
+    fm_load<T, RT>(kt, K, k0, n, r, h);
+    // The fragment reads must stay inside the tile loop: hoisted, all of the
+    // image would be held in registers.
+    asm volatile("" ::: "memory");
+    bf16x8_t ring[R];
+#pragma unroll
+    for (int g = 0; g < R; ++g) ring[g] = __builtin_bit_cast(bf16x8_t, sF[g * 64 + lane]);
+    float ss[RT] = {};
+    float nrm[RT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      floatx16_t acc[RT][4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][p] = floatx16_t{};
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const int g = (4 * b + p) * T + t;
+          const bf16x8_t A = ring[g % R];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            acc[rt][p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, kt.a[rt][t], acc[rt][p], 0, 0, 0);
+          if (g + R < NF) ring[g % R] = __builtin_bit_cast(bf16x8_t, sF[(g + R) * 64 + lane]);
+          if (b == 0 && p == 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              const uint4 v = __builtin_bit_cast(uint4, kt.a[rt][t]);
+              const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const bf16x2_t kx = __builtin_bit_cast(bf16x2_t, w4[e]);
+                ss[rt] = __builtin_amdgcn_fdot2_f32_bf16(kx, kx, ss[rt], false);
+              }
+            }
+          }
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (b == 0) {
+        // each lane summed half of its key's chunks; lane half h stores the
+        // norm of column tile h (for RT = 1, half 0 stores)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) nrm[rt] = sqrtf(ss[rt] + __shfl_xor(ss[rt], 32));
+        if (RT > 1 || h == 0) {
+          const int64_t key = k0 + 32 * (RT > 1 ? h : 0) + r;
+          if (key < n)
+            __builtin_nontemporal_store(RT > 1 && h ? nrm[RT > 1 ? 1 : 0] : nrm[0],
+                                        norms + (MAPPED ? map_row(map, key) : key));
+        }
+      }
+      // ---- second stage of block b, per column tile
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float z[64];
+        const float4 *gp = reinterpret_cast<const float4 *>(sG + 128 * b + 64 * h);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float4 gv = gp[k];
+          const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[4 * k + e] = acc[rt][k / 4][4 * (k % 4) + e] * g4[e];
+        }
+        fwht_reg<64>(z);
+        // Top stage across the lane halves, two coordinates (i, i + 32) at a
+        // time.  The first swap brings a_0 and a_1 of coordinate i to half 0
+        // and of i + 32 to half 1; each half forms both the sum and the
+        // difference; the second swap sends each half the one it owns:
+        // afterwards lane half h holds y[64 h + i] and y[64 h + i + 32].
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[i]),
+                                                           __float_as_uint(z[i + 32]), false, false);
+          const float x = __uint_as_float(p1[0]), y = __uint_as_float(p1[1]);
+          const auto p2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x + y),
+                                                           __float_as_uint(x - y), false, false);
+          z[i] = __uint_as_float(p2[0]);
+          z[i + 32] = __uint_as_float(p2[1]);
+        }
+        const int64_t key = k0 + 32 * rt + r;
+        const int64_t orow = MAPPED ? map_row(map, key < n ? key : 0) : (key < n ? key : 0);
+        if (DITHER) {
+          const float amp = rho * nrm[rt];
+          const uint64_t pair0 =
+              (uint64_t)(base + orow) * (uint64_t)(M / 2) + (uint64_t)((128 * b + 64 * h) / 2);
+#pragma unroll
+          for (int c = 0; c < 64; c += 2) {
+            float xc, xs;
+            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            z[c] += amp * xc;
+            z[c + 1] += amp * xs;
+          }
+        }
+        const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
+        if (key < n)
+          __builtin_nontemporal_store(
+              u32x2_t{w0, w1},
+              reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
+        // keep the next block's matrix work (and its registers) out of this one
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+template <int M, bool DITHER, bool MAPPED>
+hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t base,
+                     const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
+#ifndef QJL_FM_RT
+#define QJL_FM_RT 1
+#endif
+  constexpr int RT = QJL_FM_RT;
+  constexpr int WAVES = M <= 256 ? 4 : 8;
+  auto kern = fqjl_mfma_kernel<M, WAVES, RT, DITHER, MAPPED>;
+  static const int resident = resident_workgroups(kern, 64 * WAVES);  // on the whole device
+  const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
+  const int64_t want = (ntiles + WAVES - 1) / WAVES;
+  const int grid = (int)(want < resident ? want : resident);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->Fmfma, sk->Gs, n, base,
+                     map, sk->host.rho, sk->dither_key, norms, bits);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_fm_m(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t base,
+                       const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
+  const bool dith = sk->host.rho > 0.f, mapped = map.per_group != 0;
+  if (dith && mapped) return launch_fm<M, true, true>(sk, K, n, base, map, norms, bits, st);
+  if (dith) return launch_fm<M, true, false>(sk, K, n, base, map, norms, bits, st);
+  if (mapped) return launch_fm<M, false, true>(sk, K, n, base, map, norms, bits, st);
+  return launch_fm<M, false, false>(sk, K, n, base, map, norms, bits, st);
+}
+
+}  // namespace
+
+bool fqjl_mfma_supported(const qjl_sketch *sk, const void *K, int dtype, const uint32_t *bits) {
+  const HostSketch &h = sk->host;
+  if (h.variant == QJL_VARIANT_DENSE || dtype != QJL_DTYPE_BF16 || sk->Fmfma == nullptr)
+    return false;
+  if (!fqjl_mfma_image_shape(h.d, h.m)) return false;
+  return ((uintptr_t)K & 15) == 0 && ((uintptr_t)bits & 15) == 0;
+}
+
+hipError_t launch_fqjl_mfma(const qjl_sketch *sk, const void *Kv, int64_t n, int64_t base,
+                            const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
+  const uint16_t *K = static_cast<const uint16_t *>(Kv);
+  switch (sk->host.m) {
+    case 128: return launch_fm_m<128>(sk, K, n, base, map, norms, bits, st);
+    case 256: return launch_fm_m<256>(sk, K, n, base, map, norms, bits, st);
+    case 512: return launch_fm_m<512>(sk, K, n, base, map, norms, bits, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qjl

@@ -17,26 +17,11 @@
 // pre-scaled by 1/sqrt(d) on the host, so the kernel computes
 // H (Gs_b * (H (D_b x))[P_b]).
 #include "device_common.h"
+#include "fwht_common.h"
 
 namespace qjl {
 
 namespace {
-
-template <int D>
-__device__ __forceinline__ void fwht_reg(float (&u)[D]) {
-#pragma unroll
-  for (int h = 1; h < D; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < D; i += 2 * h) {
-#pragma unroll
-      for (int j = i; j < i + h; ++j) {
-        const float a = u[j], b = u[j + h];
-        u[j] = a + b;
-        u[j + h] = a - b;
-      }
-    }
-  }
-}
 
 // Row loads as 16-byte vectors (a 2-byte load per element leaves each load
 // instruction touching 64 cache lines for 128 bytes).
@@ -58,15 +43,6 @@ __device__ __forceinline__ void load_row_vec(const T *__restrict__ xr, bool vali
       }
     }
   }
-}
-
-// Sign bits of 32 consecutive coordinates, bit t = [u[t] >= 0]: adding +0
-// turns -0 into +0, then each v_alignbit_b32 shifts one sign bit in.
-__device__ __forceinline__ uint32_t pack_nonneg(const float *u) {
-  uint32_t word = 0;
-#pragma unroll
-  for (int t = 31; t >= 0; --t) word = __builtin_amdgcn_alignbit(word, __float_as_uint(u[t] + 0.0f), 31);
-  return ~word;
 }
 
 // PERM = false: the block has no permutation (D-FQJL), so the transformed
@@ -482,6 +458,9 @@ hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
 
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
                        const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st) {
+  // bf16 keys at d = 128: the first stage on the matrix cores (k_fqjl_mfma)
+  if (Y == nullptr && fqjl_mfma_supported(sk, X, dtype, bits))
+    return launch_fqjl_mfma(sk, X, n, base, map, norms, bits, st);
   if (dtype == QJL_DTYPE_F32)
     return launch_fqjl_d(sk, static_cast<const float *>(X), n, base, map, norms, bits, Y, st);
   return launch_fqjl_d(sk, static_cast<const uint16_t *>(X), n, base, map, norms, bits, Y, st);

@@ -82,6 +82,8 @@ struct qjl_sketch {
   const uint32_t *Dsign = nullptr;    // nb*d sign masks: 0 (D=+1) or 0x80000000 (D=-1)
   const int32_t *P = nullptr;         // nb*d
   const float *Gs = nullptr;          // nb*d  G_b[c] / sqrt(d), rounded to float32
+  const uint16_t *Fmfma = nullptr;    // m*d bf16 (+-1): Pi_b H diag(D_b) in matrix-core operand
+                                      // order (k_fqjl_mfma), for d = 128; null otherwise
 };
 
 namespace qjl {
@@ -100,6 +102,9 @@ bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
                              const uint32_t *bits);
 hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, const RowMap &map,
                                 float *norms, uint32_t *bits, hipStream_t st);
+bool fqjl_mfma_supported(const qjl_sketch *sk, const void *K, int dtype, const uint32_t *bits);
+hipError_t launch_fqjl_mfma(const qjl_sketch *sk, const void *K, int64_t n, int64_t base,
+                            const RowMap &map, float *norms, uint32_t *bits, hipStream_t st);
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
                        const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st);
 hipError_t launch_score_generic(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
