@@ -123,7 +123,7 @@ SENTINEL_NORM = -7.0
     ("dense", 128, 512, "bf16", 0.0, 3, 129, 129, 0),     # whole groups
     ("dense", 128, 256, "f32", 0.0, 9, 3, 11, 8),         # float32 keys (generic kernel)
     ("dense", 96, 64, "bf16", 0.3, 4, 33, 40, 5),         # dithered dense (generic kernel)
-    ("fqjl", 128, 256, "bf16", 0.0, 64, 1, 50, 13),       # two lanes per row
+    ("fqjl", 128, 256, "bf16", 0.0, 64, 1, 50, 13),       # matrix-core first stage
     ("fqjl", 128, 256, "bf16", 0.1, 6, 45, 64, 19),       # with dither
     ("dfqjl", 128, 256, "bf16", 0.1, 7, 2, 9, 7),
     ("fqjl", 64, 192, "f32", 0.2, 5, 17, 17, 0),          # one row per lane
@@ -153,6 +153,30 @@ def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
     untouched[rows] = False
     assert np.all(got_b[untouched] == np.uint32(SENTINEL_BITS))
     assert np.all(got_n[untouched] == SENTINEL_NORM)
+    sk.close()
+
+
+@pytest.mark.parametrize("variant,rho", [("fqjl", 0.0), ("fqjl", 0.2), ("dfqjl", 0.1),
+                                         ("dense", 0.0)])
+def test_bits_buffer_alignment_paths(variant, rho):
+    # bits_out 4 bytes past a 16-byte boundary takes the vector kernels
+    # (FQJL: fqjl128_kernel, dense: the generic kernel) instead of the
+    # matrix-core ones; both agree with the oracle.
+    note("misaligned bits", variant, rho)
+    d, m, n = 128, 256, 777
+    W = m // 32
+    K = (torch.randn(n, d, generator=torch.Generator().manual_seed(3)) * 1.7).to(torch.bfloat16)
+    sk = qj.make_sketch(6, d, m, variant, rho)
+    flat = torch.empty(n * W + 4, dtype=torch.int32, device=DEV)
+    bits = flat[1:1 + n * W].view(n, W)
+    assert bits.data_ptr() % 16 == 4
+    norms = torch.empty(n, dtype=torch.float32, device=DEV)
+    qj.quantize_keys(sk, K.to(DEV), key_index_base=5, norms_out=norms, bits_out=bits)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(6, d, m, variant, rho)
+    rb, rn, mg, _ = oq.quantize(ref, to_np_f64(K), "bf16", key_index_base=5)
+    check_bits(bits_np(bits.contiguous()), rb, mg, m)
+    check_norms(to_np_f64(norms), rn)
     sk.close()
 
 
