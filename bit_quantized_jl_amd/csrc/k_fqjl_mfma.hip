@@ -86,6 +86,7 @@ __device__ __forceinline__ uint32_t pack_signs(const float *u) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int FM_RING = 4;  // S fragments in flight from LDS
 
@@ -133,14 +134,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
   constexpr int KEYS = 32 * RT;
   const int64_t ntiles = (n + KEYS - 1) / KEYS;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
-  // The next tile's keys load while this one is processed (rows past n are
-  // clamped, so a wave's last prefetch reads row n - 1 and is discarded).
+  // Up to m = 256 the next tile's keys load while this one is processed
+  // (rows past n are clamped, so a wave's last prefetch reads row n - 1 and
+  // is discarded); at m = 512 the registers are not there.
+  constexpr bool PF = M <= 256;
   FmKeys<T, RT> nxt;
-  fm_load<T, RT>(nxt, K, ((int64_t)blockIdx.x * WAVES + wave) * KEYS, n, r, h);
+  if (PF) fm_load<T, RT>(nxt, K, ((int64_t)blockIdx.x * WAVES + wave) * KEYS, n, r, h);
   for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
     const int64_t k0 = tile * KEYS;
-    const FmKeys<T, RT> kt = nxt;
-    fm_load<T, RT>(nxt, K, (tile + stride) * KEYS, n, r, h);
+    FmKeys<T, RT> kt;
+    if (PF) {
+      kt = nxt;
+      fm_load<T, RT>(nxt, K, (tile + stride) * KEYS, n, r, h);
+    } else {
+      fm_load<T, RT>(kt, K, k0, n, r, h);
+    }
     // The fragment reads must stay inside the tile loop: hoisted, all of the
     // image would be held in registers.
     asm volatile("" ::: "memory");
@@ -149,6 +157,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
     for (int g = 0; g < R; ++g) ring[g] = __builtin_bit_cast(bf16x8_t, sF[g * 64 + lane]);
     float ss[RT] = {};
     float nrm[RT];
+    uint32_t held[RT][2];  // the previous (even) block's two words, see the stores
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       floatx16_t acc[RT][4];
@@ -235,10 +244,28 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
           }
         }
         const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
-        if (key < n)
-          __builtin_nontemporal_store(
-              u32x2_t{w0, w1},
-              reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
+        if constexpr (NB != 2) {
+          // m = 128: a row is 16 bytes, written by the two halves in one
+          // instruction; m = 512 keeps 8-byte writes (no registers to spare)
+          if (key < n)
+            __builtin_nontemporal_store(
+                u32x2_t{w0, w1}, reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
+        } else if (b % 2 == 0) {
+          held[rt][0] = w0;  // words 4b + 2h, +1: written with the next block's
+          held[rt][1] = w1;
+        } else {
+          // Blocks b - 1 and b hold words [4 (b - 1), 4 b + 4) of the row, two
+          // per lane.  One swap per register gives lane half 0 the four words
+          // of block b - 1 and half 1 those of block b, so each half stores 16
+          // contiguous bytes and the pair of halves the whole 32-byte span
+          // (split 8-byte writes made the caches fetch the lines first).
+          const auto s0 = __builtin_amdgcn_permlane32_swap(held[rt][0], w0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(held[rt][1], w1, false, false);
+          if (key < n)
+            __builtin_nontemporal_store(
+                u32x4_t{s0[0], s1[0], s0[1], s1[1]},
+                reinterpret_cast<u32x4_t *>(bits + orow * W + 4 * (b - 1) + 4 * h));
+        }
         // keep the next block's matrix work (and its registers) out of this one
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
