@@ -16,6 +16,11 @@
 // Coordinates: block b produces sketch coordinates [b d, (b+1) d).  G_b is
 // pre-scaled by 1/sqrt(d) on the host, so the kernel computes
 // H (Gs_b * (H (D_b x))[P_b]).
+//
+// These all-vector kernels serve projections, float32 keys, d < 128 and
+// buffers that are not 16-byte aligned; bfloat16 keys at d = 128 are
+// quantized by k_fqjl_mfma.hip, which applies the first stage on the matrix
+// cores (launch_fqjl routes them).
 #include "device_common.h"
 #include "fwht_common.h"
 
