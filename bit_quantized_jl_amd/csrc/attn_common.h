@@ -43,11 +43,12 @@ hipError_t launch_attn_combine(const float *ws, int64_t rows, int P, float *out,
 
 // The multi-query partial kernel (k_attention_mq.hip): m = 128 T with T in
 // {1, 2, 4}, bf16 values of width 128, three or more queries per group.
-// *P_out receives the partials per row it writes.
+// *P_out receives the partials per row it writes into ws; when it is 1 the
+// kernel wrote the normalised result to out itself and no combine is needed.
 hipError_t launch_attn_mq_partials(int T, const float *Sq, const uint32_t *bits,
                                    const float *norms, const uint16_t *V, int64_t G, int64_t nq,
-                                   int64_t nk, float c, float sl2, float *ws, int *P_out,
-                                   hipStream_t st);
+                                   int64_t nk, float c, float sl2, float *ws, float *out,
+                                   int *P_out, hipStream_t st);
 int attn_mq_partials(int T, int64_t G, int64_t nk);
 bool attn_mq_supported(int T);
 

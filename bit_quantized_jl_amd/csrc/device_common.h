@@ -26,6 +26,16 @@ int resident_workgroups(K kernel, int threads) {
   return cus * per_cu;
 }
 
+// Compute units of the current device (fallback 256).
+inline int device_compute_units() {
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }

@@ -207,7 +207,8 @@ template <int T, int QP, bool PAIR>
 __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
-    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws) {
+    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws,
+    float *__restrict__ out) {
   static_assert(QP == 1 || QP == 2, "one or two query pairs per pass");
   constexpr int W = 4 * T;
   constexpr int m = 32 * W;
@@ -296,12 +297,20 @@ __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kern
           o0 = fmaf(f, sPart[w][h][lane], o0);
           o1 = fmaf(f, sPart[w][h][lane + 64], o1);
         }
-        float *dst = ws + ((g * nq + q0 + h) * (int64_t)P + blockIdx.x) * AT_PART;
-        dst[lane] = o0;
-        dst[lane + 64] = o1;
-        if (lane == 0) {
-          dst[AT_DV] = M;
-          dst[AT_DV + 1] = L;
+        if (P == 1) {
+          // the group's only workgroup: its merged state is the result
+          const float inv = 1.f / L;
+          float *o = out + (g * nq + q0 + h) * (int64_t)AT_DV;
+          o[lane] = o0 * inv;
+          o[lane + 64] = o1 * inv;
+        } else {
+          float *dst = ws + ((g * nq + q0 + h) * (int64_t)P + blockIdx.x) * AT_PART;
+          dst[lane] = o0;
+          dst[lane + 64] = o1;
+          if (lane == 0) {
+            dst[AT_DV] = M;
+            dst[AT_DV + 1] = L;
+          }
         }
       }
       __syncthreads();  // sPart and the query image are free again
@@ -407,9 +416,14 @@ __global__ __launch_bounds__(256) void attn_softmax_kernel(const float *__restri
 template <int T, int QP>
 void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
   static const int resident = resident_workgroups(attn_partial_kernel<T, QP, true>, SM_THREADS);
+  static const int cus = device_compute_units();
   int64_t chunk = (G * nk + resident - 1) / resident;
   constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
   chunk = (chunk + round - 1) / round * round;
+  // With at least one group per compute unit, one workgroup per group
+  // streams as fast as two per unit (measured at the 7B decode shape:
+  // 104 against 111 us) and writes the result itself, with no combine pass.
+  if (G >= cus) chunk = (nk + round - 1) / round * round;
   *chunk_out = chunk;
   *gx_out = (int)((nk + chunk - 1) / chunk);
 }
@@ -425,13 +439,15 @@ hipError_t launch_attn_t(const float *Sq, const uint32_t *bits, const float *nor
   dim3 grid((unsigned)gx, (unsigned)(G < 65535 ? G : 65535));
   if (nq > 1)
     hipLaunchKernelGGL((attn_partial_kernel<T, QP, true>), grid, dim3(SM_THREADS), 0, st, Sq,
-                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
+                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws, out);
   else
     hipLaunchKernelGGL((attn_partial_kernel<T, 1, false>), grid, dim3(SM_THREADS), 0, st, Sq,
-                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws);
-  const int64_t rows = G * nq;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)), dim3(64),
-                     0, st, ws, rows, P, out);
+                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws, out);
+  if (P > 1) {  // with one workgroup per group the kernel wrote the output itself
+    const int64_t rows = G * nq;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)),
+                       dim3(64), 0, st, ws, rows, P, out);
+  }
   return hipGetLastError();
 }
 
@@ -497,8 +513,9 @@ hipError_t launch_attention_fused(const qjl_sketch *sk, const float *Sq, const u
   // queries per pass, their weighted sums on the matrix cores.
   if (nq >= 3 && attn_mq_supported(T)) {
     int P = 0;
-    hipError_t e = launch_attn_mq_partials(T, Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, &P, st);
-    if (e != hipSuccess) return e;
+    hipError_t e =
+        launch_attn_mq_partials(T, Sq, bits, norms, Vb, G, nq, nk, c, sl2, ws, out, &P, st);
+    if (e != hipSuccess || P == 1) return e;
     return launch_attn_combine(ws, G * nq, P, out, st);
   }
   switch (T) {

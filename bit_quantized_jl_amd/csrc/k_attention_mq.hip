@@ -209,7 +209,8 @@ template <int T, int QP>
 __global__ __launch_bounds__(SM_THREADS, 1) void attn_mq_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
-    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws) {
+    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws,
+    float *__restrict__ out) {
   constexpr int W = 4 * T;
   constexpr int m = 32 * W;
   constexpr int NQ = 2 * QP;
@@ -402,12 +403,20 @@ __global__ __launch_bounds__(SM_THREADS, 1) void attn_mq_kernel(
             o0 = fmaf(f, sPart[w2][q][lane], o0);
             o1 = fmaf(f, sPart[w2][q][lane + 64], o1);
           }
-          float *dst = ws + ((g * nq + q0 + q) * (int64_t)P + blockIdx.x) * AT_PART;
-          dst[lane] = o0;
-          dst[lane + 64] = o1;
-          if (lane == 0) {
-            dst[AT_DV] = Mx;
-            dst[AT_DV + 1] = Ls;
+          if (P == 1) {
+            // the group's only workgroup: its merged state is the result
+            const float inv = 1.f / Ls;
+            float *o = out + (g * nq + q0 + q) * (int64_t)AT_DV;
+            o[lane] = o0 * inv;
+            o[lane + 64] = o1 * inv;
+          } else {
+            float *dst = ws + ((g * nq + q0 + q) * (int64_t)P + blockIdx.x) * AT_PART;
+            dst[lane] = o0;
+            dst[lane + 64] = o1;
+            if (lane == 0) {
+              dst[AT_DV] = Mx;
+              dst[AT_DV + 1] = Ls;
+            }
           }
         }
       }
@@ -429,24 +438,24 @@ void mq_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
 template <int T, int QP>
 hipError_t launch_mq_t(const float *Sq, const uint32_t *bits, const float *norms,
                        const uint16_t *V, int64_t G, int64_t nq, int64_t nk, float c, float sl2,
-                       float *ws, int *P_out, hipStream_t st) {
+                       float *ws, float *out, int *P_out, hipStream_t st) {
   int64_t chunk = 0;
   int gx = 0;
   mq_grid<T, QP>(G, nk, &chunk, &gx);
   *P_out = gx;
   dim3 grid((unsigned)gx, (unsigned)(G < 65535 ? G : 65535));
   hipLaunchKernelGGL((attn_mq_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms, V,
-                     G, nq, nk, (int)chunk, c, sl2, ws);
+                     G, nq, nk, (int)chunk, c, sl2, ws, out);
   return hipGetLastError();
 }
 
 template <int T>
 hipError_t launch_mq_qp(const float *Sq, const uint32_t *bits, const float *norms,
                         const uint16_t *V, int64_t G, int64_t nq, int64_t nk, float c, float sl2,
-                        float *ws, int *P_out, hipStream_t st) {
+                        float *ws, float *out, int *P_out, hipStream_t st) {
   // eight queries per pass once there are more than four
-  if (nq > 4) return launch_mq_t<T, 4>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, P_out, st);
-  return launch_mq_t<T, 2>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, P_out, st);
+  if (nq > 4) return launch_mq_t<T, 4>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, out, P_out, st);
+  return launch_mq_t<T, 2>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, out, P_out, st);
 }
 
 template <int T>
@@ -473,12 +482,12 @@ int attn_mq_partials(int T, int64_t G, int64_t nk) {
 
 hipError_t launch_attn_mq_partials(int T, const float *Sq, const uint32_t *bits,
                                    const float *norms, const uint16_t *V, int64_t G, int64_t nq,
-                                   int64_t nk, float c, float sl2, float *ws, int *P_out,
-                                   hipStream_t st) {
+                                   int64_t nk, float c, float sl2, float *ws, float *out,
+                                   int *P_out, hipStream_t st) {
   switch (T) {
-    case 1: return launch_mq_qp<1>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, P_out, st);
-    case 2: return launch_mq_qp<2>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, P_out, st);
-    case 4: return launch_mq_qp<4>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, P_out, st);
+    case 1: return launch_mq_qp<1>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, out, P_out, st);
+    case 2: return launch_mq_qp<2>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, out, P_out, st);
+    case 4: return launch_mq_qp<4>(Sq, bits, norms, V, G, nq, nk, c, sl2, ws, out, P_out, st);
   }
   return hipErrorInvalidValue;
 }
