@@ -74,7 +74,11 @@ FUSED = [(128, 1, 1, 1, 128, "bf16"), (128, 2, 1, 17, 128, "bf16"),
          (128, 2, 8, 1000, 128, "bf16"), (256, 3, 7, 513, 128, "bf16"),
          (512, 2, 6, 2049, 128, "bf16"), (256, 1, 16, 4096, 128, "bf16"),
          (128, 1, 3, 31, 128, "bf16"), (512, 4, 5, 20000, 128, "bf16"),
-         (1024, 1, 4, 300, 128, "bf16")]
+         (1024, 1, 4, 300, 128, "bf16"),
+         # a group per compute unit or more: one workgroup per group writes
+         # the result itself (no combine pass), for one, two and four queries
+         (256, 256, 1, 777, 128, "bf16"), (256, 300, 2, 129, 128, "bf16"),
+         (256, 256, 4, 333, 128, "bf16"), (128, 260, 3, 65, 128, "bf16")]
 PLAIN = [(384, 1, 2, 300, 128, "bf16"), (256, 2, 1, 300, 128, "f32"),
          (256, 2, 2, 300, 64, "bf16"), (96, 1, 2, 130, 128, "bf16"),
          (2048, 1, 1, 64, 128, "bf16"), (32, 3, 3, 33, 7, "f32")]
