@@ -411,18 +411,19 @@ __global__ __launch_bounds__(256) void attn_softmax_kernel(const float *__restri
   }
 }
 
-// The fast path's grid: one resident round of workgroups over the keys of
-// all groups (as the score kernel), at most 65535 groups per launch row.
+// The fast path's grid: one workgroup per compute unit over the keys of all
+// groups, at most 65535 groups per launch row.
 template <int T, int QP>
 void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
-  static const int resident = resident_workgroups(attn_partial_kernel<T, QP, true>, SM_THREADS);
+  // One workgroup per compute unit streams as fast as two (and, with fewer
+  // partials, combines faster: long context 241 against 245 us).  With at
+  // least one group per compute unit, each group gets one workgroup, which
+  // writes the result itself with no combine pass (7B decode: 104 against
+  // 111 us with two workgroups per unit and the combine).
   static const int cus = device_compute_units();
-  int64_t chunk = (G * nk + resident - 1) / resident;
+  int64_t chunk = (G * nk + cus - 1) / cus;
   constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
   chunk = (chunk + round - 1) / round * round;
-  // With at least one group per compute unit, one workgroup per group
-  // streams as fast as two per unit (measured at the 7B decode shape:
-  // 104 against 111 us) and writes the result itself, with no combine pass.
   if (G >= cus) chunk = (nk + round - 1) / round * round;
   *chunk_out = chunk;
   *gx_out = (int)((nk + chunk - 1) / chunk);
