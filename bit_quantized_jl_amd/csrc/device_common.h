@@ -4,15 +4,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "qjl_internal.h"
 
 namespace qjl {
 
+// A launch-shape quantity (compute units, resident workgroups of a kernel)
+// cached per device: each device keeps its own value, computed on first use
+// with that device current.  Concurrent first uses compute the same value,
+// and the relaxed atomics make that benign.
+struct PerDevice {
+  static constexpr int MAX_DEVICES = 64;
+  std::atomic<int> v[MAX_DEVICES];
+};
+template <typename F>
+int per_device(PerDevice &pd, F compute) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PerDevice::MAX_DEVICES)
+    return compute();
+  int x = pd.v[dev].load(std::memory_order_relaxed);
+  if (x == 0) {
+    x = compute();
+    pd.v[dev].store(x, std::memory_order_relaxed);
+  }
+  return x;
+}
+
 // Workgroups of `kernel` (launched with `threads` threads and no dynamic
 // LDS) that the current device holds at once: compute units times the
 // occupancy the runtime reports (fallbacks: 256 units, one workgroup each).
-// Callers cache it in a function-local static, whose initialization C++
-// makes thread safe.
+// Callers cache it per device (PerDevice).
 template <typename K>
 int resident_workgroups(K kernel, int threads) {
   int dev = 0, cus = 0, per_cu = 0;

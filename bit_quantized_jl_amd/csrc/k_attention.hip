@@ -420,7 +420,8 @@ void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
   // least one group per compute unit, each group gets one workgroup, which
   // writes the result itself with no combine pass (7B decode: 104 against
   // 111 us with two workgroups per unit and the combine).
-  static const int cus = device_compute_units();
+  static PerDevice pd_cus;
+  const int cus = per_device(pd_cus, device_compute_units);
   int64_t chunk = (G * nk + cus - 1) / cus;
   constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
   chunk = (chunk + round - 1) / round * round;

@@ -427,7 +427,9 @@ __global__ __launch_bounds__(SM_THREADS, 1) void attn_mq_kernel(
 
 template <int T, int QP>
 void mq_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
-  static const int resident = resident_workgroups(attn_mq_kernel<T, QP>, SM_THREADS);
+  static PerDevice pd_res;
+  const int resident =
+      per_device(pd_res, [] { return resident_workgroups(attn_mq_kernel<T, QP>, SM_THREADS); });
   int64_t chunk = (G * nk + resident - 1) / resident;
   constexpr int round = MQ_KEYS * SM_WAVES;
   chunk = (chunk + round - 1) / round * round;

@@ -292,7 +292,8 @@ hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const R
   constexpr int WAVES = M <= 256 ? 4 : 8;
   constexpr bool DEFER = M <= 256;
   auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER, MAPPED>;
-  static const int resident = resident_workgroups(kern, 64 * WAVES);  // on the whole device
+  static PerDevice pd_res;  // workgroups resident on the whole device
+  const int resident = per_device(pd_res, [&] { return resident_workgroups(kern, 64 * WAVES); });
   const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)(want < resident ? want : resident);

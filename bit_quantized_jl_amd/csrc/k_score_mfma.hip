@@ -311,8 +311,10 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   // One workgroup per compute unit: the keys of all groups in equal chunks
   // (long context: 57.5 against 61.3 us for the resident round of two or
   // three workgroups per unit, which set up each query more often).
-  static const int resident = resident_workgroups(score_mfma_kernel<T, QP>, SM_THREADS);
-  static const int cus = device_compute_units();
+  static PerDevice pd_res, pd_cus;
+  const int resident =
+      per_device(pd_res, [] { return resident_workgroups(score_mfma_kernel<T, QP>, SM_THREADS); });
+  const int cus = per_device(pd_cus, device_compute_units);
   // chunk: a multiple of the 256 keys one block step covers
   int64_t chunk = (G * nk + cus - 1) / cus;
   chunk = (chunk + 255) / 256 * 256;
