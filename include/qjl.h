@@ -241,7 +241,9 @@ qjl_status qjl_decode_attention_workspace_size(const qjl_sketch *sk, int64_t n_g
  * Sq, bits, norms as for qjl_score; V: device [n_groups*n_k][d_v] in
  * v_dtype (values are not sketched); out: device float[n_groups][n_q][d_v];
  * workspace: device, 16-byte aligned, at least the size above (holds the
- * per-workgroup softmax partials, or the scores on the plain path).  The fast
+ * softmax partials when a group's keys are split over several workgroups, or
+ * the scores on the plain path; with a group per compute unit or more each
+ * group is one workgroup and writes out directly).  The fast
  * paths take bf16 values with d_v = 128, m of 128, 256, 512 or 1024, fewer
  * than 2^22 keys per group and 16-byte aligned bits and V (three or more
  * queries per group with m <= 512 form the weighted sums on the matrix
