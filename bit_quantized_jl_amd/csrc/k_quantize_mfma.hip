@@ -35,6 +35,9 @@
 // that the VALU packing overlaps the matrix cores.  Bits and norms are
 // written with non-temporal stores: a later kernel reads them, this one does
 // not, and streaming them past the caches measured markedly faster.
+//
+// Short calls (decode-time appends) take quantize_small_kernel below, which
+// forms the same sums without staging S in LDS.
 #include "device_common.h"
 #include "mfma_image.h"
 
@@ -302,6 +305,70 @@ hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const R
   return hipGetLastError();
 }
 
+// Few keys (a decode-time append of one key per head): the same sums with
+// the operand image read from global memory instead of staged in LDS, one
+// wave per (32 keys, output word pair p).  Lane (r, h) forms tiles 2p + 1
+// and 2p (coordinates of word p + h W/2 of key r), in the quantizer's order:
+// the same MFMA inputs accumulated in the same order, the same sign packing
+// and the same norm chain, so the bits and norms equal the quantizer's.
+template <int D, bool MAPPED>
+__global__ __launch_bounds__(256) void quantize_small_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int m, int64_t n,
+    RowMap map, float *__restrict__ norms, uint32_t *__restrict__ bits) {
+  constexpr int T = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.y * 4 + (threadIdx.x >> 6);  // word pair
+  const int W = m / 32;
+  if (p >= W / 2) return;
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t row = (int64_t)blockIdx.x * 32 + r;
+  const int64_t lrow = row < n ? row : n - 1;  // rows past n re-read row n - 1, store nothing
+  const uint4 *src = reinterpret_cast<const uint4 *>(K + lrow * D);
+  const uint4 *img = reinterpret_cast<const uint4 *>(Simg) + lane;
+  bf16x8_t ka[T], s1[T], s0[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    ka[t] = __builtin_bit_cast(bf16x8_t, src[qm_chunk(h, t)]);
+    s1[t] = __builtin_bit_cast(bf16x8_t, img[((2 * p + 1) * T + t) * 64]);
+    s0[t] = __builtin_bit_cast(bf16x8_t, img[((2 * p) * T + t) * 64]);
+  }
+  floatx16_t acc1 = floatx16_t{}, acc0 = floatx16_t{};
+  float ss = 0.f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s1[t], ka[t], acc1, 0, 0, 0);
+    const uint4 v = __builtin_bit_cast(uint4, ka[t]);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2_t kx = __builtin_bit_cast(bf16x2_t, w[e]);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(kx, kx, ss, false);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(s0[t], ka[t], acc0, 0, 0, 0);
+  const float tot = ss + __shfl_xor(ss, 32);
+  const uint32_t zm = tot > 0.f ? 0u : 0xFFFFFFFFu;
+  uint32_t x = pack_signs<15, 0>(0u, acc1);
+  x = pack_signs<15, 0>(x, acc0);
+  if (row < n) {
+    const int64_t orow = MAPPED ? map_row(map, row) : row;
+    bits[orow * W + p + h * (W / 2)] = ~x | zm;
+    if (p == 0 && h == 0) norms[orow] = sqrtf(tot);
+  }
+}
+
+template <int D, bool MAPPED>
+hipError_t launch_qs(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
+                     float *norms, uint32_t *bits, hipStream_t st) {
+  const int W = sk->host.m / 32;
+  const dim3 grid((unsigned)((n + 31) / 32), (unsigned)((W / 2 + 3) / 4));
+  hipLaunchKernelGGL((quantize_small_kernel<D, MAPPED>), grid, dim3(256), 0, st, K, sk->S16mfma,
+                     sk->host.m, n, map, norms, bits);
+  return hipGetLastError();
+}
+
 template <bool MAPPED>
 hipError_t launch_qm_dm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
                         float *norms, uint32_t *bits, hipStream_t st) {
@@ -330,6 +397,17 @@ bool quantize_mfma_supported(const qjl_sketch *sk, const void *K, int dtype,
 hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *Kv, int64_t n, const RowMap &map,
                                 float *norms, uint32_t *bits, hipStream_t st) {
   const uint16_t *K = static_cast<const uint16_t *>(Kv);
+#ifndef QJL_QS_MAX
+#define QJL_QS_MAX 16384
+#endif
+  if (n <= QJL_QS_MAX) {  // latency-bound: skip staging S in LDS
+    const bool mp = map.per_group != 0;
+    if (sk->host.d == 128)
+      return mp ? launch_qs<128, true>(sk, K, n, map, norms, bits, st)
+                : launch_qs<128, false>(sk, K, n, map, norms, bits, st);
+    return mp ? launch_qs<64, true>(sk, K, n, map, norms, bits, st)
+              : launch_qs<64, false>(sk, K, n, map, norms, bits, st);
+  }
   if (map.per_group != 0) return launch_qm_dm<true>(sk, K, n, map, norms, bits, st);
   return launch_qm_dm<false>(sk, K, n, map, norms, bits, st);
 }

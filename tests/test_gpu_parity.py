@@ -92,6 +92,16 @@ def test_quantize_shapes(variant, d, m, dt, rho):
     run_quantize_case(w, base=11)
 
 
+@pytest.mark.parametrize("d,m", [(64, 128), (64, 256), (64, 512), (128, 128), (128, 256),
+                                 (128, 512)])
+def test_quantize_dense_persistent_kernel_shapes(d, m):
+    # More than 16384 keys (a ragged count): the persistent matrix-core
+    # quantizer with S staged in LDS, for every shape it serves.
+    w = wl.Workload(f"persistent_{d}_{m}", d, m, "dense", 1, 1, 16384 + 1357, 5, "bf16",
+                    "normal", 0.0, seed=4)
+    run_quantize_case(w, base=0)
+
+
 @pytest.mark.parametrize("variant,d,m,dt,nq", [
     ("dense", 128, 256, "f32", 37), ("dense", 128, 256, "bf16", 37), ("dense", 100, 96, "bf16", 37),
     ("dense", 16, 512, "f32", 37), ("dense", 128, 256, "bf16", 300), ("dense", 64, 128, "bf16", 33),
@@ -180,13 +190,17 @@ def test_bits_buffer_alignment_paths(variant, rho):
     sk.close()
 
 
-@pytest.mark.parametrize("variant,rho", [("dense", 0.0), ("fqjl", 0.1)])
-def test_cache_built_by_appends_equals_whole(variant, rho):
+@pytest.mark.parametrize("variant,rho,m,G,T", [("dense", 0.0, 256, 24, 9), ("fqjl", 0.1, 256, 24, 9),
+                                               ("dense", 0.0, 256, 64, 300),
+                                               ("dense", 0.0, 512, 40, 420)])
+def test_cache_built_by_appends_equals_whole(variant, rho, m, G, T):
     # Appending one key per group per step, then a block of four, fills the
-    # cache exactly as one call over the whole cache (same kernels per key,
-    # dither counters given by the cache row).
-    note("appends vs whole", variant, rho)
-    d, m, G, T = 128, 256, 24, 9
+    # cache exactly as one call over the whole cache (dither counters given
+    # by the cache row).  The dense cases with G T > 16384 keys compare the
+    # persistent matrix-core kernel (whole cache) with the short-call kernel
+    # (appends): the same sums in the same order, so the same bits.
+    note("appends vs whole", variant, rho, m, G, T)
+    d = 128
     gen = torch.Generator().manual_seed(5)
     cache_keys = (torch.randn(G, T, d, generator=gen) * 1.5).to(torch.bfloat16).to(DEV)
     sk = qj.make_sketch(2, d, m, variant, rho)
