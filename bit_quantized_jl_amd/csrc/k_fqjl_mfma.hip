@@ -274,12 +274,139 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
   }
 }
 
+// The short-call kernel's second stage of block b for one key, in two parts
+// (the output row is formed between them).  The arithmetic is that of
+// fqjl_mfma_kernel's epilogue, operation for operation, which keeps the
+// two kernels' bits identical; that kernel keeps its own copy, since at its
+// 256-register limit the inlined helpers spill.
+// fm_transform: z = |G_b| * u (gp: this lane half's 64 values of
+// |G_b| / sqrt d), then y = H z: H_64 per lane half and the top stage across
+// the halves; afterwards lane half h holds y[64 h .. 64 h + 63].
+__device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const float4 *gp,
+                                             float (&z)[64]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float4 gv = gp[k];
+    const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[4 * k + e] = acc[k / 4][4 * (k % 4) + e] * g4[e];
+  }
+  fwht_reg<64>(z);
+  // Top stage, two coordinates (i, i + 32) at a time.  The first swap brings
+  // a_0 and a_1 of coordinate i to half 0 and of i + 32 to half 1; each half
+  // forms both the sum and the difference; the second swap sends each half
+  // the one it owns: lane half h then holds y[64 h + i] and y[64 h + i + 32].
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[i]),
+                                                     __float_as_uint(z[i + 32]), false, false);
+    const float x = __uint_as_float(p1[0]), y = __uint_as_float(p1[1]);
+    const auto p2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x + y),
+                                                     __float_as_uint(x - y), false, false);
+    z[i] = __uint_as_float(p2[0]);
+    z[i + 32] = __uint_as_float(p2[1]);
+  }
+}
+
+// fm_finish: dither of size amp with the pair counters of output row drow
+// (coordinates [128 b + 64 h, + 64) of the sketch), sign, and the two words.
+template <int M, bool DITHER>
+__device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float amp, uint64_t dkey,
+                                          int64_t drow, uint32_t &w0, uint32_t &w1) {
+  if (DITHER) {
+    const uint64_t pair0 =
+        (uint64_t)drow * (uint64_t)(M / 2) + (uint64_t)((128 * b + 64 * h) / 2);
+#pragma unroll
+    for (int c = 0; c < 64; c += 2) {
+      float xc, xs;
+      dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+      z[c] += amp * xc;
+      z[c + 1] += amp * xs;
+    }
+  }
+  w0 = pack_signs(&z[0]);
+  w1 = pack_signs(&z[32]);
+}
+
+// Short calls (decode-time appends, m >= 256): one wave per 32 keys and
+// block b, the block's 32 image fragments read from global memory (L2)
+// instead of staging the whole image in LDS, and the blocks of a key on
+// different waves.  Measured per call at m = 256: 7.8 us against 10.2 us
+// for 256 keys (11.1 against 14.4 us with dither); at m = 512 with dither
+// 11.3 against 35.7 us.  From ~64K keys on, the persistent kernel is as
+// fast or faster (at the 7B shape 242 against 512 us).  Same key fragments,
+// the same matrix-core accumulations in the same order, the same norm chain
+// and the same second stage as fqjl_mfma_kernel, so the bits and norms are
+// those of that kernel; a cache filled by appends equals one quantized in a
+// single call.
+template <int M, bool DITHER, bool MAPPED>
+__global__ __launch_bounds__(64) void fqjl_mfma_small_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ Fimg,
+    const float *__restrict__ Gs, int64_t n, int64_t base, RowMap map, float rho, uint64_t dkey,
+    float *__restrict__ norms, uint32_t *__restrict__ bits) {
+  constexpr int D = 128, T = D / 16, W = M / 32;
+  __shared__ float sG[D];
+  const int lane = threadIdx.x, r = lane & 31, h = lane >> 5;
+  const int b = blockIdx.y;
+  sG[lane] = fabsf(Gs[D * b + lane]);
+  sG[lane + 64] = fabsf(Gs[D * b + lane + 64]);
+  const int64_t k0 = (int64_t)blockIdx.x * 32;
+  FmKeys<T, 1> kt;
+  fm_load<T, 1>(kt, K, k0, n, r, h);
+  const uint4 *img = reinterpret_cast<const uint4 *>(Fimg) + (size_t)4 * b * T * 64 + lane;
+  floatx16_t acc[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    acc[p] = floatx16_t{};
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, img[(p * T + t) * 64]), kt.a[0][t], acc[p], 0, 0, 0);
+  }
+  float ss = 0.f;
+  if (DITHER || b == 0) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const uint4 v = __builtin_bit_cast(uint4, kt.a[0][t]);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t kx = __builtin_bit_cast(bf16x2_t, w4[e]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(kx, kx, ss, false);
+      }
+    }
+  }
+  const float nrm = sqrtf(ss + __shfl_xor(ss, 32));
+  const int64_t key = k0 + r;
+  const int64_t orow = MAPPED ? map_row(map, key < n ? key : 0) : (key < n ? key : 0);
+  if (b == 0 && h == 0 && key < n) __builtin_nontemporal_store(nrm, norms + orow);
+  __syncthreads();
+  float z[64];
+  fm_transform(acc, reinterpret_cast<const float4 *>(sG + 64 * h), z);
+  uint32_t w0, w1;
+  fm_finish<M, DITHER>(z, b, h, DITHER ? rho * nrm : 0.f, dkey, base + orow, w0, w1);
+  if (key < n)
+    __builtin_nontemporal_store(u32x2_t{w0, w1},
+                                reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
+}
+
 template <int M, bool DITHER, bool MAPPED>
 hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t base,
                      const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
 #ifndef QJL_FM_RT
 #define QJL_FM_RT 1
 #endif
+#ifndef QJL_FS_MAX
+#define QJL_FS_MAX 16384
+#endif
+  // Latency-bound calls skip staging the image in LDS (m = 128 has a
+  // single block per key, which the persistent kernel serves as fast).
+  if (M >= 256 && n <= QJL_FS_MAX) {
+    const dim3 grid((unsigned)((n + 31) / 32), M / 128);
+    hipLaunchKernelGGL((fqjl_mfma_small_kernel<M, DITHER, MAPPED>), grid, dim3(64), 0, st, K,
+                       sk->Fmfma, sk->Gs, n, base, map, sk->host.rho, sk->dither_key, norms, bits);
+    return hipGetLastError();
+  }
   constexpr int RT = QJL_FM_RT;
   constexpr int WAVES = M <= 256 ? 4 : 8;
   auto kern = fqjl_mfma_kernel<M, WAVES, RT, DITHER, MAPPED>;

@@ -92,14 +92,18 @@ def test_quantize_shapes(variant, d, m, dt, rho):
     run_quantize_case(w, base=11)
 
 
-@pytest.mark.parametrize("d,m", [(64, 128), (64, 256), (64, 512), (128, 128), (128, 256),
-                                 (128, 512)])
-def test_quantize_dense_persistent_kernel_shapes(d, m):
-    # More than 16384 keys (a ragged count): the persistent matrix-core
-    # quantizer with S staged in LDS, for every shape it serves.
-    w = wl.Workload(f"persistent_{d}_{m}", d, m, "dense", 1, 1, 16384 + 1357, 5, "bf16",
-                    "normal", 0.0, seed=4)
-    run_quantize_case(w, base=0)
+@pytest.mark.parametrize("variant,d,m,rho", [
+    ("dense", 64, 128, 0.0), ("dense", 64, 256, 0.0), ("dense", 64, 512, 0.0),
+    ("dense", 128, 128, 0.0), ("dense", 128, 256, 0.0), ("dense", 128, 512, 0.0),
+    ("fqjl", 128, 128, 0.0), ("fqjl", 128, 256, 0.2), ("fqjl", 128, 512, 0.0),
+    ("dfqjl", 128, 256, 0.1), ("dfqjl", 128, 512, 0.1)])
+def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
+    # More than 16384 bf16 keys (a ragged count): the persistent matrix-core
+    # quantizers with the operand image staged in LDS, for every shape they
+    # serve (shorter calls take the short-call kernels).
+    w = wl.Workload(f"persistent_{variant}_{d}_{m}", d, m, variant, 1, 1, 16384 + 1357, 5,
+                    "bf16", "normal", rho, seed=4)
+    run_quantize_case(w, base=3)
 
 
 @pytest.mark.parametrize("variant,d,m,dt,nq", [
@@ -192,11 +196,14 @@ def test_bits_buffer_alignment_paths(variant, rho):
 
 @pytest.mark.parametrize("variant,rho,m,G,T", [("dense", 0.0, 256, 24, 9), ("fqjl", 0.1, 256, 24, 9),
                                                ("dense", 0.0, 256, 64, 300),
-                                               ("dense", 0.0, 512, 40, 420)])
+                                               ("dense", 0.0, 512, 40, 420),
+                                               ("fqjl", 0.2, 256, 64, 300),
+                                               ("fqjl", 0.0, 512, 40, 420),
+                                               ("fqjl", 0.0, 128, 48, 380)])
 def test_cache_built_by_appends_equals_whole(variant, rho, m, G, T):
     # Appending one key per group per step, then a block of four, fills the
     # cache exactly as one call over the whole cache (dither counters given
-    # by the cache row).  The dense cases with G T > 16384 keys compare the
+    # by the cache row).  The cases with G T > 16384 keys compare the
     # persistent matrix-core kernel (whole cache) with the short-call kernel
     # (appends): the same sums in the same order, so the same bits.
     note("appends vs whole", variant, rho, m, G, T)
