@@ -140,6 +140,11 @@ SENTINEL_NORM = -7.0
     ("fqjl", 128, 256, "bf16", 0.0, 64, 1, 50, 13),       # matrix-core first stage
     ("fqjl", 128, 256, "bf16", 0.1, 6, 45, 64, 19),       # with dither
     ("dfqjl", 128, 256, "bf16", 0.1, 7, 2, 9, 7),
+    ("fqjl", 128, 512, "bf16", 0.1, 11, 3, 40, 20),       # four blocks per key, dither
+    ("pfqjl", 128, 512, "bf16", 0.0, 5, 33, 70, 37),
+    ("fqjl", 128, 128, "bf16", 0.0, 9, 2, 20, 5),         # one block: the persistent kernel
+    ("dense", 128, 256, "bf16", 0.0, 2, 9000, 9100, 50),  # > 16384 keys: persistent kernels
+    ("fqjl", 128, 256, "bf16", 0.1, 2, 9000, 9100, 50),
     ("fqjl", 64, 192, "f32", 0.2, 5, 17, 17, 0),          # one row per lane
     ("fqjl", 16, 64, "f32", 0.0, 3, 5, 12, 2)])           # narrow blocks
 def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
