@@ -464,10 +464,10 @@ hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
                        const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st) {
   // bf16 keys at d = 128: the first stage on the matrix cores (k_fqjl_mfma),
-  // for every row count: short calls (decode-time appends of a few hundred
-  // keys) would be 1-3 us faster on the kernels below, but one kernel for
-  // every size keeps a cache filled by appends bit-identical to one call
-  // over the whole cache.
+  // for every row count.  Its short-call and persistent kernels form the
+  // same sums in the same order, so a cache filled by appends is
+  // bit-identical to one call over the whole cache; the kernels below sum
+  // in another order and would not be.
   if (Y == nullptr && fqjl_mfma_supported(sk, X, dtype, bits))
     return launch_fqjl_mfma(sk, X, n, base, map, norms, bits, st);
   if (dtype == QJL_DTYPE_F32)

@@ -154,7 +154,8 @@ qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t
  * same bits as one quantized whole.  (Which kernel runs depends on the
  * dtype, the shape and whether K and bits_out are 16-byte aligned; calls
  * that take different kernels can differ in coordinates within float32
- * rounding of zero, never elsewhere.)
+ * rounding of zero, never elsewhere.  The number of keys in a call selects
+ * between kernels that give identical results.)
  * K: device, [n_keys][d] in `dtype`, aligned to its element size.
  * norms_out: device float[n_keys]; bits_out: device uint32[n_keys][m/32].
  * Keys are expected finite: the bits and norm of a row holding NaN or
