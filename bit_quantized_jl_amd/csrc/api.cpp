@@ -299,8 +299,11 @@ qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
   qjl_status st = check_device(sk);
   if (st != QJL_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (sk->host.variant != QJL_VARIANT_DENSE)
+  if (sk->host.variant != QJL_VARIANT_DENSE) {
+    if (fqjl_project_mfma_supported(sk, q, dtype, Sq_out))
+      return from_hip(launch_fqjl_project_mfma(sk, q, n_queries, Sq_out, s));
     return from_hip(launch_fqjl(sk, q, dtype, n_queries, 0, RowMap{}, nullptr, nullptr, Sq_out, s));
+  }
   if (project_mfma_supported(sk, q, dtype, n_queries, Sq_out))
     return from_hip(launch_project_mfma(sk, q, n_queries, Sq_out, s));
   return from_hip(launch_project_dense(sk, q, dtype, n_queries, Sq_out, s));

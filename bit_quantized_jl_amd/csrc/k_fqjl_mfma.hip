@@ -390,6 +390,48 @@ __global__ __launch_bounds__(64) void fqjl_mfma_small_kernel(
                                 reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
 }
 
+// Query projection y = S q of bf16 queries (no dither, no sign), laid out
+// as the short-call quantizer: one wave per 32 queries and block b; lane
+// half h writes y[128 b + 64 h .. + 63] of its query, 256 contiguous bytes.
+// The matrix cores' sums are exact products summed in float32, so y equals
+// the quantizer's pre-sign values for the same vector: a bf16 key projected
+// as a query has the signs of its quantized bits (rho = 0).
+template <int M>
+__global__ __launch_bounds__(64) void fqjl_project_mfma_kernel(const uint16_t *__restrict__ Q,
+                                                               const uint16_t *__restrict__ Fimg,
+                                                               const float *__restrict__ Gs,
+                                                               int64_t n, float *__restrict__ Y) {
+  constexpr int D = 128, T = D / 16;
+  __shared__ float sG[D];
+  const int lane = threadIdx.x, r = lane & 31, h = lane >> 5;
+  const int b = blockIdx.y;
+  sG[lane] = fabsf(Gs[D * b + lane]);
+  sG[lane + 64] = fabsf(Gs[D * b + lane + 64]);
+  const int64_t q0 = (int64_t)blockIdx.x * 32;
+  FmKeys<T, 1> kt;
+  fm_load<T, 1>(kt, Q, q0, n, r, h);
+  const uint4 *img = reinterpret_cast<const uint4 *>(Fimg) + (size_t)4 * b * T * 64 + lane;
+  floatx16_t acc[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    acc[p] = floatx16_t{};
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, img[(p * T + t) * 64]), kt.a[0][t], acc[p], 0, 0, 0);
+  }
+  __syncthreads();
+  float z[64];
+  fm_transform(acc, reinterpret_cast<const float4 *>(sG + 64 * h), z);
+  const int64_t q = q0 + r;
+  if (q < n) {
+    float4 *dst = reinterpret_cast<float4 *>(Y + q * M + 128 * b + 64 * h);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      dst[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+  }
+}
+
 template <int M, bool DITHER, bool MAPPED>
 hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t base,
                      const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
@@ -438,6 +480,37 @@ bool fqjl_mfma_supported(const qjl_sketch *sk, const void *K, int dtype, const u
     return false;
   if (!fqjl_mfma_image_shape(h.d, h.m)) return false;
   return ((uintptr_t)K & 15) == 0 && ((uintptr_t)bits & 15) == 0;
+}
+
+bool fqjl_project_mfma_supported(const qjl_sketch *sk, const void *q, int dtype, const float *Y) {
+  const HostSketch &h = sk->host;
+  if (h.variant == QJL_VARIANT_DENSE || dtype != QJL_DTYPE_BF16 || sk->Fmfma == nullptr)
+    return false;
+  if (!fqjl_mfma_image_shape(h.d, h.m)) return false;
+  return ((uintptr_t)q & 15) == 0 && ((uintptr_t)Y & 15) == 0;
+}
+
+hipError_t launch_fqjl_project_mfma(const qjl_sketch *sk, const void *q, int64_t n, float *Y,
+                                    hipStream_t st) {
+  const uint16_t *Q = static_cast<const uint16_t *>(q);
+  if ((n + 31) / 32 > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((n + 31) / 32), sk->host.m / 128);
+  switch (sk->host.m) {
+    case 128:
+      hipLaunchKernelGGL(fqjl_project_mfma_kernel<128>, grid, dim3(64), 0, st, Q, sk->Fmfma,
+                         sk->Gs, n, Y);
+      break;
+    case 256:
+      hipLaunchKernelGGL(fqjl_project_mfma_kernel<256>, grid, dim3(64), 0, st, Q, sk->Fmfma,
+                         sk->Gs, n, Y);
+      break;
+    case 512:
+      hipLaunchKernelGGL(fqjl_project_mfma_kernel<512>, grid, dim3(64), 0, st, Q, sk->Fmfma,
+                         sk->Gs, n, Y);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fqjl_mfma(const qjl_sketch *sk, const void *Kv, int64_t n, int64_t base,

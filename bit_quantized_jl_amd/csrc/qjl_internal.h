@@ -105,6 +105,9 @@ hipError_t launch_quantize_mfma(const qjl_sketch *sk, const void *K, int64_t n, 
 bool fqjl_mfma_supported(const qjl_sketch *sk, const void *K, int dtype, const uint32_t *bits);
 hipError_t launch_fqjl_mfma(const qjl_sketch *sk, const void *K, int64_t n, int64_t base,
                             const RowMap &map, float *norms, uint32_t *bits, hipStream_t st);
+bool fqjl_project_mfma_supported(const qjl_sketch *sk, const void *q, int dtype, const float *Y);
+hipError_t launch_fqjl_project_mfma(const qjl_sketch *sk, const void *q, int64_t n, float *Y,
+                                    hipStream_t st);
 hipError_t launch_fqjl(const qjl_sketch *sk, const void *X, int dtype, int64_t n, int64_t base,
                        const RowMap &map, float *norms, uint32_t *bits, float *Y, hipStream_t st);
 hipError_t launch_score_generic(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,

@@ -112,7 +112,8 @@ def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     ("dense", 256, 64, "bf16", 65), ("dense", 48, 192, "bf16", 31), ("dense", 16, 64, "bf16", 1),
     ("dense", 128, 512, "bf16", 70), ("fqjl", 128, 256, "bf16", 37), ("fqjl", 8, 32, "f32", 37),
     ("fqjl", 64, 192, "f32", 37), ("fqjl", 128, 512, "bf16", 37), ("dfqjl", 128, 256, "bf16", 37),
-    ("dfqjl", 16, 64, "f32", 37), ("pfqjl", 128, 256, "bf16", 37)])
+    ("dfqjl", 16, 64, "f32", 37), ("pfqjl", 128, 256, "bf16", 37), ("fqjl", 128, 128, "bf16", 70),
+    ("fqjl", 128, 256, "bf16", 300), ("dfqjl", 128, 512, "bf16", 1)])
 def test_project_query(variant, d, m, dt, nq):
     note("project", variant, d, m, dt, nq)
     rho = 0.1 if variant == "dfqjl" else 0.0  # queries are never dithered
@@ -124,6 +125,26 @@ def test_project_query(variant, d, m, dt, nq):
     ref = oracle_sketch(5, d, m, variant, rho)
     qd = to_np_f64(q)
     check_projection(to_np_f64(Sq), oq.project(ref, qd, dt), qd, m)
+    sk.close()
+
+
+@pytest.mark.parametrize("variant", ["dense", "fqjl", "dfqjl"])
+def test_project_query_unaligned_output(variant):
+    # Sq_out 4 bytes past a 16-byte boundary takes the vector kernels instead
+    # of the matrix-core ones; both agree with the oracle.
+    note("project, unaligned Sq", variant)
+    d, m, nq = 128, 256, 45
+    rho = 0.1 if variant == "dfqjl" else 0.0
+    q = torch.randn(nq, d, generator=torch.Generator().manual_seed(8)).to(torch.bfloat16)
+    sk = qj.make_sketch(12, d, m, variant, rho)
+    flat = torch.empty(nq * m + 4, dtype=torch.float32, device=DEV)
+    Sq = flat[1:1 + nq * m].view(nq, m)
+    assert Sq.data_ptr() % 16 == 4
+    qj.project_query(sk, q.to(DEV), Sq_out=Sq)
+    torch.cuda.synchronize()
+    qd = to_np_f64(q)
+    check_projection(to_np_f64(Sq), oq.project(oracle_sketch(12, d, m, variant, rho), qd, "bf16"),
+                     qd, m)
     sk.close()
 
 
@@ -250,15 +271,18 @@ def test_quantize_into_cache_errors():
     sk.close()
 
 
-@pytest.mark.parametrize("d,m", [(128, 256), (64, 512), (128, 128)])
-def test_projected_keys_reproduce_their_bits(d, m):
-    # Projecting bf16 keys as queries applies the same S as quantizing them
-    # (same bf16 sketch, same float32 matrix-core accumulation), so the signs
-    # of the projection are the quantized bits, bit for bit.
-    note("project-vs-quantize", d, m)
+@pytest.mark.parametrize("variant,d,m", [("dense", 128, 256), ("dense", 64, 512),
+                                         ("dense", 128, 128), ("fqjl", 128, 256),
+                                         ("fqjl", 128, 512), ("pfqjl", 128, 128)])
+def test_projected_keys_reproduce_their_bits(variant, d, m):
+    # Projecting bf16 keys as queries applies the same sketch as quantizing
+    # them (dense: the same bf16 S; FQJL: the same +-1 first stage, float32
+    # matrix-core accumulation in the same order, the same second stage), so
+    # the signs of the projection are the quantized bits, bit for bit.
+    note("project-vs-quantize", variant, d, m)
     n = 333
     K = torch.randn(n, d, generator=torch.Generator().manual_seed(d + m)).to(torch.bfloat16)
-    sk = qj.make_sketch(9, d, m, "dense", 0.0)
+    sk = qj.make_sketch(9, d, m, variant, 0.0)
     norms, bits = qj.quantize_keys(sk, K.to(DEV))
     Sq = qj.project_query(sk, K.to(DEV))
     torch.cuda.synchronize()
