@@ -201,8 +201,10 @@ qjl_status qjl_quantize_keys_into(const qjl_sketch *sk, const void *K, int32_t d
  * and bfloat16 queries with d % 16 == 0, m % 64 == 0 and 16-byte aligned q
  * and Sq_out, the products run on the matrix cores exactly as in the
  * quantizer (exact bf16 products, float32 sums), so projecting a key gives
- * the very signs qjl_quantize_keys stores for it; other cases sum in
- * float32 in increasing coordinate order.
+ * the very signs qjl_quantize_keys stores for it.  The same holds for the
+ * FQJL sketches with bfloat16 queries at d = 128, m in {128, 256, 512} and
+ * 16-byte aligned q and Sq_out (first stage on the matrix cores as in the
+ * quantizer).  Other cases sum in float32 in the order of their kernel.
  */
 qjl_status qjl_project_query(const qjl_sketch *sk, const void *q, int32_t dtype,
                              int64_t n_queries, float *Sq_out, void *stream);
