@@ -538,7 +538,7 @@ def run_only(kind: str):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the kernels work on one GPU's shard; see the sharding note in the design).",
               file=sys.stderr)
         sys.exit(2)

@@ -100,7 +100,7 @@ typedef enum { QJL_DTYPE_F32 = 0, QJL_DTYPE_BF16 = 1 } qjl_dtype;
 
 typedef struct qjl_sketch qjl_sketch; /* opaque, library-owned */
 
-/* Limits of this build.  dense: 1 <= d <= 512;  FQJL: d a power of two in
+/* Limits of this library.  dense: 1 <= d <= 512;  FQJL: d a power of two in
  * [8, 128] and m a multiple of d;  both: 32 <= m <= 8192, m % 32 == 0. */
 #define QJL_MAX_D 512
 #define QJL_MAX_M 8192
