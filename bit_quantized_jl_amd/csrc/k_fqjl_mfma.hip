@@ -33,6 +33,14 @@
 // hide one another's vector work behind the matrix cores.  (Measured on the
 // 7B shape: the prefetch gains 2-3%; two column tiles per wave spill and lose
 // 25%; alternating the four passes' accumulation chains changes nothing.)
+//
+// Three kernels share the layout: fqjl_mfma_kernel (persistent, image in
+// LDS: large calls), fqjl_mfma_small_kernel (short calls at m >= 256, image
+// fragments from L2, one wave per key tile and block) and
+// fqjl_project_mfma_kernel (queries: the same first and second stage, the
+// float32 values stored instead of signs).  All three form the same sums
+// in the same order, so a key's bits do not depend on the call's size and
+// a projected key has the signs of its bits.
 #include "device_common.h"
 #include "fwht_common.h"
 #include "mfma_image.h"
