@@ -22,9 +22,11 @@
 // block, lane (key r, half h) holds u_b[64 h .. 64 h + 63] of its key, in
 // order, in its 64 accumulator registers.  The second transform splits as
 // H_128 = [[H_64, H_64], [H_64, -H_64]]: each lane half runs H_64 on its own
-// half (a_h), one v_permlane32_swap gives every lane a_0 and a_1, and lane
-// half h keeps y[64 h + i] = a_0[i] + (-1)^h a_1[i].  Coordinates
-// [128 b + 64 h, + 64) are two output words, stored as 8 bytes.
+// half (a_h); one v_permlane32_swap per coordinate pair (i, i + 32) gives
+// half h a_0 and a_1 at coordinate i + 32 h, and it keeps both
+// y[32 h + i] = a_0 + a_1 and y[64 + 32 h + i] = a_0 - a_1.  Those are
+// output words 4 b + h and 4 b + 2 + h; one more swap per word pair puts
+// them in row order for the store.
 //
 // Schedule as in the dense quantizer: S fragments stream from LDS through a
 // ring of registers, each feeding RT column tiles of 32 keys; the key tile is
@@ -223,43 +225,44 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
         }
         fwht_reg<64>(z);
         // Top stage across the lane halves, two coordinates (i, i + 32) at a
-        // time.  The first swap brings a_0 and a_1 of coordinate i to half 0
-        // and of i + 32 to half 1; each half forms both the sum and the
-        // difference; the second swap sends each half the one it owns:
-        // afterwards lane half h holds y[64 h + i] and y[64 h + i + 32].
+        // time: one swap brings a_0 and a_1 of coordinate i to half 0 and of
+        // i + 32 to half 1, and each half keeps both the sum and the
+        // difference.  Lane half h then holds y[32 h + i] in z[i] and
+        // y[64 + 32 h + i] in z[32 + i]: its words are 4 b + h and
+        // 4 b + 2 + h, put in row order by one swap per word pair below.
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[i]),
                                                            __float_as_uint(z[i + 32]), false, false);
           const float x = __uint_as_float(p1[0]), y = __uint_as_float(p1[1]);
-          const auto p2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x + y),
-                                                           __float_as_uint(x - y), false, false);
-          z[i] = __uint_as_float(p2[0]);
-          z[i + 32] = __uint_as_float(p2[1]);
+          z[i] = x + y;
+          z[i + 32] = x - y;
         }
         const int64_t key = k0 + 32 * rt + r;
         const int64_t orow = MAPPED ? map_row(map, key < n ? key : 0) : (key < n ? key : 0);
         if (DITHER) {
           const float amp = rho * nrm[rt];
           const uint64_t pair0 =
-              (uint64_t)(base + orow) * (uint64_t)(M / 2) + (uint64_t)((128 * b + 64 * h) / 2);
+              (uint64_t)(base + orow) * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
 #pragma unroll
           for (int c = 0; c < 64; c += 2) {
             float xc, xs;
-            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            dither_pair(dkey, pair0 + (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
             z[c] += amp * xc;
             z[c + 1] += amp * xs;
           }
         }
         const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
         if constexpr (NB != 2) {
+          // One swap gives lane half h words 4 b + 2 h and 4 b + 2 h + 1.
           // m = 128: a row is 16 bytes, written by the two halves in one
           // instruction; m = 512 keeps 8-byte writes (no registers to spare)
+          const auto sw = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);
           if (key < n)
             __builtin_nontemporal_store(
-                u32x2_t{w0, w1}, reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
+                u32x2_t{sw[0], sw[1]}, reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
         } else if (b % 2 == 0) {
-          held[rt][0] = w0;  // words 4b + 2h, +1: written with the next block's
+          held[rt][0] = w0;  // words 4b + h and 4b + 2 + h: written with the next block's
           held[rt][1] = w1;
         } else {
           // Blocks b - 1 and b hold words [4 (b - 1), 4 b + 4) of the row, two
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
           const auto s1 = __builtin_amdgcn_permlane32_swap(held[rt][1], w1, false, false);
           if (key < n)
             __builtin_nontemporal_store(
-                u32x4_t{s0[0], s1[0], s0[1], s1[1]},
+                u32x4_t{s0[0], s0[1], s1[0], s1[1]},
                 reinterpret_cast<u32x4_t *>(bits + orow * W + 4 * (b - 1) + 4 * h));
         }
         // keep the next block's matrix work (and its registers) out of this one
@@ -300,34 +303,33 @@ __device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const f
     for (int e = 0; e < 4; ++e) z[4 * k + e] = acc[k / 4][4 * (k % 4) + e] * g4[e];
   }
   fwht_reg<64>(z);
-  // Top stage, two coordinates (i, i + 32) at a time.  The first swap brings
-  // a_0 and a_1 of coordinate i to half 0 and of i + 32 to half 1; each half
-  // forms both the sum and the difference; the second swap sends each half
-  // the one it owns: lane half h then holds y[64 h + i] and y[64 h + i + 32].
+  // Top stage, two coordinates (i, i + 32) at a time: one swap brings a_0
+  // and a_1 of coordinate i to half 0 and of i + 32 to half 1, and each half
+  // keeps both the sum and the difference: lane half h then holds
+  // y[32 h + i] in z[i] and y[64 + 32 h + i] in z[32 + i].
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(z[i]),
                                                      __float_as_uint(z[i + 32]), false, false);
     const float x = __uint_as_float(p1[0]), y = __uint_as_float(p1[1]);
-    const auto p2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x + y),
-                                                     __float_as_uint(x - y), false, false);
-    z[i] = __uint_as_float(p2[0]);
-    z[i + 32] = __uint_as_float(p2[1]);
+    z[i] = x + y;
+    z[i + 32] = x - y;
   }
 }
 
 // fm_finish: dither of size amp with the pair counters of output row drow
-// (coordinates [128 b + 64 h, + 64) of the sketch), sign, and the two words.
+// (the coordinates fm_transform left in lane half h), sign, and the two
+// words: 4 b + h and 4 b + 2 + h of the row.
 template <int M, bool DITHER>
 __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float amp, uint64_t dkey,
                                           int64_t drow, uint32_t &w0, uint32_t &w1) {
   if (DITHER) {
     const uint64_t pair0 =
-        (uint64_t)drow * (uint64_t)(M / 2) + (uint64_t)((128 * b + 64 * h) / 2);
+        (uint64_t)drow * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
 #pragma unroll
     for (int c = 0; c < 64; c += 2) {
       float xc, xs;
-      dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+      dither_pair(dkey, pair0 + (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
       z[c] += amp * xc;
       z[c + 1] += amp * xs;
     }
@@ -393,14 +395,16 @@ __global__ __launch_bounds__(64) void fqjl_mfma_small_kernel(
   fm_transform(acc, reinterpret_cast<const float4 *>(sG + 64 * h), z);
   uint32_t w0, w1;
   fm_finish<M, DITHER>(z, b, h, DITHER ? rho * nrm : 0.f, dkey, base + orow, w0, w1);
+  const auto sw = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);  // words 4b + 2h, +1
   if (key < n)
-    __builtin_nontemporal_store(u32x2_t{w0, w1},
+    __builtin_nontemporal_store(u32x2_t{sw[0], sw[1]},
                                 reinterpret_cast<u32x2_t *>(bits + orow * W + 4 * b + 2 * h));
 }
 
 // Query projection y = S q of bf16 queries (no dither, no sign), laid out
 // as the short-call quantizer: one wave per 32 queries and block b; lane
-// half h writes y[128 b + 64 h .. + 63] of its query, 256 contiguous bytes.
+// half h writes the 64 coordinates fm_transform leaves it, two runs of 128
+// contiguous bytes.
 // The matrix cores' sums are exact products summed in float32, so y equals
 // the quantizer's pre-sign values for the same vector: a bf16 key projected
 // as a query has the signs of its quantized bits (rho = 0).
@@ -432,11 +436,14 @@ __global__ __launch_bounds__(64) void fqjl_project_mfma_kernel(const uint16_t *_
   float z[64];
   fm_transform(acc, reinterpret_cast<const float4 *>(sG + 64 * h), z);
   const int64_t q = q0 + r;
-  if (q < n) {
-    float4 *dst = reinterpret_cast<float4 *>(Y + q * M + 128 * b + 64 * h);
+  if (q < n) {  // coordinates 128 b + 32 h + [0, 32) and 128 b + 64 + 32 h + [0, 32)
+    float4 *lo = reinterpret_cast<float4 *>(Y + q * M + 128 * b + 32 * h);
+    float4 *hi = reinterpret_cast<float4 *>(Y + q * M + 128 * b + 64 + 32 * h);
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      dst[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+    for (int k = 0; k < 8; ++k) {
+      lo[k] = make_float4(z[4 * k], z[4 * k + 1], z[4 * k + 2], z[4 * k + 3]);
+      hi[k] = make_float4(z[32 + 4 * k], z[33 + 4 * k], z[34 + 4 * k], z[35 + 4 * k]);
+    }
   }
 }
 
