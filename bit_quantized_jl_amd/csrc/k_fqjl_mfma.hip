@@ -170,6 +170,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
     uint32_t held[RT][2];  // the previous (even) block's two words, see the stores
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      // Without dither, the wave issuing its matrix-core chain runs at a
+      // raised priority and drops it for the vector epilogue, so the other
+      // wave's epilogue fills the gaps without delaying the chain: 212
+      // against 231 us at m = 256, 406 against 427 us at m = 512.  With
+      // dither the epilogue dominates and the raise costs up to 4%.
+      if constexpr (!DITHER) __builtin_amdgcn_s_setprio(1);
       floatx16_t acc[RT][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -211,6 +217,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
                                         norms + (MAPPED ? map_row(map, key) : key));
         }
       }
+      if constexpr (!DITHER) __builtin_amdgcn_s_setprio(0);
       // ---- second stage of block b, per column tile
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
