@@ -83,8 +83,12 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_
 // revolutions (sin(2 pi u2) = v_sin_f32(u2), u2 in [0, 1)).  Their float32
 // errors move a dither value by ~1e-6 of its size, far below the band of
 // coordinates whose sign is not compared bit for bit.
-__device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &xc, float &xs) {
-  const uint64_t h = stream_draw(key, ctr);
+// From the generator's state key + PHI (ctr + 1) (stream_draw's argument to
+// mix64): a loop over consecutive counters forms the state once and adds
+// multiples of PHI, which the compiler would otherwise fold back into a
+// 64-bit multiply-add per pair.
+__device__ __forceinline__ void dither_pair_state(uint64_t state, float &xc, float &xs) {
+  const uint64_t h = mix64(state);
   const uint32_t a = (uint32_t)(h >> 40);
   const uint32_t b = (uint32_t)(h >> 16) & 0xFFFFFFu;
   const float u1 = (float)(a + 1u) * 0x1p-24f;
@@ -92,6 +96,18 @@ __device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &x
   const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
   xc = r * __builtin_amdgcn_cosf(u2);
   xs = r * __builtin_amdgcn_sinf(u2);
+}
+
+__device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &xc, float &xs) {
+  dither_pair_state(key + PHI * (ctr + 1), xc, xs);
+}
+
+// State of counter ctr, opaque to the optimiser (an empty asm on its
+// register pair), so that state + PHI k stays one 64-bit add per pair.
+__device__ __forceinline__ uint64_t dither_state(uint64_t key, uint64_t ctr) {
+  uint64_t s = key + PHI * (ctr + 1);
+  asm volatile("" : "+v"(s));
+  return s;
 }
 
 __device__ __forceinline__ float dither_one(uint64_t key, uint64_t key_index, int m, int j) {

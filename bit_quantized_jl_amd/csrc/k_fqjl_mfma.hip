@@ -251,10 +251,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
           const float amp = rho * nrm[rt];
           const uint64_t pair0 =
               (uint64_t)(base + orow) * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
+          const uint64_t st0 = dither_state(dkey, pair0);
 #pragma unroll
           for (int c = 0; c < 64; c += 2) {
             float xc, xs;
-            dither_pair(dkey, pair0 + (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
+            dither_pair_state(st0 + PHI * (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
             z[c] += amp * xc;
             z[c + 1] += amp * xs;
           }
@@ -333,10 +334,11 @@ __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float am
   if (DITHER) {
     const uint64_t pair0 =
         (uint64_t)drow * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
+    const uint64_t st0 = dither_state(dkey, pair0);
 #pragma unroll
     for (int c = 0; c < 64; c += 2) {
       float xc, xs;
-      dither_pair(dkey, pair0 + (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
+      dither_pair_state(st0 + PHI * (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
       z[c] += amp * xc;
       z[c + 1] += amp * xs;
     }

@@ -119,10 +119,11 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
           const float amp = rho * nrm;
           const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) +
                                  (uint64_t)(b * D / 2);
+          const uint64_t st0 = dither_state(dkey, pair0);
 #pragma unroll
           for (int c = 0; c < D; c += 2) {
             float xc, xs;
-            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
             u[c] += amp * xc;
             u[c + 1] += amp * xs;
           }
@@ -265,10 +266,11 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
         if (DITHER) {
           const float amp = rho * nrm;
           const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
+          const uint64_t st0 = dither_state(dkey, pair0);
 #pragma unroll
           for (int c = 0; c < H; c += 2) {
             float xc, xs;
-            dither_pair(dkey, pair0 + (uint64_t)(c / 2), xc, xs);
+            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
             t[c] += amp * xc;
             t[c + 1] += amp * xs;
           }
