@@ -251,6 +251,25 @@ def test_cache_built_by_appends_equals_whole(variant, rho, m, G, T):
     sk.close()
 
 
+@pytest.mark.parametrize("variant,m,rho", [("dense", 256, 0.0), ("dense", 512, 0.0),
+                                           ("fqjl", 256, 0.0), ("fqjl", 512, 0.1),
+                                           ("dfqjl", 256, 0.1), ("fqjl", 128, 0.2)])
+def test_call_size_does_not_change_bits(variant, m, rho):
+    # The first 3000 keys quantized alone (short-call kernels) and as part of
+    # a 20000-key call (persistent kernels): identical bits and norms.
+    note("call size", variant, m, rho)
+    d, n = 128, 20000
+    K = (torch.randn(n, d, generator=torch.Generator().manual_seed(m + 3)) * 1.3)
+    K = K.to(torch.bfloat16).to(DEV)
+    sk = qj.make_sketch(21, d, m, variant, rho)
+    n_all, b_all = qj.quantize_keys(sk, K, key_index_base=9)
+    n_few, b_few = qj.quantize_keys(sk, K[:3000].contiguous(), key_index_base=9)
+    torch.cuda.synchronize()
+    assert torch.equal(b_few, b_all[:3000])
+    assert torch.equal(n_few, n_all[:3000])
+    sk.close()
+
+
 def test_quantize_into_cache_errors():
     note("quantize into cache errors")
     sk = qj.make_sketch(0, 128, 256, "dense", 0.0)
