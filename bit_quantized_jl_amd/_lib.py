@@ -122,6 +122,31 @@ def _dev_tensor(t, name: str, ndim: int | None = None):
     return t
 
 
+def _f32_types():
+    import torch
+    return (torch.float32,)
+
+
+def _word_types():
+    """Tensor dtypes that hold the uint32 sign words (4-byte integers)."""
+    import torch
+    return tuple(t for t in (torch.int32, getattr(torch, "uint32", None)) if t is not None)
+
+
+def _buffer(t, name: str, dtypes: tuple, numel: int):
+    """A device buffer the library reads or writes `numel` 4-byte elements of:
+    contiguous, on the GPU, of one of `dtypes` and at least that large.  The
+    kernels write whole 4-byte words, so a narrower dtype with enough elements
+    would be overrun; it is rejected here, before any launch."""
+    _dev_tensor(t, name)
+    if t.dtype not in dtypes:
+        names = " or ".join(str(d) for d in dtypes)
+        raise TypeError(f"{name} must be {names}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    return t
+
+
 class Sketch:
     """An owned qjl_sketch handle (see qjl_make_sketch)."""
 
@@ -220,10 +245,8 @@ def quantize_keys(sk: Sketch, K, key_index_base: int = 0, norms_out=None, bits_o
         norms_out = torch.empty(n, dtype=torch.float32, device=K.device)
     if bits_out is None:
         bits_out = torch.empty((n, sk.m // 32), dtype=torch.int32, device=K.device)
-    _dev_tensor(norms_out, "norms_out")
-    _dev_tensor(bits_out, "bits_out")
-    if norms_out.numel() < n or bits_out.numel() < n * (sk.m // 32):
-        raise ValueError("output buffers too small")
+    _buffer(norms_out, "norms_out", _f32_types(), n)
+    _buffer(bits_out, "bits_out", _word_types(), n * (sk.m // 32))
     _check(load().qjl_quantize_keys(sk.handle, _ptr(K), _dtype_code(K), n, int(key_index_base),
                                     _ptr(norms_out), _ptr(bits_out), _stream(stream)),
            "qjl_quantize_keys")
@@ -243,11 +266,9 @@ def quantize_keys_into(sk: Sketch, K, n_groups: int, norms_cache, bits_cache,
     if n_groups <= 0 or K.shape[0] % n_groups != 0:
         raise ValueError("K's rows must split evenly into n_groups groups")
     kpg = K.shape[0] // n_groups
-    _dev_tensor(norms_cache, "norms_cache")
-    _dev_tensor(bits_cache, "bits_cache")
     rows = n_groups * int(cache_rows_per_group)
-    if norms_cache.numel() < rows or bits_cache.numel() < rows * (sk.m // 32):
-        raise ValueError("cache buffers smaller than n_groups * cache_rows_per_group rows")
+    _buffer(norms_cache, "norms_cache", _f32_types(), rows)
+    _buffer(bits_cache, "bits_cache", _word_types(), rows * (sk.m // 32))
     _check(load().qjl_quantize_keys_into(sk.handle, _ptr(K), _dtype_code(K), int(n_groups), kpg,
                                          int(cache_rows_per_group), int(first_row),
                                          int(key_index_base), _ptr(norms_cache),
@@ -265,9 +286,7 @@ def project_query(sk: Sketch, q, Sq_out=None, stream=None):
         raise ValueError(f"q has {q.shape[1]} columns, sketch d = {sk.d}")
     if Sq_out is None:
         Sq_out = torch.empty((n, sk.m), dtype=torch.float32, device=q.device)
-    _dev_tensor(Sq_out, "Sq_out")
-    if Sq_out.numel() < n * sk.m:
-        raise ValueError("Sq_out too small")
+    _buffer(Sq_out, "Sq_out", _f32_types(), n * sk.m)
     _check(load().qjl_project_query(sk.handle, _ptr(q), _dtype_code(q), n, _ptr(Sq_out),
                                     _stream(stream)), "qjl_project_query")
     return Sq_out
@@ -277,20 +296,12 @@ def score(sk: Sketch, Sq, bits, norms, n_groups: int, n_q: int, n_k: int, scores
           stream=None):
     """Estimated scores [n_groups, n_q, n_k] float32."""
     import torch
-    for t, nm in ((Sq, "Sq"), (bits, "bits"), (norms, "norms")):
-        _dev_tensor(t, nm)
-    if Sq.dtype != torch.float32 or norms.dtype != torch.float32:
-        raise TypeError("Sq and norms must be float32")
-    if bits.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
-        raise TypeError("bits must be int32 (uint32 words)")
-    if (Sq.numel() < n_groups * n_q * sk.m or bits.numel() < n_groups * n_k * (sk.m // 32)
-            or norms.numel() < n_groups * n_k):
-        raise ValueError("input buffers too small for the given counts")
+    _buffer(Sq, "Sq", _f32_types(), n_groups * n_q * sk.m)
+    _buffer(bits, "bits", _word_types(), n_groups * n_k * (sk.m // 32))
+    _buffer(norms, "norms", _f32_types(), n_groups * n_k)
     if scores_out is None:
         scores_out = torch.empty((n_groups, n_q, n_k), dtype=torch.float32, device=Sq.device)
-    _dev_tensor(scores_out, "scores_out")
-    if scores_out.numel() < n_groups * n_q * n_k:
-        raise ValueError("scores_out too small")
+    _buffer(scores_out, "scores_out", _f32_types(), n_groups * n_q * n_k)
     _check(load().qjl_score(sk.handle, _ptr(Sq), _ptr(bits), _ptr(norms), int(n_groups),
                             int(n_q), int(n_k), _ptr(scores_out), _stream(stream)),
            "qjl_score")
@@ -315,27 +326,21 @@ def decode_attention(sk: Sketch, Sq, bits, norms, V, n_groups: int, n_q: int, n_
     GPU tensor) is allocated here when not given.
     """
     import torch
-    for t, nm in ((Sq, "Sq"), (bits, "bits"), (norms, "norms"), (V, "V")):
-        _dev_tensor(t, nm)
-    if Sq.dtype != torch.float32 or norms.dtype != torch.float32:
-        raise TypeError("Sq and norms must be float32")
-    if bits.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
-        raise TypeError("bits must be int32 (uint32 words)")
+    _dev_tensor(V, "V")
     if V.dim() < 1:
         raise ValueError("V must have a last dimension d_v")
     d_v = int(V.shape[-1])
-    if (Sq.numel() < n_groups * n_q * sk.m or bits.numel() < n_groups * n_k * (sk.m // 32)
-            or norms.numel() < n_groups * n_k or V.numel() < n_groups * n_k * d_v):
-        raise ValueError("input buffers too small for the given counts")
+    _buffer(Sq, "Sq", _f32_types(), n_groups * n_q * sk.m)
+    _buffer(bits, "bits", _word_types(), n_groups * n_k * (sk.m // 32))
+    _buffer(norms, "norms", _f32_types(), n_groups * n_k)
+    _buffer(V, "V", (torch.float32, torch.bfloat16), n_groups * n_k * d_v)
     need = decode_attention_workspace_size(sk, n_groups, n_q, n_k, d_v)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Sq.device)
     _dev_tensor(workspace, "workspace")
     if out is None:
         out = torch.empty((n_groups, n_q, d_v), dtype=torch.float32, device=Sq.device)
-    _dev_tensor(out, "out")
-    if out.dtype != torch.float32 or out.numel() < n_groups * n_q * d_v:
-        raise ValueError("out must be float32 with n_groups * n_q * d_v elements")
+    _buffer(out, "out", _f32_types(), n_groups * n_q * d_v)
     nbytes = workspace.numel() * workspace.element_size()
     _check(load().qjl_decode_attention(sk.handle, _ptr(Sq), _ptr(bits), _ptr(norms), _ptr(V),
                                        _dtype_code(V), d_v, int(n_groups), int(n_q), int(n_k),
@@ -343,3 +348,4 @@ def decode_attention(sk: Sketch, Sq, bits, norms, V, n_groups: int, n_q: int, n_
                                        _ptr(out), _stream(stream)),
            "qjl_decode_attention")
     return out
+

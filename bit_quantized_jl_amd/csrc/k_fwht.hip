@@ -17,10 +17,10 @@
 // pre-scaled by 1/sqrt(d) on the host, so the kernel computes
 // H (Gs_b * (H (D_b x))[P_b]).
 //
-// These all-vector kernels serve projections, float32 keys, d < 128 and
-// buffers that are not 16-byte aligned; bfloat16 keys at d = 128 are
-// quantized by k_fqjl_mfma.hip, which applies the first stage on the matrix
-// cores (launch_fqjl routes them).
+// These all-vector kernels serve projections, float32 keys, d < 128,
+// d = 256 (fqjl256_kernel: four lanes per row) and buffers that are not
+// 16-byte aligned; bfloat16 keys at d = 128 are quantized by k_fqjl_mfma.hip,
+// which applies the first stage on the matrix cores (launch_fqjl routes them).
 #include "device_common.h"
 #include "fwht_common.h"
 
@@ -285,6 +285,127 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
   }
 }
 
+// d = 256 with four lanes per row (16 rows per wave).  Sylvester order puts
+// the quarter index in the top two bits of a coordinate, so H_256 = H_4 (x)
+// H_64: quarter s of H_256 z is H_64 (sum_t H_4[s][t] z_t), z_t the t-th 64
+// coordinates.  Lane quarter s (lanes 16 s .. 16 s + 15, one row each) holds
+// z_s; the H_4 mix is two butterfly stages across the quarters,
+// v_permlane16_swap of a value with itself handing every lane the values of
+// quarters s & ~1 and s | 1, v_permlane32_swap those of s & ~2 and s | 2.
+// Then each lane runs a 64-point transform on its own registers.  The
+// permutation goes through a 16 KB LDS tile (element c of row k at
+// 16 (c ^ (c >> 6)) + k, so the four quarters' writes land in distinct
+// banks); each lane gathers its own quarter of the permuted, Gaussian-scaled
+// row and the second transform repeats the first's pattern.  A row's
+// quarters are read by the four lanes that own it, so every register holds
+// 64 coordinates and the row is loaded once.
+template <typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM, bool MAPPED>
+__global__ __launch_bounds__(64) void fqjl256_kernel(
+    const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
+    const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
+    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    float *__restrict__ Y) {
+  constexpr int D = 256, H = 64;
+  __shared__ float lds[D * 16];
+  const int lane = threadIdx.x;
+  const int k = lane & 15, s = lane >> 4;
+  const float sg0 = (s & 1) ? -1.f : 1.f;  // H_4 sign of this quarter, bit 0
+  const float sg1 = (s & 2) ? -1.f : 1.f;  // and bit 1
+  const int W = m / 32;
+  // H_4 across the quarters, in place: t_s <- sum_u H_4[s][u] t_u.
+  auto h4_mix = [&](float (&t)[H]) {
+#pragma unroll
+    for (int c = 0; c < H; ++c) {
+      const uint32_t v = __float_as_uint(t[c]);
+      const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      const uint32_t x = __float_as_uint(fmaf(sg0, __uint_as_float(a[1]), __uint_as_float(a[0])));
+      const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      t[c] = fmaf(sg1, __uint_as_float(b[1]), __uint_as_float(b[0]));
+    }
+  };
+  for (int64_t r0 = (int64_t)blockIdx.x * 16; r0 < n; r0 += (int64_t)gridDim.x * 16) {
+    const int64_t row = r0 + k;
+    const bool valid = row < n;
+    const int64_t orow = MAPPED ? map_row(map, valid ? row : 0) : (valid ? row : 0);  // output row
+    const T *xr = X + (valid ? row : 0) * (int64_t)D + H * s;  // this lane's quarter
+    float x[H];
+    if constexpr (VEC) {
+      load_row_vec<H, T>(xr, valid, x);
+    } else {
+#pragma unroll
+      for (int c = 0; c < H; ++c) x[c] = valid ? load_as_f32(xr, c) : 0.f;
+    }
+    float nrm = 0.f;
+    if (!PROJECT) {
+      float ssq = 0.f;
+#pragma unroll
+      for (int c = 0; c < H; ++c) ssq = fmaf(x[c], x[c], ssq);
+      ssq += __shfl_xor(ssq, 16);
+      ssq += __shfl_xor(ssq, 32);
+      nrm = sqrtf(ssq);
+      if (valid && s == 0 && blockIdx.y == 0) norms[orow] = nrm;
+    }
+    // blocks b = blockIdx.y, blockIdx.y + gridDim.y, ...: a short call
+    // spreads its blocks over workgroups
+    for (int b = blockIdx.y; b < nb; b += gridDim.y) {
+      const uint32_t *ds = Dsign + b * D + H * s;
+      const int32_t *pb = P + b * D + H * s;
+      const float *gb = Gs + b * D + H * s;
+      float t[H];
+#pragma unroll
+      for (int c = 0; c < H; ++c) t[c] = __uint_as_float(__float_as_uint(x[c]) ^ ds[c]);
+      h4_mix(t);
+      fwht_reg<H>(t);
+      if constexpr (PERM) {
+#pragma unroll
+        for (int c = 0; c < H; ++c) {
+          const int e = H * s + c;
+          lds[((e ^ (e >> 6)) << 4) + k] = t[c];
+        }
+        // Gather in groups of 16 (as in fqjl128_kernel: keeps the compiler
+        // from hoisting every read and its address at once).
+#pragma unroll
+        for (int c = 0; c < H; ++c) {
+          if (c % 16 == 0) asm volatile("" ::: "memory");
+          const int e = pb[c];
+          t[c] = lds[((e ^ (e >> 6)) << 4) + k] * gb[c];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < H; ++c) t[c] *= gb[c];
+      }
+      h4_mix(t);
+      fwht_reg<H>(t);
+      const int j0 = b * D + H * s;  // sketch coordinate of t[0]
+      if (PROJECT) {
+        if (valid) {
+          float *yr = Y + row * (int64_t)m + j0;
+#pragma unroll
+          for (int c = 0; c < H; ++c) yr[c] = t[c];
+        }
+      } else {
+        if (DITHER) {
+          const float amp = rho * nrm;
+          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
+          const uint64_t st0 = dither_state(dkey, pair0);
+#pragma unroll
+          for (int c = 0; c < H; c += 2) {
+            float xc, xs;
+            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
+            t[c] += amp * xc;
+            t[c + 1] += amp * xs;
+          }
+        }
+        if (valid) {
+          uint32_t *br = bits + orow * (int64_t)W + j0 / 32;
+          br[0] = pack_nonneg(&t[0]);
+          br[1] = pack_nonneg(&t[32]);
+        }
+      }
+    }
+  }
+}
+
 // d = 8 or 16: a block is narrower than one 32-bit word, so the bits of
 // consecutive blocks share words.  These small sizes exist so the GPU chain
 // can be checked against explicit matrices; they run a plain per-lane loop
@@ -369,6 +490,28 @@ void launch_fqjl128(const T *X, const FqjlArgs &a, dim3 grid, hipStream_t st) {
                        a.norms, a.bits, a.Y);
 }
 
+template <typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
+void launch_fqjl256(const T *X, const FqjlArgs &a, dim3 grid, hipStream_t st) {
+  if (!PROJECT && a.map.per_group != 0)
+    hipLaunchKernelGGL((fqjl256_kernel<T, PROJECT, DITHER, VEC, PERM, true>), grid, dim3(64), 0,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+  else
+    hipLaunchKernelGGL((fqjl256_kernel<T, PROJECT, DITHER, VEC, PERM, false>), grid, dim3(64), 0,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       a.norms, a.bits, a.Y);
+}
+
+template <typename T, bool VEC>
+void launch_fqjl256_cases(const T *X, const FqjlArgs &a, bool proj, bool dith, bool perm,
+                          dim3 grid, hipStream_t st) {
+  if (!perm && proj) launch_fqjl256<T, true, false, VEC, false>(X, a, grid, st);
+  else if (!perm && dith) launch_fqjl256<T, false, true, VEC, false>(X, a, grid, st);
+  else if (proj) launch_fqjl256<T, true, false, VEC, true>(X, a, grid, st);
+  else if (dith) launch_fqjl256<T, false, true, VEC, true>(X, a, grid, st);
+  else launch_fqjl256<T, false, false, VEC, true>(X, a, grid, st);
+}
+
 template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
 void launch_fqjl_row(const T *X, const FqjlArgs &a, int grid, hipStream_t st) {
   if (!PROJECT && a.map.per_group != 0)
@@ -434,7 +577,18 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
       return hipGetLastError();
     }
   }
-  if constexpr (D >= 32) {
+  if constexpr (D == 256) {
+    const int64_t tiles4 = (n + 15) / 16;
+    const int grid4 = (int)(tiles4 < 32768 ? tiles4 : 32768);
+    // Few rows: one workgroup per (row tile, block), as for d = 128.
+    const dim3 g4(grid4, tiles4 * a.nb <= 4096 ? a.nb : 1);
+    if (((uintptr_t)X & 15) == 0)  // each quarter row is whole 16-byte vectors
+      launch_fqjl256_cases<T, true>(X, a, proj, dith, perm, g4, st);
+    else
+      launch_fqjl256_cases<T, false>(X, a, proj, dith, perm, g4, st);
+    return hipGetLastError();
+  }
+  if constexpr (D >= 32 && D <= 128) {
     if (((uintptr_t)X & 15) == 0)  // rows are whole 16-byte vectors
       launch_fqjl_rows<D, T, true>(X, a, proj, dith, perm, grid, st);
     else
@@ -457,6 +611,7 @@ hipError_t launch_fqjl_d(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
     case 32: return launch_fqjl_t<32>(sk, X, n, base, map, norms, bits, Y, st);
     case 64: return launch_fqjl_t<64>(sk, X, n, base, map, norms, bits, Y, st);
     case 128: return launch_fqjl_t<128>(sk, X, n, base, map, norms, bits, Y, st);
+    case 256: return launch_fqjl_t<256>(sk, X, n, base, map, norms, bits, Y, st);
   }
   return hipErrorInvalidValue;
 }

@@ -56,7 +56,7 @@ qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float r
   if (variant == QJL_VARIANT_DENSE) {
     if (d > QJL_MAX_D) return QJL_ERR_UNSUPPORTED;
   } else {
-    if (!is_pow2(d) || d < 8 || d > 128 || m % d != 0) return QJL_ERR_UNSUPPORTED;
+    if (!is_pow2(d) || d < 8 || d > 256 || m % d != 0) return QJL_ERR_UNSUPPORTED;
   }
   return QJL_OK;
 }

@@ -20,6 +20,9 @@ Tolerances:
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
+
 import numpy as np
 import torch
 
@@ -115,3 +118,84 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray, V: np.ndarray, dx: np.ndar
         i = np.unravel_index(np.argmax(err - tol), err.shape)
         raise AssertionError(f"attention mismatch at {i}: gpu {gpu[i]} ref {ref[i]} tol {tol[i]} "
                              f"({int((err > tol).sum())} of {err.size})")
+
+
+# ---------------------------------------------------------------- reporting
+# (config, coordinates compared, in-band sign differences) of the parity
+# checks that ran; the conftest's terminal summary prints one line per entry.
+INBAND_REPORT: list = []
+
+
+def report_inband(name: str, coords: int, inband: int) -> None:
+    INBAND_REPORT.append((name, int(coords), int(inband)))
+
+
+# ------------------------------------------------------------ whole outputs
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _one_blas_thread():
+    """A context in which numpy's BLAS runs single-threaded (the chunks are
+    already spread over a thread pool)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:  # threadpoolctl missing: run as is
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def oracle_check_all_rows(ref, K: torch.Tensor, dtype: str, gpu_bits: np.ndarray,
+                          gpu_norms: np.ndarray, key_index_base: int = 0, chunk: int = 8192):
+    """Every row of a quantized cache against the oracle.
+
+    The oracle quantizes K (a host tensor, [n, d]) chunk by chunk on a
+    thread pool; each chunk's bits and norms are compared with the GPU's
+    (check_bits / check_norms).  Returns (in-band sign differences, oracle
+    bits [n, m/32], oracle norms [n])."""
+    n = K.shape[0]
+    m = ref.m
+    rb_all = np.empty((n, m // 32), dtype=np.uint32)
+    rn_all = np.empty(n, dtype=np.float64)
+
+    def work(s):
+        e = min(n, s + chunk)
+        Kd = K[s:e].to(torch.float64).numpy()
+        rb, rn, mg, _ = oq.quantize(ref, Kd, dtype, key_index_base=key_index_base + s)
+        nb = check_bits(gpu_bits[s:e], rb, mg, m)
+        check_norms(gpu_norms[s:e], rn)
+        rb_all[s:e] = rb
+        rn_all[s:e] = rn
+        return nb
+
+    with _one_blas_thread(), cf.ThreadPoolExecutor(_workers()) as ex:
+        inband = sum(ex.map(work, range(0, n, chunk)))
+    return inband, rb_all, rn_all
+
+
+def oracle_check_all_scores(ref, q: torch.Tensor, dtype: str, gpu_Sq: np.ndarray,
+                            gpu_scores: np.ndarray, gpu_bits: np.ndarray, rb: np.ndarray,
+                            rn: np.ndarray, rho: float, G: int, nq: int, nk: int) -> None:
+    """Every group's scores against the oracle's, formed from the oracle's own
+    projection of the queries and its own bits and norms (rb, rn: all rows);
+    a sign that differs inside the band widens its scores' bound by its whole
+    effect (inband_slack).  The projections are checked diagnostically."""
+    m = ref.m
+    qd_all = q.to(torch.float64).numpy()
+
+    def work(g):
+        qd = qd_all[g * nq:(g + 1) * nq]
+        Sq_ref = oq.project(ref, qd, dtype)
+        check_projection(gpu_Sq[g * nq:(g + 1) * nq], Sq_ref, qd, m)
+        sl = slice(g * nk, (g + 1) * nk)
+        s_ref = oq.score(Sq_ref, rb[sl], rn[sl], m, rho, 1, nq, nk)
+        slack = inband_slack(gpu_bits[sl], rb[sl], Sq_ref, rn[sl], m, rho, 1, nq, nk)
+        check_scores(gpu_scores[g], s_ref[0], slack[0])
+
+    with _one_blas_thread(), cf.ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(work, range(G)))

@@ -57,7 +57,8 @@ def test_status_strings_and_version():
     ((0, 96, 192, 1, 0.0), 2),       # FQJL d not a power of two
     ((0, 128, 320, 1, 0.0), 2),      # FQJL m % d != 0
     ((0, 4, 32, 1, 0.0), 2),         # FQJL d < 8
-    ((0, 256, 512, 1, 0.0), 2),      # FQJL d > 128
+    ((0, 512, 1024, 1, 0.0), 2),     # FQJL d > 256
+    ((0, 256, 384, 1, 0.0), 2),      # FQJL m % d != 0 at d = 256
     ((0, 128, 256, 4, 0.0), 1),      # no variant 4
     ((0, 128, 256, 2, 0.0), 1),      # D-FQJL needs dither
     ((0, 128, 256, 3, 0.1), 1),      # P-FQJL has none
@@ -105,7 +106,8 @@ def test_host_dense_sketch_equals_oracle(seed, d, m):
 
 
 @pytest.mark.parametrize("variant", ["fqjl", "dfqjl", "pfqjl"])
-@pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (5, 8, 32), (9, 64, 192), (2, 128, 512)])
+@pytest.mark.parametrize("seed,d,m", [(0, 128, 256), (5, 8, 32), (9, 64, 192), (2, 128, 512),
+                                      (4, 256, 512)])
 def test_host_fqjl_params_equal_oracle(seed, d, m, variant):
     got = qj.generate_sketch_host(seed, d, m, variant)
     ref = osk.make_sketch(seed, d, m, variant, 0.1 if variant == "dfqjl" else 0.0)
@@ -128,3 +130,77 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises((ValueError, RuntimeError, qj.QJLError)):
         sk = _lib.Sketch(0, 0, 128, 256, "dense", 0.0)
         qj.quantize_keys(sk, torch.zeros(4, 128))
+
+
+class _DevStub:
+    """Stands in for a contiguous GPU tensor (shape and dtype only): the
+    binding's checks run on it without a GPU, and reaching a launch (which
+    reads data_ptr) fails the test."""
+
+    def __init__(self, shape, dtype):
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.is_cuda = True
+
+    def is_contiguous(self):
+        return True
+
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def data_ptr(self):
+        raise AssertionError("a launch was reached with a mistyped buffer")
+
+
+@pytest.mark.parametrize("bad", ["float16", "bfloat16", "int16", "float64", "uint8"])
+def test_binding_rejects_mistyped_buffers_before_launch(bad):
+    # A narrower dtype with enough elements would let the kernels write 4-byte
+    # words past the allocation; a wider one would be misread.  Every buffer
+    # the library reads or writes is checked before the call.
+    import types
+
+    import torch
+    bad = getattr(torch, bad)
+    n, d, m = 64, 128, 256
+    sk = types.SimpleNamespace(d=d, m=m, handle=None)
+    K = _DevStub((n, d), torch.bfloat16)
+    f32 = lambda *s: _DevStub(s, torch.float32)
+    words = lambda *s: _DevStub(s, torch.int32)
+    wrong = lambda *s: _DevStub((2 * int(np.prod(s)),), bad)   # twice the elements
+    calls = [
+        lambda: qj.quantize_keys(sk, K, norms_out=wrong(n), bits_out=words(n, m // 32)),
+        lambda: qj.quantize_keys(sk, K, norms_out=f32(n), bits_out=wrong(n, m // 32)),
+        lambda: qj.quantize_keys_into(sk, K, 1, wrong(n), words(n, m // 32), n, 0),
+        lambda: qj.quantize_keys_into(sk, K, 1, f32(n), wrong(n, m // 32), n, 0),
+        lambda: qj.project_query(sk, K, Sq_out=wrong(n, m)),
+        lambda: qj.score(sk, f32(1, m), words(n, m // 32), f32(n), 1, 1, n,
+                         scores_out=wrong(1, 1, n)),
+        lambda: qj.score(sk, wrong(1, m), words(n, m // 32), f32(n), 1, 1, n,
+                         scores_out=f32(1, 1, n)),
+        lambda: qj.score(sk, f32(1, m), wrong(n, m // 32), f32(n), 1, 1, n,
+                         scores_out=f32(1, 1, n)),
+        lambda: qj.score(sk, f32(1, m), words(n, m // 32), wrong(n), 1, 1, n,
+                         scores_out=f32(1, 1, n)),
+    ]
+    for call in calls:
+        with pytest.raises(TypeError):
+            call()
+
+
+def test_binding_rejects_short_buffers_before_launch():
+    import types
+
+    import torch
+    n, d, m = 64, 128, 256
+    sk = types.SimpleNamespace(d=d, m=m, handle=None)
+    K = _DevStub((n, d), torch.bfloat16)
+    with pytest.raises(ValueError):
+        qj.quantize_keys(sk, K, norms_out=_DevStub((n - 1,), torch.float32),
+                         bits_out=_DevStub((n, m // 32), torch.int32))
+    with pytest.raises(ValueError):
+        qj.score(sk, _DevStub((1, m), torch.float32), _DevStub((n, m // 32), torch.int32),
+                 _DevStub((n,), torch.float32), 1, 1, n,
+                 scores_out=_DevStub((n - 1,), torch.float32))

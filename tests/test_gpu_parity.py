@@ -15,7 +15,8 @@ import torch
 import bit_quantized_jl_amd as qj
 import workloads as wl
 from gpu_helpers import (bits_np, check_bits, check_norms, check_projection, check_scores,
-                         inband_slack, to_np_f64)
+                         inband_slack, oracle_check_all_rows, oracle_check_all_scores,
+                         report_inband, to_np_f64)
 from oracle import qjl as oq
 from oracle import sketch as osk
 
@@ -66,8 +67,9 @@ QUANT_CASES = [
 
 @pytest.mark.parametrize("w", QUANT_CASES, ids=lambda w: w.name)
 def test_quantize_workloads_scaled(w):
-    nband, *_ = run_quantize_case(w)
+    nband, K, *_ = run_quantize_case(w)
     note("in-band sign differences:", nband)
+    report_inband(f"{w.name} ({K.shape[0]} keys)", K.shape[0] * w.m, nband)
 
 
 SHAPES = (
@@ -82,6 +84,11 @@ SHAPES = (
                                                 (128, 512)) for dt in ("f32", "bf16")]
     + [("pfqjl", d, m, dt, 0.0) for (d, m) in ((16, 32), (64, 192), (128, 256))
        for dt in ("f32", "bf16")]
+    # d = 256: four lanes per row (one and two blocks per key)
+    + [("fqjl", 256, m, dt, rho) for m in (256, 512) for dt in ("f32", "bf16")
+       for rho in (0.0, 0.3)]
+    + [("dfqjl", 256, m, dt, 0.1) for m in (256, 512) for dt in ("f32", "bf16")]
+    + [("pfqjl", 256, 512, dt, 0.0) for dt in ("f32", "bf16")]
 )
 
 
@@ -96,7 +103,7 @@ def test_quantize_shapes(variant, d, m, dt, rho):
     ("dense", 64, 128, 0.0), ("dense", 64, 256, 0.0), ("dense", 64, 512, 0.0),
     ("dense", 128, 128, 0.0), ("dense", 128, 256, 0.0), ("dense", 128, 512, 0.0),
     ("fqjl", 128, 128, 0.0), ("fqjl", 128, 256, 0.2), ("fqjl", 128, 512, 0.0),
-    ("dfqjl", 128, 256, 0.1), ("dfqjl", 128, 512, 0.1)])
+    ("dfqjl", 128, 256, 0.1), ("dfqjl", 128, 512, 0.1), ("fqjl", 256, 512, 0.3)])
 def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     # More than 16384 bf16 keys (a ragged count): the persistent matrix-core
     # quantizers with the operand image staged in LDS, for every shape they
@@ -113,7 +120,9 @@ def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     ("dense", 128, 512, "bf16", 70), ("fqjl", 128, 256, "bf16", 37), ("fqjl", 8, 32, "f32", 37),
     ("fqjl", 64, 192, "f32", 37), ("fqjl", 128, 512, "bf16", 37), ("dfqjl", 128, 256, "bf16", 37),
     ("dfqjl", 16, 64, "f32", 37), ("pfqjl", 128, 256, "bf16", 37), ("fqjl", 128, 128, "bf16", 70),
-    ("fqjl", 128, 256, "bf16", 300), ("dfqjl", 128, 512, "bf16", 1)])
+    ("fqjl", 128, 256, "bf16", 300), ("dfqjl", 128, 512, "bf16", 1),
+    ("fqjl", 256, 512, "bf16", 37), ("fqjl", 256, 256, "f32", 37), ("dfqjl", 256, 256, "bf16", 37),
+    ("pfqjl", 256, 512, "f32", 37), ("fqjl", 256, 512, "bf16", 300)])
 def test_project_query(variant, d, m, dt, nq):
     note("project", variant, d, m, dt, nq)
     rho = 0.1 if variant == "dfqjl" else 0.0  # queries are never dithered
@@ -166,6 +175,8 @@ SENTINEL_NORM = -7.0
     ("fqjl", 128, 128, "bf16", 0.0, 9, 2, 20, 5),         # one block: the persistent kernel
     ("dense", 128, 256, "bf16", 0.0, 2, 9000, 9100, 50),  # > 16384 keys: persistent kernels
     ("fqjl", 128, 256, "bf16", 0.1, 2, 9000, 9100, 50),
+    ("fqjl", 256, 512, "bf16", 0.1, 5, 3, 10, 4),         # four lanes per row
+    ("dfqjl", 256, 256, "f32", 0.2, 3, 20, 33, 13),
     ("fqjl", 64, 192, "f32", 0.2, 5, 17, 17, 0),          # one row per lane
     ("fqjl", 16, 64, "f32", 0.0, 3, 5, 12, 2)])           # narrow blocks
 def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
@@ -217,6 +228,32 @@ def test_bits_buffer_alignment_paths(variant, rho):
     rb, rn, mg, _ = oq.quantize(ref, to_np_f64(K), "bf16", key_index_base=5)
     check_bits(bits_np(bits.contiguous()), rb, mg, m)
     check_norms(to_np_f64(norms), rn)
+    sk.close()
+
+
+@pytest.mark.parametrize("variant,dt,rho", [("fqjl", "bf16", 0.0), ("fqjl", "f32", 0.3),
+                                            ("dfqjl", "bf16", 0.1)])
+def test_fqjl256_unaligned_keys(variant, dt, rho):
+    # d = 256 keys one element past a 16-byte boundary: the four-lanes-per-row
+    # kernel with element loads instead of 16-byte vectors; same oracle bar.
+    note("fqjl d=256 unaligned keys", variant, dt, rho)
+    d, m, n = 256, 512, 301
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    K = (torch.randn(n, d, generator=torch.Generator().manual_seed(17)) * 0.7).to(tdt)
+    flat = torch.empty(n * d + 1, dtype=tdt, device=DEV)
+    Ku = flat[1:].view(n, d)
+    Ku.copy_(K.to(DEV))
+    assert Ku.data_ptr() % 16 != 0
+    sk = qj.make_sketch(13, d, m, variant, rho)
+    norms, bits = qj.quantize_keys(sk, Ku, key_index_base=40)
+    Sq = qj.project_query(sk, Ku)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(13, d, m, variant, rho)
+    Kd = to_np_f64(K)
+    rb, rn, mg, _ = oq.quantize(ref, Kd, dt, key_index_base=40)
+    check_bits(bits_np(bits), rb, mg, m)
+    check_norms(to_np_f64(norms), rn)
+    check_projection(to_np_f64(Sq), oq.project(ref, Kd, dt), Kd, m)
     sk.close()
 
 
@@ -292,7 +329,8 @@ def test_quantize_into_cache_errors():
 
 @pytest.mark.parametrize("variant,d,m", [("dense", 128, 256), ("dense", 64, 512),
                                          ("dense", 128, 128), ("fqjl", 128, 256),
-                                         ("fqjl", 128, 512), ("pfqjl", 128, 128)])
+                                         ("fqjl", 128, 512), ("pfqjl", 128, 128),
+                                         ("fqjl", 256, 512), ("pfqjl", 256, 256)])
 def test_projected_keys_reproduce_their_bits(variant, d, m):
     # Projecting bf16 keys as queries applies the same sketch as quantizing
     # them (dense: the same bf16 S; FQJL: the same +-1 first stage, float32
@@ -500,77 +538,55 @@ def test_dither_key_index_base_appends():
 
 
 # ---------------------------------------------------------------- full size
-def _sample_rows(n, count, seed):
-    rs = np.random.default_rng(seed)
-    idx = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
-                                    rs.choice(n, count, replace=False)]))
-    return idx
-
-
-def full_size_quantize(w: wl.Workload, sample=3000):
+# The full-size workloads run in the launch configuration the benchmark
+# times, and every output is compared with the oracle: all rows' bits and
+# norms, every group's scores (the oracle runs chunk by chunk on a thread
+# pool of the host's cores).
+def full_size_quantize(w: wl.Workload):
     note("full quantize", w.name)
     K = wl.make_keys(w, DEV)
     sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
     norms, bits = qj.quantize_keys(sk, K)
     torch.cuda.synchronize()
     ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
-    idx = _sample_rows(K.shape[0], sample, 1)
-    it = torch.from_numpy(idx).to(DEV)
-    Kd = to_np_f64(K[it])
-    rb, rn, mg, _ = oq.quantize(ref, Kd, w.dtype, key_index=idx)
-    nband = check_bits(bits_np(bits[it]), rb, mg, w.m)
-    check_norms(to_np_f64(norms[it]), rn)
-    note("in-band sign differences on sample:", nband)
-    return sk, K, norms, bits
+    Kh = K.cpu()
+    nband, rb, rn = oracle_check_all_rows(ref, Kh, w.dtype, bits_np(bits), to_np_f64(norms))
+    note("in-band sign differences, all rows:", nband)
+    report_inband(f"{w.name} (all {w.n_keys} keys)", w.n_keys * w.m, nband)
+    return sk, ref, norms, bits, rb, rn
 
 
-def full_size_score(w: wl.Workload, sk, K, norms, bits, groups_checked=4):
+def full_size_score(w: wl.Workload, sk, ref, norms, bits, rb, rn):
+    note("full score", w.name)
     q = wl.make_queries(w, DEV)
     Sq = qj.project_query(sk, q)
+    # the GPU scores its own bits and norms; the oracle scores its own
     out = qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k)
     torch.cuda.synchronize()
-    ref = oracle_sketch(w.seed, w.d, w.m, w.variant, w.rho)
-    rs = np.random.default_rng(2)
-    gs = sorted(set([0, w.groups - 1] + rs.choice(w.groups, groups_checked, replace=False).tolist()))
-    for g in gs:
-        note("full score group", g)
-        sl = slice(g * w.n_k, (g + 1) * w.n_k)
-        qd = to_np_f64(q[g * w.n_q:(g + 1) * w.n_q])
-        Sq_ref = oq.project(ref, qd, w.dtype)
-        check_projection(to_np_f64(Sq[g * w.n_q:(g + 1) * w.n_q]), Sq_ref, qd, w.m)
-        # the oracle quantizes this group's keys itself
-        rb, rn, mg, _ = oq.quantize(ref, to_np_f64(K[sl]), w.dtype,
-                                    key_index=np.arange(sl.start, sl.stop))
-        gb = bits_np(bits[sl])
-        check_bits(gb, rb, mg, w.m)
-        s_ref = oq.score(Sq_ref, rb, rn, w.m, w.rho, 1, w.n_q, w.n_k)
-        slack = inband_slack(gb, rb, Sq_ref, rn, w.m, w.rho, 1, w.n_q, w.n_k)
-        check_scores(to_np_f64(out[g]), s_ref[0], slack[0])
-    # every group: finite and zero exactly where the norm is zero
     assert torch.isfinite(out).all()
+    oracle_check_all_scores(ref, q.cpu(), w.dtype, to_np_f64(Sq), to_np_f64(out), bits_np(bits),
+                            rb, rn, w.rho, w.groups, w.n_q, w.n_k)
+
+
+def _full(w: wl.Workload, scores: bool):
+    sk, ref, norms, bits, rb, rn = full_size_quantize(w)
+    if scores:
+        full_size_score(w, sk, ref, norms, bits, rb, rn)
+    sk.close()
 
 
 def test_full_size_decode_7b():
-    w = wl.DECODE_7B
-    sk, K, norms, bits = full_size_quantize(w)
-    full_size_score(w, sk, K, norms, bits)
-    sk.close()
+    _full(wl.DECODE_7B, scores=True)
 
 
 def test_full_size_long_context():
-    w = wl.LONG_CTX
-    sk, K, norms, bits = full_size_quantize(w, sample=2000)
-    full_size_score(w, sk, K, norms, bits, groups_checked=2)
-    sk.close()
+    _full(wl.LONG_CTX, scores=True)
 
 
 def test_full_size_prefill():
-    sk, *_ = full_size_quantize(wl.PREFILL)
-    sk.close()
+    _full(wl.PREFILL, scores=False)
 
 
 @pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER, wl.DFQJL_7B], ids=lambda w: w.name)
 def test_full_size_fqjl(w):
-    sk, K, norms, bits = full_size_quantize(w, sample=2000)
-    full_size_score(w, sk, K, norms, bits, groups_checked=2)
-    sk.close()
+    _full(w, scores=True)
