@@ -12,10 +12,12 @@ from ._lib import (  # noqa: F401
     ERR_OUT_OF_MEMORY,
     ERR_UNSUPPORTED,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     OK,
     QJLError,
     Sketch,
     decode_attention,
+    decode_attention_noalloc,
     decode_attention_workspace_size,
     destroy_sketch,
     generate_sketch_host,

@@ -57,6 +57,8 @@ def _declare(lib: ctypes.CDLL) -> None:
                                                           c.POINTER(c.c_size_t)]),
         "qjl_decode_attention": (c.c_int, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64, f32,
                                            vp, c.c_size_t, vp, vp]),
+        "qjl_decode_attention_noalloc": (c.c_int, [vp, vp, vp, vp, vp, i32, i32, i64, i64, i64,
+                                                   f32, vp, vp]),
         "qjl_status_string": (c.c_char_p, [c.c_int]),
         "qjl_version": (c.c_char_p, []),
     }
@@ -349,3 +351,28 @@ def decode_attention(sk: Sketch, Sq, bits, norms, V, n_groups: int, n_q: int, n_
            "qjl_decode_attention")
     return out
 
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # QJL_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(sk: Sketch, Sq, bits, norms, V, n_groups: int, n_q: int, n_k: int,
+                             softmax_scale: float, out, stream=None):
+    """decode_attention with the library's per-GPU scratch as its workspace:
+    no allocation anywhere in the call (the caller passes `out`, float32
+    [n_groups, n_q, d_v]).  Calls that overlap on one GPU race on the scratch."""
+    import torch
+    _dev_tensor(V, "V")
+    if V.dim() < 1:
+        raise ValueError("V must have a last dimension d_v")
+    d_v = int(V.shape[-1])
+    _buffer(Sq, "Sq", _f32_types(), n_groups * n_q * sk.m)
+    _buffer(bits, "bits", _word_types(), n_groups * n_k * (sk.m // 32))
+    _buffer(norms, "norms", _f32_types(), n_groups * n_k)
+    _buffer(V, "V", (torch.float32, torch.bfloat16), n_groups * n_k * d_v)
+    _buffer(out, "out", _f32_types(), n_groups * n_q * d_v)
+    _check(load().qjl_decode_attention_noalloc(sk.handle, _ptr(Sq), _ptr(bits), _ptr(norms),
+                                               _ptr(V), _dtype_code(V), d_v, int(n_groups),
+                                               int(n_q), int(n_k), float(softmax_scale),
+                                               _ptr(out), _stream(stream)),
+           "qjl_decode_attention_noalloc")
+    return out

@@ -344,24 +344,50 @@ qjl_status qjl_decode_attention(const qjl_sketch *sk, const float *Sq, const uin
                                 int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
                                 float softmax_scale, void *workspace, size_t workspace_bytes,
                                 float *out, void *stream) {
+  bool noop = false;
+  qjl_status st = attention_check_args(sk, Sq, bits, norms, V, v_dtype, d_v, n_groups,
+                                       n_q_per_group, n_k_per_group, softmax_scale, out, &noop);
+  if (st != QJL_OK || noop) return st;
+  if (!workspace || !aligned(workspace, 16)) return QJL_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes <
+      attention_workspace_bytes(sk, n_groups, n_q_per_group, n_k_per_group, d_v))
+    return QJL_ERR_INVALID_ARGUMENT;
+  return attention_run(sk, Sq, bits, norms, V, v_dtype, d_v, n_groups, n_q_per_group,
+                       n_k_per_group, softmax_scale, static_cast<float *>(workspace), out,
+                       stream);
+}
+
+}  // extern "C"
+
+namespace qjl {
+
+qjl_status attention_check_args(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                                int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                                float softmax_scale, const float *out, bool *noop) {
+  *noop = false;
   if (!sk || n_groups < 0 || n_q_per_group < 0 || n_k_per_group < 0 || d_v < 1)
     return QJL_ERR_INVALID_ARGUMENT;
   if (v_dtype != QJL_DTYPE_F32 && v_dtype != QJL_DTYPE_BF16) return QJL_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(softmax_scale)) return QJL_ERR_INVALID_ARGUMENT;
-  if (n_groups == 0 || n_q_per_group == 0) return QJL_OK;
+  if (n_groups == 0 || n_q_per_group == 0) {
+    *noop = true;
+    return QJL_OK;
+  }
   if (n_k_per_group == 0) return QJL_ERR_INVALID_ARGUMENT;  // softmax over no keys
-  if (!Sq || !bits || !norms || !V || !workspace || !out) return QJL_ERR_INVALID_ARGUMENT;
+  if (!Sq || !bits || !norms || !V || !out) return QJL_ERR_INVALID_ARGUMENT;
   const size_t vsz = v_dtype == QJL_DTYPE_F32 ? 4 : 2;
   if (!aligned(Sq, 4) || !aligned(bits, 4) || !aligned(norms, 4) || !aligned(V, vsz) ||
-      !aligned(out, 4) || !aligned(workspace, 16))
+      !aligned(out, 4))
     return QJL_ERR_INVALID_ARGUMENT;
-  qjl_status st = check_device(sk);
-  if (st != QJL_OK) return st;
-  if (workspace_bytes <
-      attention_workspace_bytes(sk, n_groups, n_q_per_group, n_k_per_group, d_v))
-    return QJL_ERR_INVALID_ARGUMENT;
+  return check_device(sk);
+}
+
+qjl_status attention_run(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                         const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                         int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                         float softmax_scale, float *ws, float *out, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float *ws = static_cast<float *>(workspace);
   if (attention_fused_supported(sk, bits, V, v_dtype, d_v, n_k_per_group))
     return from_hip(launch_attention_fused(sk, Sq, bits, norms, V, n_groups, n_q_per_group,
                                            n_k_per_group, softmax_scale, ws, out, s));
@@ -371,9 +397,6 @@ qjl_status qjl_decode_attention(const qjl_sketch *sk, const float *Sq, const uin
                                            n_k_per_group, softmax_scale, out, s));
 }
 
-}  // extern "C"
-
-namespace qjl {
 float estimator_scale(int m, float rho) {
   const double c = std::sqrt(M_PI / 2.0) * std::sqrt(1.0 + (double)rho * (double)rho) / (double)m;
   return (float)c;

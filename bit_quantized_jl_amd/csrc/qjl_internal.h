@@ -131,4 +131,18 @@ hipError_t launch_attention_softmax(const float *scores, const void *V, int v_dt
 // Host-computed data the score kernels take per launch.
 float estimator_scale(int m, float rho);
 
+// qjl_decode_attention's argument checks other than the workspace (pointers,
+// counts, dtype, alignment, the sketch's device), shared with the
+// allocation-free variant; *noop is set when there is nothing to compute.
+qjl_status attention_check_args(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                                const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                                int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                                float softmax_scale, const float *out, bool *noop);
+// Enqueue the decode attention with `ws` as its workspace (at least
+// attention_workspace_bytes, 16-byte aligned; checked by the caller).
+qjl_status attention_run(const qjl_sketch *sk, const float *Sq, const uint32_t *bits,
+                         const float *norms, const void *V, int32_t v_dtype, int32_t d_v,
+                         int64_t n_groups, int64_t n_q_per_group, int64_t n_k_per_group,
+                         float softmax_scale, float *ws, float *out, void *stream);
+
 }  // namespace qjl

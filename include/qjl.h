@@ -263,6 +263,32 @@ qjl_status qjl_decode_attention(const qjl_sketch *sk, const float *Sq, const uin
                                 float softmax_scale, void *workspace, size_t workspace_bytes,
                                 float *out, void *stream);
 
+/* Bytes of device scratch the allocation-free decode attention may use on
+ * each GPU (32 MiB): calls whose workspace (qjl_decode_attention_workspace_size)
+ * would exceed it are rejected. */
+#define QJL_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * qjl_decode_attention without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus the workspace), result and errors as
+ * qjl_decode_attention; the workspace is a library-owned device array of
+ * QJL_NOALLOC_SCRATCH_BYTES per GPU that stays allocated until the process
+ * ends.  The call allocates nothing (no hipMalloc, no library allocator)
+ * and only enqueues kernels on `stream`.  Every GPU has one such array and
+ * each call uses all of it that it needs: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ * Errors: as qjl_decode_attention; a shape whose workspace would exceed
+ * QJL_NOALLOC_SCRATCH_BYTES -> UNSUPPORTED (use qjl_decode_attention with
+ * a caller workspace); the scratch not found on the device -> DEVICE.
+ */
+qjl_status qjl_decode_attention_noalloc(const qjl_sketch *sk, const float *Sq,
+                                        const uint32_t *bits, const float *norms, const void *V,
+                                        int32_t v_dtype, int32_t d_v, int64_t n_groups,
+                                        int64_t n_q_per_group, int64_t n_k_per_group,
+                                        float softmax_scale, float *out, void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *qjl_status_string(qjl_status s);
 
