@@ -37,6 +37,7 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "quantize_dense_llama7b_decode_pmc.txt")
 QUANT_KERNEL_SRC = os.path.join(ROOT, "bit_quantized_jl_amd", "csrc", "k_quantize_mfma.hip")
+PROBE_LIB = os.path.join(ROOT, "bit_quantized_jl_amd", "libqjl_probe.so")
 
 
 def parse():
@@ -54,6 +55,9 @@ def parse():
     p.add_argument("--only", choices=["quantize", "fqjl", "fqjl_dither", "score", "attention"],
                    help="run only a few launches of one kernel on its 7B-decode-shape workload "
                         "(for hardware-counter passes)")
+    p.add_argument("--tu-hash", metavar="SOURCE",
+                   help="print the hash of a kernel source and every header it includes "
+                        "(the value recorded in profiles/*_pmc.txt) and exit")
     p.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
                    help="run only the dense quantize launch back to back for SECONDS while "
                         "sampling socket power and graphics clocks with amd-smi")
@@ -131,14 +135,43 @@ def sustain(seconds: float):
                       "gfx_clock_samples": len(clocks)}), flush=True)
 
 
-def kernel_src_hash() -> str:
-    with open(QUANT_KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def translation_unit_files(src: str) -> list:
+    """A source file and every header it includes with #include "...",
+    recursively (each once, in the order first reached)."""
+    import re
+    seen, order = set(), []
+
+    def visit(path):
+        path = os.path.normpath(path)
+        if path in seen or not os.path.exists(path):
+            return
+        seen.add(path)
+        order.append(path)
+        with open(path) as f:
+            for inc in re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), flags=re.M):
+                visit(os.path.join(os.path.dirname(path), inc))
+
+    visit(src)
+    return order
+
+
+def kernel_tu_hash(src: str = QUANT_KERNEL_SRC) -> str:
+    """sha256 (first 16 hex digits) over a kernel's whole translation unit:
+    the source and every header it includes, each as (path relative to the
+    repository, contents), so a change to any of them changes the hash."""
+    h = hashlib.sha256()
+    for path in translation_unit_files(src):
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
     """HBM bytes per quantize launch from the committed rocprofv3 PMC summary,
-    or None when absent or taken on another version of the kernel source."""
+    or None when absent or taken on another version of the kernel's
+    translation unit (its source or any header it includes)."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
@@ -146,7 +179,7 @@ def read_traffic():
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_src_hash():
+    if vals.get("kernel_tu_sha256_16") != kernel_tu_hash():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -154,9 +187,11 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(w, seconds: float):
-    """The float64 oracle on whole (batch, head) groups of the same step until
-    about `seconds` of CPU time; throughput in the metric's unit (GB/s)."""
+def cpu_baseline(w, K_dev, seconds: float):
+    """The float64 oracle on the (batch, head) groups of the same step, one
+    group after another (group g = its 8192 cached keys, copied from the
+    GPU, and its query), until about `seconds` of CPU time; throughput in the
+    metric's unit (GB/s)."""
     import numpy as np
     import torch
 
@@ -171,14 +206,15 @@ def cpu_baseline(w, seconds: float):
         blas_threads = 1
     cores = len(os.sched_getaffinity(0))
     sk = osk.make_dense(w.seed, w.d, w.m)
-    one = w.scaled(batch=1, heads=1)
-    K = wl.make_keys(one, "cpu").double().numpy()   # one group's keys (same recipe)
-    q = wl.make_queries(one, "cpu").double().numpy()
+    Kh = K_dev.cpu()                                # the step's cache, on the host
+    q = wl.make_queries(w, "cpu").double().numpy()  # the step's queries (same recipe)
     t0 = time.perf_counter()
     groups = 0
     while True:
-        bits, norms, _, _ = oq.quantize(sk, K, w.dtype)
-        Sq = oq.project(sk, q, w.dtype)
+        g = groups
+        K = Kh[g * w.n_k:(g + 1) * w.n_k].double().numpy()
+        bits, norms, _, _ = oq.quantize(sk, K, w.dtype, key_index_base=g * w.n_k)
+        Sq = oq.project(sk, q[g * w.n_q:(g + 1) * w.n_q], w.dtype)
         oq.score(Sq, bits, norms, w.m, 0.0, 1, w.n_q, w.n_k)
         groups += 1
         el = time.perf_counter() - t0
@@ -188,8 +224,9 @@ def cpu_baseline(w, seconds: float):
     return {"value": per_group_bytes * groups / el / 1e9, "unit": "GB/s",
             "cores": int(min(cores, blas_threads)),
             "host_cores": cores, "blas_threads": blas_threads, "kind": "oracle",
-            "sample": f"{groups} of {w.groups} (batch, head) groups of the same step "
-                      f"({groups * w.n_k} keys: quantize + project + score, float64 numpy), "
+            "sample": f"groups 0..{groups - 1} ({groups} of {w.groups} distinct (batch, head) "
+                      f"groups of the same step: {groups * w.n_k} cached keys copied from the "
+                      f"GPU and their queries; quantize + project + score, float64 numpy), "
                       f"{el:.1f} s"}
 
 
@@ -322,6 +359,66 @@ def copy_peak_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
     del src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes / best / 1e9
+
+
+def read_ceiling(torch, nbytes: int, n_sets: int, iters: int = 40):
+    """Measured read-bandwidth ceiling for a kernel that streams `nbytes`:
+    plain 16-byte-vector read kernels (libqjl_probe.so: chunked and
+    grid-stride patterns, 2/4/8 loads in flight per lane, 1/2/4 workgroups of
+    256 lanes per compute unit) over `n_sets` distinct buffers of that size
+    in rotation (as the score timing rotates its inputs past the 256 MB
+    Infinity Cache), timed like the kernels: mean of per-call HIP-event
+    times.  Returns the best configuration's rate."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.qjl_probe_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    n16 = (nbytes + 15) // 16
+    bufs = [torch.full((n16 * 4,), 1.0, dtype=torch.float32, device="cuda:0")
+            for _ in range(n_sets)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(4 * cus * 256, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    best = None
+    per_pattern = {}
+    for pattern in (0, 1):
+        for unroll in (2, 4, 8):
+            for wpc in (1, 2, 4):
+                grid = cus * wpc
+
+                def call(i):
+                    rc = fn(bufs[i % n_sets].data_ptr(), n16 * 16, pattern, unroll, grid,
+                            sink.data_ptr(), st.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"qjl_probe_read failed ({rc})")
+
+                for i in range(2 * n_sets):
+                    call(i)
+                torch.cuda.synchronize()
+                evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
+                for i in range(iters):
+                    evs[i][0].record(st)
+                    call(i)
+                    evs[i][1].record(st)
+                torch.cuda.synchronize()
+                mean = sum(a.seconds_to(b) for a, b in evs) / iters
+                key = "chunked" if pattern == 0 else "grid-stride"
+                per_pattern[key] = min(per_pattern.get(key, mean), mean)
+                if best is None or mean < best["mean_s"]:
+                    best = {"mean_s": mean, "GBps": n16 * 16 / mean / 1e9,
+                            "pattern": "chunked" if pattern == 0 else "grid-stride",
+                            "loads_in_flight_per_lane": unroll, "workgroups_per_cu": wpc}
+    del bufs, sink
+    torch.cuda.empty_cache()
+    best["bytes"] = n16 * 16
+    best["rotation"] = f"{n_sets} buffers"
+    best["best_GBps_by_pattern"] = {k: n16 * 16 / v / 1e9 for k, v in per_pattern.items()}
+    best["frac_hbm"] = best["GBps"] / HBM_PEAK_GBPS
+    return best
 
 
 def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
@@ -537,6 +634,9 @@ def run_only(kind: str):
 
 def main():
     args = parse()
+    if args.tu_hash:
+        print(kernel_tu_hash(os.path.abspath(args.tu_hash)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the kernels work on one GPU's shard; see the sharding note in the design).",
@@ -625,6 +725,10 @@ def main():
         "metric": METRIC,
         "value": step_bytes(w) / per_step / 1e9,
         "unit": "GB/s",
+        "value_is": "algorithmic bytes of one whole step (quantize 2,097,152 keys + project "
+                    "256 queries + score 256 x 8192 pairs: "
+                    f"{step_bytes(w):.0f} B) / its time, K steps back to back; the score "
+                    "kernel's own GB/s and fraction of HBM are in score_decode7b",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -657,13 +761,23 @@ def main():
         sb = score_bytes(w)
         s_mean, s_med, s_p10, s_p90 = time_score_rotating(qj, torch, w, sk, n_sets=4, iters=100)
         _, sw_med, _, _ = time_score_rotating(qj, torch, w, sk, n_sets=1, iters=100)
+        rc84 = read_ceiling(torch, int(sb), n_sets=4)
+        rc302 = read_ceiling(torch, int(score_bytes(wl.LONG_CTX)), n_sets=2)
+        rc612 = read_ceiling(torch, int(qbytes), n_sets=2)
+        result["read_ceiling"] = {"score_decode7b_bytes": rc84, "score_long_context_bytes": rc302,
+                                  "quantize_bytes": rc612}
+        if rc612:
+            result["roofline"]["frac_read_ceiling"] = achieved / rc612["GBps"]
         result["score_decode7b"] = {"GBps": sb / s_mean / 1e9, "frac_hbm": sb / s_mean / 1e9 / HBM_PEAK_GBPS,
+                                    "frac_read_ceiling": (sb / s_mean / 1e9 / rc84["GBps"]
+                                                          if rc84 else None),
                                     "frac_copy_peak": sb / s_mean / 1e9 / copy_gbps,
                                     "scores_per_s": w.groups * w.n_q * w.n_k / s_mean,
                                     "mean_s": s_mean, "median_s": s_med, "p10_s": s_p10,
                                     "p90_s": s_p90, "bytes": sb,
                                     "rotation": "4 sets x 75.8 MB",
                                     "warm_median_s": sw_med, "warm_GBps": sb / sw_med / 1e9}
+        K_host = K.cpu() if not args.no_cpu_baseline else None
         del K
         torch.cuda.empty_cache()
         wl2 = wl.LONG_CTX
@@ -673,6 +787,8 @@ def main():
                                                               iters=100)
         result["score_long_context"] = {"workload": wl2.name, "GBps": sb2 / s2_mean / 1e9,
                                         "frac_hbm": sb2 / s2_mean / 1e9 / HBM_PEAK_GBPS,
+                                        "frac_read_ceiling": (sb2 / s2_mean / 1e9 / rc302["GBps"]
+                                                              if rc302 else None),
                                         "frac_copy_peak": sb2 / s2_mean / 1e9 / copy_gbps,
                                         "scores_per_s": wl2.groups * wl2.n_k / s2_mean,
                                         "mean_s": s2_mean, "median_s": s2_med,
@@ -707,7 +823,9 @@ def main():
                             "timing": "10 launches back to back"}
         result["decode_time"] = decode_time_extras(qj, torch, w, sk)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if args.skip_extras:
+            K_host = K.cpu()
+        result["cpu_baseline"] = cpu_baseline(w, K_host, args.cpu_seconds)
     sk.close()
     print(json.dumps(result), flush=True)
 

@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqjl.so")
+PROBE_LIB = os.path.join(HERE, "libqjl_probe.so")
 ARCH = os.environ.get("QJL_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [
@@ -41,7 +42,7 @@ def sources() -> list[str]:
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD, os.path.relpath(src, CSRC).replace(os.sep, "_") + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [_hipcc(), *COMMON, *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,20 +51,33 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def probe_sources() -> list[str]:
+    d = os.path.join(CSRC, "probe")
+    return sorted(os.path.join(d, f) for f in os.listdir(d) if f.endswith(".hip"))
+
+
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Build libqjl.so (the library) and libqjl_probe.so (the benchmark's
+    plain read kernels, kept out of the library)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    psrcs = probe_sources()
+    workers = min(len(srcs) + len(psrcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, srcs + psrcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 

@@ -7,12 +7,6 @@
 
 #include "qjl_internal.h"
 
-namespace qjl {
-void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out);
-bool fqjl_mfma_image_shape(int d, int m);
-void build_fqjl_mfma_image(const HostSketch &hs, uint16_t *out);
-}
-
 using namespace qjl;
 
 namespace {
@@ -40,6 +34,7 @@ const char *qjl_status_string(qjl_status s) {
     case QJL_ERR_UNSUPPORTED: return "QJL_ERR_UNSUPPORTED";
     case QJL_ERR_OUT_OF_MEMORY: return "QJL_ERR_OUT_OF_MEMORY";
     case QJL_ERR_DEVICE: return "QJL_ERR_DEVICE";
+    default: break;
   }
   return "QJL_ERR_UNKNOWN";
 }

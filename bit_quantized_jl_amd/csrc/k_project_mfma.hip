@@ -1,6 +1,6 @@
 // Dense query projection Sq = q S^T for bfloat16 queries on the gfx950
-// matrix cores: the QJL abstract's "standard JL transform without
-// quantization" applied to the query.
+// matrix cores: the query's side of the QJL abstract, projected by the same
+// JL matrix as the keys and left unquantized.
 //
 // The quantizer's contraction without the sign, on the same operand image of
 // S (read from global memory: a call projects few rows, so staging S in LDS

@@ -3,8 +3,8 @@
 // Computes, for bfloat16 keys, Y = K S^T with v_mfma_f32_32x32x16_bf16
 // (float32 accumulation; bf16 x bf16 products are exact), and fuses in
 // registers: the sign test, packing of the signs into 32-bit words, and the
-// key norm ||k||.  This is the QJL abstract's "JL transform followed by
-// sign-bit quantization" with a dense Gaussian S.
+// key norm ||k||.  This is the key side of the QJL abstract (a JL projection
+// whose coordinates are reduced to their signs) with a dense Gaussian S.
 //
 // Tiling.  A workgroup keeps the whole bf16 sketch in LDS (m*d*2 bytes: 64 KB
 // at d=128, m=256) and its waves stream keys.  S is the MFMA A operand (rows
@@ -46,24 +46,6 @@ namespace qjl {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
-// Host: write S in the operand order of mfma_image.h.
-void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out) {
-  if (d % 16 != 0 || m % 64 != 0) return;  // the MFMA path's shapes; image unused otherwise
-  const int T = d / 16, W = m / 32;
-  for (int tau = 0; tau < m / 32; ++tau) {
-    const int p = tau >> 1, s = tau & 1;
-    for (int t = 0; t < T; ++t)
-      for (int l = 0; l < 64; ++l) {
-        const int r = l & 31, hh = l >> 5;
-        const int a = r >> 3, h = (r >> 2) & 1, b = r & 3;
-        const int j = 32 * (p + h * (W / 2)) + 16 * s + 4 * a + b;
-        for (int e = 0; e < 8; ++e)
-          out[(((size_t)tau * T + t) * 64 + l) * 8 + e] =
-              S16[(size_t)j * d + 8 * qm_chunk(hh, t) + e];
-      }
-  }
-}
 
 namespace {
 

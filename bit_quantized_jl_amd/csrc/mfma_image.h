@@ -3,6 +3,7 @@
 // of S with bf16 vectors loaded the same way, so they apply the same sums).
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qjl {

@@ -64,6 +64,13 @@ uint16_t f32_to_bf16_rne(float x);
 // Explicit m x d FQJL matrix (double), for export.
 void fqjl_explicit(const HostSketch &hs, std::vector<double> &out);
 
+// Host-written operand images (images_host.cpp): the dense bf16 S in the
+// matrix-core operand order (m * d values), and the FQJL first stage
+// (m * d values, only for the shapes fqjl_mfma_image_shape accepts).
+void build_mfma_b_layout(const uint16_t *S16, int d, int m, uint16_t *out);
+bool fqjl_mfma_image_shape(int d, int m);
+void build_fqjl_mfma_image(const HostSketch &hs, uint16_t *out);
+
 }  // namespace qjl
 
 // Device-resident sketch.  All device arrays live in one allocation `dmem`.

@@ -275,8 +275,11 @@ __device__ __forceinline__ void tile_limb_acc(const uint32_t *wb, const QueryOpe
 // Combine the limb rows a lane holds with those of lane group g ^ 1 (the
 // same key, the query's other rows): v_permlane16_swap of a value with
 // itself leaves rows (0, 0, 2, 2) in one result and (1, 1, 3, 3) in the
-// other, so their sum is v + v[lane ^ 16] with no LDS traffic.  The result
-// is the exact sum_j (2 b_j - 1) X_j (integers below 2^24 throughout).
+// other, so their sum is v + v[lane ^ 16] with no LDS traffic.  Each limb
+// row R_c is an exact integer; their weighted sum sum_c 32^(4-c) R_c =
+// sum_j (2 b_j - 1) X_j reaches m 2^23 in magnitude, so the float32 chain
+// that forms it rounds, by at most about 2^-24 m max_j |X_j| in all (far
+// below the score tolerance once scaled by 2^-F).
 __device__ __forceinline__ float limb_rows_combine(const v4f_t &acc, const float (&wgt)[4]) {
   float v = acc[0] * wgt[0];
   v = fmaf(acc[1], wgt[1], v);

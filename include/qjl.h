@@ -87,7 +87,11 @@ typedef enum {
                                    wrong device, m not a multiple of 32, bad rho */
   QJL_ERR_UNSUPPORTED = 2,      /* valid but outside the implemented shapes */
   QJL_ERR_OUT_OF_MEMORY = 3,    /* host or device allocation failed (qjl_make_sketch only) */
-  QJL_ERR_DEVICE = 4            /* no usable GPU, or a HIP call / kernel launch failed */
+  QJL_ERR_DEVICE = 4,           /* no usable GPU, or a HIP call / kernel launch failed */
+  /* Not statuses: they give the type the range of int32, so any integer a
+   * caller passes to qjl_status_string is a value of the type. */
+  QJL_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  QJL_STATUS_RANGE_MAX_ = 2147483647
 } qjl_status;
 
 typedef enum {
@@ -147,8 +151,8 @@ qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t
 
 /*
  * Quantize n_keys keys: bits_out[i] = packed signs of S k_i (+ dither),
- * norms_out[i] = ||k_i||_2 (QJL abstract: JL transform followed by sign-bit
- * quantization; no per-block constants, one norm per key).
+ * norms_out[i] = ||k_i||_2 (QJL abstract: a JL projection whose coordinates
+ * are reduced to their signs; no per-block constants, one norm per key).
  * key_index_base is the global index of row 0; the dither of key i is drawn
  * from counter (key_index_base + i), so a cache appended in pieces gets the
  * same bits as one quantized whole.  (Which kernel runs depends on the
@@ -195,8 +199,8 @@ qjl_status qjl_quantize_keys_into(const qjl_sketch *sk, const void *K, int32_t d
 
 /*
  * Project n_queries queries: Sq_out[i] = S q_i in float32, not quantized (the
- * "standard JL transform without quantization" of the QJL abstract; no
- * dither).  q: device [n_queries][d] in `dtype`; Sq_out: device
+ * QJL abstract projects the query with the same JL matrix and keeps it
+ * unquantized; no dither).  q: device [n_queries][d] in `dtype`; Sq_out: device
  * float[n_queries][m].  Errors as for qjl_quantize_keys.  For a dense sketch
  * and bfloat16 queries with d % 16 == 0, m % 64 == 0 and 16-byte aligned q
  * and Sq_out, the products run on the matrix cores exactly as in the

@@ -9,9 +9,9 @@ projects with a Johnson-Lindenstrauss matrix; the Fast Quantized JL page
 projection.  S[j, c] ~ N(0, 1) iid.
 
 FQJL: the same page ("The paper" abstract; "Key concepts", P-FQJL) replaces
-S by compositions of randomized Hadamard transforms, with a Gaussian rather
-than Rademacher diagonal in the second stage and a uniform random
-permutation between the two Hadamard transforms.  One block is
+S by compositions of randomized Hadamard transforms: the diagonal of the
+second stage is Gaussian (the first keeps random signs), and a uniform
+random permutation sits between the two Hadamard transforms.  One block is
 
     B_b = H diag(G_b) Pi_b (H / sqrt(d)) diag(D_b)
 

@@ -204,3 +204,20 @@ def test_binding_rejects_short_buffers_before_launch():
         qj.score(sk, _DevStub((1, m), torch.float32), _DevStub((n, m // 32), torch.int32),
                  _DevStub((n,), torch.float32), 1, 1, n,
                  scores_out=_DevStub((n - 1,), torch.float32))
+
+
+def test_probe_library_loads():
+    # the benchmark's plain read kernels: a separate library, not part of libqjl
+    from bit_quantized_jl_amd import build as b
+    assert os.path.exists(b.PROBE_LIB)
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    fn = lib.qjl_probe_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    # argument checks happen before any HIP call
+    assert fn(None, 16, 0, 4, 1, None, None) == 1
+    assert fn(16, 15, 0, 4, 1, 16, None) == 1          # bytes not a multiple of 16
+    assert fn(16, 16, 2, 4, 1, 16, None) == 1          # bad pattern
+    assert fn(16, 16, 0, 3, 1, 16, None) == 1          # bad unroll
+    assert "qjl_probe_read" not in {n for n in dir(qj.load()) if n.startswith("qjl_")}
