@@ -216,10 +216,11 @@ struct StageRead<8> {
 // u % 2 of select source u / 2), and leave with one 256-byte store per query.
 // The query scale lives in the lane groups of its member (A: 0-1, B: 2-3),
 // so each member's is read from one of its lanes.
-template <int T, int QP>
+template <int T, int QP, bool DEFER>
 __device__ __forceinline__ void score_stage(const StageRead<T> &sr, const QueryOperands<T, QP> &qo,
-                                            int64_t key, int64_t kend, int gq, int nqp,
-                                            float *__restrict__ outq, int64_t nk) {
+                                            int64_t key, int64_t kbeg, int64_t kend, int gq,
+                                            int nqp, float *__restrict__ outq, int64_t nk,
+                                            float *sDefer, int chunk) {
   v4f_t acc[4][QP];
 #pragma unroll
   for (int u = 0; u < 4; ++u) tile_limb_acc<T, QP>(sr.w[u], qo, acc[u]);
@@ -237,13 +238,22 @@ __device__ __forceinline__ void score_stage(const StageRead<T> &sr, const QueryO
     const float sb = __uint_as_float(__builtin_amdgcn_readlane(qs, 32)) * sr.n;
     if (key < kend) {
       const int qa = 2 * qp, qb = 2 * qp + 1;
-      if (qa < nqp) __builtin_nontemporal_store(__uint_as_float(sw[0]) * sa, outq + qa * nk + key);
-      if (qb < nqp) __builtin_nontemporal_store(__uint_as_float(sw[1]) * sb, outq + qb * nk + key);
+      if constexpr (DEFER) {
+        const int kl = (int)(key - kbeg);
+        if (qa < nqp) sDefer[qa * chunk + kl] = __uint_as_float(sw[0]) * sa;
+        if (qb < nqp) sDefer[qb * chunk + kl] = __uint_as_float(sw[1]) * sb;
+      } else {
+        if (qa < nqp) __builtin_nontemporal_store(__uint_as_float(sw[0]) * sa, outq + qa * nk + key);
+        if (qb < nqp) __builtin_nontemporal_store(__uint_as_float(sw[1]) * sb, outq + qb * nk + key);
+      }
     }
   }
 }
 
-template <int T, int QP>
+// With DEFER the scores of a pass stay in LDS (sDefer: [queries][chunk]) and
+// leave at the end of the workgroup's keys as 16-byte non-temporal stores;
+// otherwise each stage stores its own.
+template <int T, int QP, bool DEFER>
 __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, int64_t G, int64_t nq, int64_t nk, int chunk, float cscale,
@@ -256,6 +266,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
   constexpr int JL = (m + 63) / 64;            // query coordinates per lane
   __shared__ __attribute__((aligned(16))) unsigned char sAimg[QueryOperands<T, QP>::IMAGE_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sRing[SM_WAVES][R][SB];
+  extern __shared__ __attribute__((aligned(16))) float sDefer[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
@@ -297,11 +308,59 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         StageRead<T> sr;
         sr.read(lds_address(slot + ((lane & 15) * W + T * gq) * 4),
                 lds_address(slot + Ring<T>::BITS_BYTES + lane * 4));
-        score_stage<T, QP>(sr, qo, k0 + lane, kend, gq, nqp, out + (g * nq + q0) * nk, nk);
+        score_stage<T, QP, DEFER>(sr, qo, k0 + lane, kbeg, kend, gq, nqp,
+                                  out + (g * nq + q0) * nk, nk, sDefer, chunk);
+      }
+      if constexpr (DEFER) {
+        // every wave's scores are in LDS; then the workgroup writes them, four
+        // consecutive keys per lane (scalar stores where a row is not 16-byte
+        // aligned or for the last few keys)
+        asm volatile("" ::: "memory");
+        lds_barrier();
+        const int nkb = (int)(kend - kbeg);
+        for (int qi = 0; qi < nqp; ++qi) {
+          float *dst = out + (g * nq + q0 + qi) * nk + kbeg;
+          const float *srcq = sDefer + qi * chunk;
+          const bool vec = ((uintptr_t)dst & 15) == 0;
+          for (int i = 4 * tid; i < nkb; i += 4 * SM_THREADS) {
+            if (vec && i + 3 < nkb) {
+              const v4f_t v = *reinterpret_cast<const v4f_t *>(srcq + i);
+              __builtin_nontemporal_store(v, reinterpret_cast<v4f_t *>(dst + i));
+            } else {
+              for (int t = 0; t < 4 && i + t < nkb; ++t)
+                __builtin_nontemporal_store(srcq[i + t], dst + i + t);
+            }
+          }
+        }
+        // the next pass (more queries, or another group) writes sDefer again
+        asm volatile("" ::: "memory");
+        lds_barrier();
       }
     }
   }
   wait_vmcnt<0>();  // DMA of stages past the end must land before exit
+}
+
+// LDS the deferred scores may take per workgroup (beside the ring and the
+// query image, within the 160 KB of a compute unit).
+constexpr size_t DEFER_MAX_BYTES = 64 << 10;
+
+template <int T, int QP, bool DEFER>
+void launch_sm_kernel(dim3 grid, size_t dyn, hipStream_t st, const float *Sq,
+                      const uint32_t *bits, const float *norms, int64_t G, int64_t nq,
+                      int64_t nk, int chunk, float c, float *scores) {
+  if constexpr (DEFER) {
+    // allow the dynamic LDS beyond the default limit, once per device
+    static PerDevice pd_attr;
+    (void)per_device(pd_attr, [] {
+      (void)hipFuncSetAttribute((const void *)score_mfma_kernel<T, QP, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)DEFER_MAX_BYTES);
+      return 1;
+    });
+  }
+  hipLaunchKernelGGL((score_mfma_kernel<T, QP, DEFER>), grid, dim3(SM_THREADS), dyn, st, Sq,
+                     bits, norms, G, nq, nk, chunk, c, scores);
 }
 
 template <int T, int QP>
@@ -313,7 +372,7 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   // three workgroups per unit, which set up each query more often).
   static PerDevice pd_res, pd_cus;
   const int resident =
-      per_device(pd_res, [] { return resident_workgroups(score_mfma_kernel<T, QP>, SM_THREADS); });
+      per_device(pd_res, [] { return resident_workgroups(score_mfma_kernel<T, QP, false>, SM_THREADS); });
   const int cus = per_device(pd_cus, device_compute_units);
   // chunk: a multiple of the 256 keys one block step covers
   int64_t chunk = (G * nk + cus - 1) / cus;
@@ -324,8 +383,36 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   // one workgroup per group leaves the chip a wave per SIMD and is slower.
   if (G >= cus && 2 * G <= resident) chunk = ((nk + 1) / 2 + 255) / 256 * 256;
   dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
-  hipLaunchKernelGGL((score_mfma_kernel<T, QP>), grid, dim3(SM_THREADS), 0, st, Sq, bits, norms,
-                     G, nq, nk, (int)chunk, c, scores);
+  // Scores written per stage cost more than the same bytes written in one
+  // burst per workgroup (long context: 56 against 53.5 us): defer them to
+  // LDS when a pass's scores of the workgroup's keys fit and the extra LDS
+  // leaves as many of this launch's workgroups resident at once.
+  const int64_t nqd = nq < 2 * QP ? nq : 2 * QP;
+  const size_t dyn = (size_t)(nqd * chunk) * sizeof(float);
+  static PerDevice pd_lds, pd_static;
+  const int lds_cu = per_device(pd_lds, [] {
+    int dev = 0, v = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || v <= 0)
+      v = 160 << 10;
+    return v;
+  });
+  const int lds_static = per_device(pd_static, [] {
+    hipFuncAttributes a{};
+    if (hipFuncGetAttributes(&a, (const void *)score_mfma_kernel<T, QP, true>) != hipSuccess)
+      return 1 << 30;  // unknown: never defer
+    return (int)a.sharedSizeBytes + 1;
+  }) - 1;
+  const int64_t wgs = (int64_t)grid.x * grid.y;
+  const int64_t per_cu_plain = resident / cus;
+  const int64_t per_cu_defer = (int64_t)lds_cu / ((int64_t)lds_static + (int64_t)dyn);
+  const int64_t need_per_cu = (wgs + cus - 1) / cus;
+  const int64_t want = need_per_cu < per_cu_plain ? need_per_cu : per_cu_plain;
+  if (dyn <= DEFER_MAX_BYTES && per_cu_defer >= want)
+    launch_sm_kernel<T, QP, true>(grid, dyn, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);
+  else
+    launch_sm_kernel<T, QP, false>(grid, 0, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);
   return hipGetLastError();
 }
 
