@@ -220,4 +220,10 @@ def test_probe_library_loads():
     assert fn(16, 15, 0, 4, 1, 16, None) == 1          # bytes not a multiple of 16
     assert fn(16, 16, 2, 4, 1, 16, None) == 1          # bad pattern
     assert fn(16, 16, 0, 3, 1, 16, None) == 1          # bad unroll
+    dc = lib.qjl_probe_dither_cost
+    dc.restype = ctypes.c_int
+    dc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert dc(0, 1, 1, None, None) == 1                 # no output buffer
+    assert dc(3, 1, 1, 16, None) == 1                   # bad mode
+    assert dc(0, 0, 1, 16, None) == 1                   # empty grid
     assert "qjl_probe_read" not in {n for n in dir(qj.load()) if n.startswith("qjl_")}
