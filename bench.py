@@ -130,7 +130,8 @@ def sustain(seconds: float):
         clk = re.match(r"\s*CLK: (\d+) MHz", line)
         if clk and section.startswith("GFX_"):  # graphics clock of one XCD
             clocks.append(float(clk.group(1)))
-    print(json.dumps({"sustain_s": seconds, "launches": launches,
+    print(json.dumps({"sustain_s": seconds, "dense_schedule": dense_schedule(),
+                      "launches": launches,
                       "mean_launch_s": a.seconds_to(b) / launches,
                       "socket_power_w_mean": sum(power) / len(power) if power else None,
                       "socket_power_w_samples": len(power),
@@ -203,10 +204,22 @@ def kernel_tu_hash(src: str = QUANT_KERNEL_SRC) -> str:
     return h.hexdigest()[:16]
 
 
+DENSE_SCHEDULES = ("default", "prefetch", "rt4", "immediate")
+
+
+def dense_schedule() -> str:
+    """The dense quantizer's register schedule this process launches: the
+    library reads QJL_DENSE_SCHEDULE, and any value other than the three
+    alternatives means the default."""
+    s = os.environ.get("QJL_DENSE_SCHEDULE", "default")
+    return s if s in DENSE_SCHEDULES else "default"
+
+
 def read_traffic():
     """HBM bytes per quantize launch from the committed rocprofv3 PMC summary,
-    or None when absent or taken on another version of the kernel's
-    translation unit (its source or any header it includes)."""
+    or None when absent, taken on another version of the kernel's
+    translation unit (its source or any header it includes), or taken with
+    another register schedule than this process launches."""
     if not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
@@ -215,6 +228,8 @@ def read_traffic():
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_tu_sha256_16") != kernel_tu_hash():
+        return None
+    if vals.get("dense_schedule", "default") != dense_schedule():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -664,7 +679,10 @@ def run_only(kind: str):
         t = time_quantize(qj, torch, w, reps=3)[0]
     if sk is not None:
         sk.close()
-    print(json.dumps({"only": kind, "workload": w.name, "mean_s": t}), flush=True)
+    out = {"only": kind, "workload": w.name, "mean_s": t}
+    if kind == "quantize":
+        out["dense_schedule"] = dense_schedule()
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -772,6 +790,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": qbytes, "avg_launch_s": q_avg,
+                     "dense_schedule": dense_schedule(),
                      "timing": "HIP events around each quantize launch inside the timed K steps",
                      "launch_s_min": min(q_times), "launch_s_max": max(q_times),
                      "mfma_tflops": q_flops / q_avg / 1e12,

@@ -34,27 +34,36 @@ int per_device(PerDevice &pd, F compute) {
 // Workgroups of `kernel` (launched with `threads` threads and no dynamic
 // LDS) that the current device holds at once: compute units times the
 // occupancy the runtime reports (fallbacks: 256 units, one workgroup each).
-// Callers cache it per device (PerDevice).
+// Callers cache it per device (PerDevice).  A failed query is cleared from
+// the runtime's last-error state, which the launchers report after their
+// launches.
 template <typename K>
 int resident_workgroups(K kernel, int threads) {
   int dev = 0, cus = 0, per_cu = 0;
   (void)hipGetDevice(&dev);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
+      cus <= 0) {
+    (void)hipGetLastError();
     cus = 256;
+  }
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-      per_cu <= 0)
+      per_cu <= 0) {
+    (void)hipGetLastError();
     per_cu = 1;
+  }
   return cus * per_cu;
 }
 
-// Compute units of the current device (fallback 256).
+// Compute units of the current device (fallback 256, the failed query
+// cleared as above).
 inline int device_compute_units() {
   int dev = 0, cus = 0;
   (void)hipGetDevice(&dev);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
+      cus <= 0) {
+    (void)hipGetLastError();
     cus = 256;
+  }
   return cus;
 }
 

@@ -38,6 +38,9 @@
 //
 // Short calls (decode-time appends) take quantize_small_kernel below, which
 // forms the same sums without staging S in LDS.
+#include <stdlib.h>
+#include <string.h>
+
 #include "device_common.h"
 #include "mfma_image.h"
 
@@ -49,12 +52,8 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 namespace {
 
-#ifndef QJL_QM_RING
-#define QJL_QM_RING 4  // S fragments in flight from LDS
-#endif
-constexpr int QM_RING = QJL_QM_RING;
 // A wave tile is RT 32-key column tiles: each S fragment read from LDS feeds
-// RT MFMAs.
+// RT MFMAs.  R S fragments are in flight from LDS at a time.
 
 template <int T, int RT>
 struct KeyTile {
@@ -103,7 +102,7 @@ __device__ __forceinline__ uint32_t pack_signs(uint32_t x, const floatx16_t &acc
 // scheduling barrier closes every MFMA step: without it the scheduler hoists
 // all MFMAs of the tile and runs out of registers.  Norms of column tiles
 // 2i and 2i + 1 leave in one 64-lane store (lane half h writes tile 2i + h).
-template <int D, int M, int RT, bool DEFER, bool MAPPED>
+template <int D, int M, int RT, int R, bool DEFER, bool MAPPED>
 __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, const uint4 *sS,
                                              int64_t k0, int64_t n, int lane, int r, int h,
                                              const RowMap &map, float *__restrict__ norms,
@@ -111,7 +110,6 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, cons
   constexpr int T = D / 16;
   constexpr int W = M / 32;
   constexpr int NF = W * T;    // S fragments per tile walk
-  constexpr int R = QM_RING;
   // The S reads below must stay inside the tile loop: hoisted out of it, all
   // m*d/512 fragments would be held in registers.
   asm volatile("" ::: "memory");
@@ -236,10 +234,12 @@ __device__ __forceinline__ void process_tile(const KeyTile<D / 16, RT> &kt, cons
   }
 }
 
-// Persistent kernel: each wave walks 64-key tiles with a stride of all waves
-// in the grid; the grid is sized to what is resident at once.  Two waves per
-// SIMD hide one another's HBM latency.
-template <int D, int M, int WAVES, int RT, bool DEFER, bool MAPPED>
+// Persistent kernel: each wave walks tiles of 32 RT keys with a stride of all
+// waves in the grid; the grid is sized to what is resident at once.  Two
+// waves per SIMD hide one another's HBM latency.  With PF a wave also issues
+// the loads of its next tile before it processes the current one (two tiles'
+// keys live in registers).
+template <int D, int M, int WAVES, int RT, int R, bool DEFER, bool PF, bool MAPPED>
 __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Simg, int64_t n, RowMap map,
     float *__restrict__ norms, uint32_t *__restrict__ bits) {
@@ -257,26 +257,36 @@ __global__ __launch_bounds__(64 * WAVES, 2) void quantize_mfma_kernel(
   constexpr int KEYS = 32 * RT;
   const int64_t ntiles = (n + KEYS - 1) / KEYS;
   const int64_t stride = (int64_t)gridDim.x * WAVES;
-  for (int64_t tile = (int64_t)blockIdx.x * WAVES + wave; tile < ntiles; tile += stride) {
-    KeyTile<D / 16, RT> kt;
-    load_tile<D, RT>(kt, K, tile * KEYS, n, r, h);
-    process_tile<D, M, RT, DEFER, MAPPED>(kt, sS, tile * KEYS, n, lane, r, h, map, norms, bits);
+  int64_t tile = (int64_t)blockIdx.x * WAVES + wave;
+  if constexpr (PF) {
+    KeyTile<D / 16, RT> ka, kb;
+    if (tile < ntiles) load_tile<D, RT>(ka, K, tile * KEYS, n, r, h);
+    while (tile < ntiles) {
+      const int64_t t1 = tile + stride;
+      if (t1 < ntiles) load_tile<D, RT>(kb, K, t1 * KEYS, n, r, h);
+      process_tile<D, M, RT, R, DEFER, MAPPED>(ka, sS, tile * KEYS, n, lane, r, h, map, norms,
+                                               bits);
+      if (t1 >= ntiles) break;
+      const int64_t t2 = t1 + stride;
+      if (t2 < ntiles) load_tile<D, RT>(ka, K, t2 * KEYS, n, r, h);
+      process_tile<D, M, RT, R, DEFER, MAPPED>(kb, sS, t1 * KEYS, n, lane, r, h, map, norms,
+                                               bits);
+      tile = t2;
+    }
+  } else {
+    for (; tile < ntiles; tile += stride) {
+      KeyTile<D / 16, RT> kt;
+      load_tile<D, RT>(kt, K, tile * KEYS, n, r, h);
+      process_tile<D, M, RT, R, DEFER, MAPPED>(kt, sS, tile * KEYS, n, lane, r, h, map, norms,
+                                               bits);
+    }
   }
 }
 
-// Launch shape per sketch size (measured on MI355X): up to m = 256 two
-// 4-wave workgroups share a CU, each with its own copy of S, and packing is
-// deferred; at m = 512 S takes 128 KB of LDS, so one 8-wave workgroup per CU
-// packs each pass as it ends to stay within two waves' registers per SIMD.
-template <int D, int M, bool MAPPED>
-hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
-                     float *norms, uint32_t *bits, hipStream_t st) {
-  // Two column tiles per wave: four (halving the LDS reads of S) measured
-  // slower, with no room left to defer the packing.
-  constexpr int RT = 2;
-  constexpr int WAVES = M <= 256 ? 4 : 8;
-  constexpr bool DEFER = M <= 256;
-  auto kern = quantize_mfma_kernel<D, M, WAVES, RT, DEFER, MAPPED>;
+template <int D, int M, int WAVES, int RT, int R, bool DEFER, bool PF, bool MAPPED>
+hipError_t launch_qm_kernel(const qjl_sketch *sk, const uint16_t *K, int64_t n,
+                            const RowMap &map, float *norms, uint32_t *bits, hipStream_t st) {
+  auto kern = quantize_mfma_kernel<D, M, WAVES, RT, R, DEFER, PF, MAPPED>;
   static PerDevice pd_res;  // workgroups resident on the whole device
   const int resident = per_device(pd_res, [&] { return resident_workgroups(kern, 64 * WAVES); });
   const int64_t ntiles = (n + 32 * RT - 1) / (32 * RT);
@@ -285,6 +295,62 @@ hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const R
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->S16mfma, n, map, norms,
                      bits);
   return hipGetLastError();
+}
+
+// Launch shape per sketch size (measured on MI355X): up to m = 256 two
+// 4-wave workgroups share a CU, each with its own copy of S, two column tiles
+// per wave, four S fragments in flight, and packing deferred; at m = 512 S
+// takes 128 KB of LDS, so one 8-wave workgroup per CU packs each pass as it
+// ends to stay within two waves' registers per SIMD.
+//
+// Up to m = 256 the environment variable QJL_DENSE_SCHEDULE selects one of
+// three other register schedules for unmapped launches (any other value, or
+// none, keeps the one above).  All four form every sum from the same inputs
+// in the same order and pack the same signs, so the bits and norms are
+// identical; they differ only in time and power:
+//   prefetch   the next tile's keys are loaded while the current one is
+//              processed (two S fragments in flight, to fit the registers;
+//              at d = m = 128 each pass packed as it ends)
+//   rt4        four column tiles per wave (half the LDS reads of S), each
+//              pass packed as it ends, two S fragments in flight
+//   immediate  each pass packed as it ends (no deferral)
+// On MI355X the default measured fastest; sustained, every schedule holds the
+// socket at its power limit.
+enum class QmSchedule { Default, Prefetch, Rt4, Immediate };
+
+QmSchedule dense_schedule() {
+  const char *s = getenv("QJL_DENSE_SCHEDULE");
+  if (s == nullptr) return QmSchedule::Default;
+  if (strcmp(s, "prefetch") == 0) return QmSchedule::Prefetch;
+  if (strcmp(s, "rt4") == 0) return QmSchedule::Rt4;
+  if (strcmp(s, "immediate") == 0) return QmSchedule::Immediate;
+  return QmSchedule::Default;
+}
+
+template <int D, int M, bool MAPPED>
+hipError_t launch_qm(const qjl_sketch *sk, const uint16_t *K, int64_t n, const RowMap &map,
+                     float *norms, uint32_t *bits, hipStream_t st) {
+  if constexpr (M <= 256 && !MAPPED) {
+    switch (dense_schedule()) {
+      case QmSchedule::Prefetch: {
+        constexpr bool PDEFER = !(D == 128 && M == 128);  // there deferral would spill
+        return launch_qm_kernel<D, M, 4, 2, 2, PDEFER, true, false>(sk, K, n, map, norms, bits,
+                                                                    st);
+      }
+      case QmSchedule::Rt4:
+        return launch_qm_kernel<D, M, 4, 4, 2, false, false, false>(sk, K, n, map, norms, bits,
+                                                                     st);
+      case QmSchedule::Immediate:
+        return launch_qm_kernel<D, M, 4, 2, 4, false, false, false>(sk, K, n, map, norms, bits,
+                                                                     st);
+      case QmSchedule::Default:
+        break;
+    }
+  }
+  constexpr int WAVES = M <= 256 ? 4 : 8;
+  constexpr bool DEFER = M <= 256;
+  return launch_qm_kernel<D, M, WAVES, 2, 4, DEFER, false, MAPPED>(sk, K, n, map, norms, bits,
+                                                                   st);
 }
 
 // Few keys (a decode-time append of one key per head): the same sums with

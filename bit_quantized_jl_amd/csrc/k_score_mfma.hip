@@ -345,20 +345,42 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
 // query image, within the 160 KB of a compute unit).
 constexpr size_t DEFER_MAX_BYTES = 64 << 10;
 
+// The dynamic LDS a deferring launch of score_mfma_kernel<T, QP, true> may
+// take on the current device: DEFER_MAX_BYTES, or less where the kernel's
+// static LDS leaves less room within a workgroup's limit (m = 1024: the
+// stage ring and the query image already take most of it); 0 when the
+// kernel's attribute cannot be raised (then the scores are stored per stage).
+// The attribute is set once per device; a refusal is cleared from the
+// runtime's last-error state so that it does not surface as a launch error.
+template <int T, int QP>
+size_t defer_limit() {
+  static PerDevice pd;
+  return (size_t)(per_device(pd, [] {
+    int dev = 0, max_block = 0;
+    hipFuncAttributes a{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        hipFuncGetAttributes(&a, (const void *)score_mfma_kernel<T, QP, true>) != hipSuccess) {
+      (void)hipGetLastError();
+      return 1;
+    }
+    const int64_t room = (int64_t)max_block - (int64_t)a.sharedSizeBytes;
+    const int lim = (int)(room < (int64_t)DEFER_MAX_BYTES ? room : (int64_t)DEFER_MAX_BYTES);
+    if (lim <= 0) return 1;
+    if (hipFuncSetAttribute((const void *)score_mfma_kernel<T, QP, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lim) != hipSuccess) {
+      (void)hipGetLastError();
+      return 1;
+    }
+    return lim + 1;
+  }) - 1);
+}
+
 template <int T, int QP, bool DEFER>
 void launch_sm_kernel(dim3 grid, size_t dyn, hipStream_t st, const float *Sq,
                       const uint32_t *bits, const float *norms, int64_t G, int64_t nq,
                       int64_t nk, int chunk, float c, float *scores) {
-  if constexpr (DEFER) {
-    // allow the dynamic LDS beyond the default limit, once per device
-    static PerDevice pd_attr;
-    (void)per_device(pd_attr, [] {
-      (void)hipFuncSetAttribute((const void *)score_mfma_kernel<T, QP, true>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)DEFER_MAX_BYTES);
-      return 1;
-    });
-  }
   hipLaunchKernelGGL((score_mfma_kernel<T, QP, DEFER>), grid, dim3(SM_THREADS), dyn, st, Sq,
                      bits, norms, G, nq, nk, chunk, c, scores);
 }
@@ -394,14 +416,18 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
     int dev = 0, v = 0;
     (void)hipGetDevice(&dev);
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-            hipSuccess || v <= 0)
+            hipSuccess || v <= 0) {
+      (void)hipGetLastError();  // a failed query is not a launch error
       v = 160 << 10;
+    }
     return v;
   });
   const int lds_static = per_device(pd_static, [] {
     hipFuncAttributes a{};
-    if (hipFuncGetAttributes(&a, (const void *)score_mfma_kernel<T, QP, true>) != hipSuccess)
-      return 1 << 30;  // unknown: never defer
+    if (hipFuncGetAttributes(&a, (const void *)score_mfma_kernel<T, QP, true>) != hipSuccess) {
+      (void)hipGetLastError();  // a failed query is not a launch error
+      return 1 << 30;           // unknown: never defer
+    }
     return (int)a.sharedSizeBytes + 1;
   }) - 1;
   const int64_t wgs = (int64_t)grid.x * grid.y;
@@ -409,7 +435,7 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   const int64_t per_cu_defer = (int64_t)lds_cu / ((int64_t)lds_static + (int64_t)dyn);
   const int64_t need_per_cu = (wgs + cus - 1) / cus;
   const int64_t want = need_per_cu < per_cu_plain ? need_per_cu : per_cu_plain;
-  if (dyn <= DEFER_MAX_BYTES && per_cu_defer >= want)
+  if (dyn > 0 && dyn <= defer_limit<T, QP>() && per_cu_defer >= want)
     launch_sm_kernel<T, QP, true>(grid, dyn, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);
   else
     launch_sm_kernel<T, QP, false>(grid, 0, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);

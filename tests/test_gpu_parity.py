@@ -1,8 +1,9 @@
 """GPU parity: the HIP library (through the C ABI) against the CPU oracle.
 
-Small and medium shapes are checked element by element; the full-size
-workloads (run in the same launch configuration the benchmark times) are
-checked on sampled rows that the oracle recomputes one by one.
+Small and medium shapes are checked element by element, and so are the
+full-size workloads (run in the same launch configuration the benchmark
+times): every row of their caches and every score, against the oracle run
+chunk by chunk on a thread pool.
 """
 from __future__ import annotations
 
@@ -111,6 +112,34 @@ def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     w = wl.Workload(f"persistent_{variant}_{d}_{m}", d, m, variant, 1, 1, 16384 + 1357, 5,
                     "bf16", "normal", rho, seed=4)
     run_quantize_case(w, base=3)
+
+
+@pytest.mark.parametrize("d,m", [(64, 128), (64, 256), (128, 128), (128, 256)])
+def test_dense_schedules_identical(monkeypatch, d, m):
+    # The dense quantizer's register schedules (QJL_DENSE_SCHEDULE): each one's
+    # bits and norms equal the default schedule's, whose every row is checked
+    # against the oracle.  The key count gives each wave of the persistent
+    # grid several tiles, an odd number for some waves and an even number for
+    # others (both exits of the prefetching loop), and a short last tile.
+    n = 3 * 2048 * 128 + 777
+    w = wl.Workload(f"schedules_{d}_{m}", d, m, "dense", 1, 1, n, 5, "bf16", "normal", 0.0,
+                    seed=6)
+    note("dense schedules", d, m, n)
+    Kh = wl.make_keys(w, "cpu")
+    K = Kh.to(DEV)
+    sk = qj.make_sketch(w.seed, d, m, "dense", 0.0)
+    monkeypatch.delenv("QJL_DENSE_SCHEDULE", raising=False)
+    n0, b0 = qj.quantize_keys(sk, K)
+    torch.cuda.synchronize()
+    ref = oracle_sketch(w.seed, d, m, "dense", 0.0)
+    oracle_check_all_rows(ref, Kh, "bf16", bits_np(b0), to_np_f64(n0))
+    for schedule in ("prefetch", "rt4", "immediate"):
+        monkeypatch.setenv("QJL_DENSE_SCHEDULE", schedule)
+        n1, b1 = qj.quantize_keys(sk, K)
+        torch.cuda.synchronize()
+        assert torch.equal(b1, b0), schedule
+        assert torch.equal(n1, n0), schedule
+    sk.close()
 
 
 @pytest.mark.parametrize("variant,d,m,dt,nq", [
@@ -351,8 +380,12 @@ def test_projected_keys_reproduce_their_bits(variant, d, m):
 
 @pytest.mark.parametrize("m,G,nq,nk", [(256, 1, 16, 4096), (256, 3, 1, 1000), (512, 2, 1, 777),
                                        (32, 2, 3, 65), (96, 1, 2, 130), (1024, 1, 1, 300),
-                                       (128, 5, 4, 17), (256, 2, 7, 1), (2048, 1, 2, 64)])
+                                       (128, 5, 4, 17), (256, 2, 7, 1), (2048, 1, 2, 64),
+                                       (1024, 2, 3, 300), (1024, 1, 4, 5000)])
 def test_score_random_bits(m, G, nq, nk):
+    # m = 1024 with query pairs: the kernel whose stage ring and query image
+    # leave the least LDS for deferred scores (and no room for the default
+    # 64 KB allowance) still defers them.
     note("score", m, G, nq, nk)
     rs = np.random.default_rng(m + G + nq + nk)
     sk = qj.make_sketch(0, 128, m, "dense", 0.0)
