@@ -411,13 +411,35 @@ def copy_peak_gbps(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / best / 1e9
 
 
+def per_call_times(torch, call, iters: int) -> list:
+    """Sorted seconds of `iters` calls, each between its own fence-free HIP
+    event pair on the current stream, with Python's garbage collector off:
+    a collection between a call's start event and its launch, with the queue
+    drained, would be timed as part of that call."""
+    import gc
+    st = torch.cuda.current_stream()
+    evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        for i in range(iters):
+            evs[i][0].record(st)
+            call(i)
+            evs[i][1].record(st)
+        torch.cuda.synchronize()
+    finally:
+        if was:
+            gc.enable()
+    return sorted(a.seconds_to(b) for a, b in evs)
+
+
 def read_ceiling(torch, nbytes: int, n_sets: int, iters: int = 40):
     """Measured read-bandwidth ceiling for a kernel that streams `nbytes`:
     plain 16-byte-vector read kernels (libqjl_probe.so: chunked and
     grid-stride patterns, 2/4/8 loads in flight per lane, 1/2/4 workgroups of
     256 lanes per compute unit) over `n_sets` distinct buffers of that size
     in rotation (as the score timing rotates its inputs past the 256 MB
-    Infinity Cache), timed like the kernels: mean of per-call HIP-event
+    Infinity Cache), timed like the kernels: median of per-call HIP-event
     times.  Returns the best configuration's rate."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
@@ -449,17 +471,13 @@ def read_ceiling(torch, nbytes: int, n_sets: int, iters: int = 40):
                 for i in range(2 * n_sets):
                     call(i)
                 torch.cuda.synchronize()
-                evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
-                for i in range(iters):
-                    evs[i][0].record(st)
-                    call(i)
-                    evs[i][1].record(st)
-                torch.cuda.synchronize()
-                mean = sum(a.seconds_to(b) for a, b in evs) / iters
+                ts = per_call_times(torch, call, iters)
+                med = ts[len(ts) // 2]
                 key = "chunked" if pattern == 0 else "grid-stride"
-                per_pattern[key] = min(per_pattern.get(key, mean), mean)
-                if best is None or mean < best["mean_s"]:
-                    best = {"mean_s": mean, "GBps": n16 * 16 / mean / 1e9,
+                per_pattern[key] = min(per_pattern.get(key, med), med)
+                if best is None or med < best["median_s"]:
+                    best = {"median_s": med, "mean_s": sum(ts) / len(ts),
+                            "GBps": n16 * 16 / med / 1e9,
                             "pattern": "chunked" if pattern == 0 else "grid-stride",
                             "loads_in_flight_per_lane": unroll, "workgroups_per_cu": wpc}
     del bufs, sink
@@ -469,6 +487,20 @@ def read_ceiling(torch, nbytes: int, n_sets: int, iters: int = 40):
     best["best_GBps_by_pattern"] = {k: n16 * 16 / v / 1e9 for k, v in per_pattern.items()}
     best["frac_hbm"] = best["GBps"] / HBM_PEAK_GBPS
     return best
+
+
+# Memory and fabric clocks fall while the GPU idles (set-up, a host copy):
+# the first tens of calls after such a stretch ran ~8% slower.  Each rotating
+# measurement therefore starts with ~30 ms of untimed calls.
+WARM_S = 0.03
+
+
+def warm_up(torch, call, n_sets: int, est_s: float):
+    """Untimed calls before a rotating measurement: every input set twice and
+    at least WARM_S of GPU time (est_s: a rough duration of one call)."""
+    for i in range(max(2 * n_sets, int(WARM_S / est_s) + 1)):
+        call(i)
+    torch.cuda.synchronize()
 
 
 def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
@@ -483,19 +515,14 @@ def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
         Sq = torch.randn(w.groups * w.n_q, w.m, device=dev) * 11
         out = torch.empty(w.groups, w.n_q, w.n_k, device=dev)
         sets.append((Sq, bits, norms, out))
-    for i in range(2 * n_sets):
-        Sq, bits, norms, out = sets[i % n_sets]
-        qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k, scores_out=out)
-    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
-    for i in range(iters):
+
+    def call(i):
         Sq, bits, norms, out = sets[i % n_sets]
-        evs[i][0].record(st)
         qj.score(sk, Sq, bits, norms, w.groups, w.n_q, w.n_k, scores_out=out, stream=st)
-        evs[i][1].record(st)
-    torch.cuda.synchronize()
-    ts = sorted(a.seconds_to(b) for a, b in evs)
+
+    warm_up(torch, call, n_sets, score_bytes(w) / 5e12)
+    ts = per_call_times(torch, call, iters)
     del sets
     torch.cuda.empty_cache()
     pct = lambda p: ts[min(len(ts) - 1, int(p * len(ts)))]
@@ -527,16 +554,8 @@ def time_attention_rotating(qj, torch, w, sk, n_sets: int, iters: int, d_v: int 
         qj.decode_attention(sk, Sq, bits, norms, V, w.groups, w.n_q, w.n_k, scale,
                             workspace=ws, out=out, stream=st)
 
-    for i in range(2 * n_sets):
-        call(i)
-    torch.cuda.synchronize()
-    evs = [(HipEvent(), HipEvent()) for _ in range(iters)]
-    for i in range(iters):
-        evs[i][0].record(st)
-        call(i)
-        evs[i][1].record(st)
-    torch.cuda.synchronize()
-    ts = sorted(a.seconds_to(b) for a, b in evs)
+    warm_up(torch, call, n_sets, attention_bytes(w, d_v) / 5e12)
+    ts = per_call_times(torch, call, iters)
     del sets, ws
     torch.cuda.empty_cache()
     pct = lambda p: ts[min(len(ts) - 1, int(p * len(ts)))]
@@ -719,6 +738,8 @@ def main():
     dev = "cuda:0"
     w = wl.DECODE_7B
     K = wl.make_keys(w, dev)
+    # the oracle's copy of the keys, taken now: the copy leaves the GPU idle
+    K_host = K.cpu() if not args.no_cpu_baseline else None
     q = wl.make_queries(w, dev)
     sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
     norms = torch.empty(w.n_keys, dtype=torch.float32, device=dev)
@@ -746,14 +767,18 @@ def main():
     # step time covers; the chip's clock falls within milliseconds of
     # sustained load, so a separate pass would see another clock.  The event
     # records stay inside the step time.
+    # Python's garbage collector stays off while the steps are enqueued.
+    import gc
     evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     t_start, t_end = HipEvent(), HipEvent()
     torch.cuda.synchronize()
+    gc.disable()
     t_start.record(st)
     for i in range(args.steps):
         step(evs[i])
     t_end.record(st)
     torch.cuda.synchronize()
+    gc.enable()
     total_s = t_start.seconds_to(t_end)
     per_step = total_s / args.steps
     q_times = [a.seconds_to(b) for a, b in evs]
@@ -814,16 +839,16 @@ def main():
                                   "quantize_bytes": rc612}
         if rc612:
             result["roofline"]["frac_read_ceiling"] = achieved / rc612["GBps"]
-        result["score_decode7b"] = {"GBps": sb / s_mean / 1e9, "frac_hbm": sb / s_mean / 1e9 / HBM_PEAK_GBPS,
-                                    "frac_read_ceiling": (sb / s_mean / 1e9 / rc84["GBps"]
+        result["score_decode7b"] = {"GBps": sb / s_med / 1e9, "frac_hbm": sb / s_med / 1e9 / HBM_PEAK_GBPS,
+                                    "frac_read_ceiling": (sb / s_med / 1e9 / rc84["GBps"]
                                                           if rc84 else None),
-                                    "frac_copy_peak": sb / s_mean / 1e9 / copy_gbps,
-                                    "scores_per_s": w.groups * w.n_q * w.n_k / s_mean,
+                                    "frac_copy_peak": sb / s_med / 1e9 / copy_gbps,
+                                    "scores_per_s": w.groups * w.n_q * w.n_k / s_med,
                                     "mean_s": s_mean, "median_s": s_med, "p10_s": s_p10,
                                     "p90_s": s_p90, "bytes": sb,
                                     "rotation": "4 sets x 75.8 MB",
+                                    "statistic": "median of 100 per-call HIP-event times",
                                     "warm_median_s": sw_med, "warm_GBps": sb / sw_med / 1e9}
-        K_host = K.cpu() if not args.no_cpu_baseline else None
         del K
         torch.cuda.empty_cache()
         wl2 = wl.LONG_CTX
@@ -831,15 +856,16 @@ def main():
         sb2 = score_bytes(wl2)
         s2_mean, s2_med, s2_p10, s2_p90 = time_score_rotating(qj, torch, wl2, sk2, n_sets=2,
                                                               iters=100)
-        result["score_long_context"] = {"workload": wl2.name, "GBps": sb2 / s2_mean / 1e9,
-                                        "frac_hbm": sb2 / s2_mean / 1e9 / HBM_PEAK_GBPS,
-                                        "frac_read_ceiling": (sb2 / s2_mean / 1e9 / rc302["GBps"]
+        result["score_long_context"] = {"workload": wl2.name, "GBps": sb2 / s2_med / 1e9,
+                                        "frac_hbm": sb2 / s2_med / 1e9 / HBM_PEAK_GBPS,
+                                        "frac_read_ceiling": (sb2 / s2_med / 1e9 / rc302["GBps"]
                                                               if rc302 else None),
-                                        "frac_copy_peak": sb2 / s2_mean / 1e9 / copy_gbps,
-                                        "scores_per_s": wl2.groups * wl2.n_k / s2_mean,
+                                        "frac_copy_peak": sb2 / s2_med / 1e9 / copy_gbps,
+                                        "scores_per_s": wl2.groups * wl2.n_k / s2_med,
                                         "mean_s": s2_mean, "median_s": s2_med,
                                         "p10_s": s2_p10, "p90_s": s2_p90, "bytes": sb2,
-                                        "rotation": "2 sets x 302 MB"}
+                                        "rotation": "2 sets x 302 MB",
+                                        "statistic": "median of 100 per-call HIP-event times"}
         # decode-step attention on the scores (fused: the scores never reach HBM)
         for name, wa, sk_a, n_sets in (("attention_decode7b", w, sk, 2),
                                        ("attention_long_context", wl2, sk2, 2)):
@@ -847,14 +873,14 @@ def main():
             a_mean, a_med, a_p10, a_p90 = time_attention_rotating(qj, torch, wa, sk_a, n_sets,
                                                                   iters=50)
             result[name] = {"workload": wa.name, "values": "bf16, d_v 128",
-                            "GBps": ab / a_mean / 1e9,
-                            "frac_hbm": ab / a_mean / 1e9 / HBM_PEAK_GBPS,
-                            "frac_copy_peak": ab / a_mean / 1e9 / copy_gbps,
-                            "keys_per_s": wa.groups * wa.n_k / a_mean,
+                            "GBps": ab / a_med / 1e9,
+                            "frac_hbm": ab / a_med / 1e9 / HBM_PEAK_GBPS,
+                            "frac_copy_peak": ab / a_med / 1e9 / copy_gbps,
+                            "keys_per_s": wa.groups * wa.n_k / a_med,
                             "mean_s": a_mean, "median_s": a_med, "p10_s": a_p10,
                             "p90_s": a_p90, "bytes": ab,
                             "timing": "HIP events around each call (partials + combine), "
-                                      f"{n_sets} input sets rotated"}
+                                      f"{n_sets} input sets rotated; rates from the median"}
         sk2.close()
         # the other quantize configurations (same 2,097,152-key cache size)
         for name, wq in (("quantize_prefill", wl.PREFILL), ("quantize_fqjl", wl.FQJL_7B),
@@ -869,8 +895,6 @@ def main():
                             "timing": "10 launches back to back"}
         result["decode_time"] = decode_time_extras(qj, torch, w, sk)
     if not args.no_cpu_baseline:
-        if args.skip_extras:
-            K_host = K.cpu()
         result["cpu_baseline"] = cpu_baseline(w, K_host, args.cpu_seconds)
     sk.close()
     print(json.dumps(result), flush=True)

@@ -164,6 +164,10 @@ qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t
  * norms_out: device float[n_keys]; bits_out: device uint32[n_keys][m/32].
  * Keys are expected finite: the bits and norm of a row holding NaN or
  * infinity are unspecified (no error is raised).
+ * Environment: QJL_DENSE_SCHEDULE = prefetch, rt4 or immediate selects another
+ * register schedule of the dense bfloat16 quantizer for calls of more than
+ * 16384 keys at m <= 256 (any other value, or none, the default); every
+ * schedule gives identical bits and norms, only the time differs.
  * Errors: NULL pointers (n_keys > 0), n_keys < 0, key_index_base < 0, bad
  * dtype, misalignment, sketch of another device -> INVALID_ARGUMENT;
  * launch failure -> DEVICE.
