@@ -503,9 +503,31 @@ def warm_up(torch, call, n_sets: int, est_s: float):
     torch.cuda.synchronize()
 
 
+def back_to_back_mean(torch, call, iters: int) -> float:
+    """Mean seconds per call of `iters` calls enqueued back to back between one
+    pair of events (launch gaps included), garbage collector off."""
+    import gc
+    st = torch.cuda.current_stream()
+    a, b = HipEvent(), HipEvent()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        a.record(st)
+        for i in range(iters):
+            call(i)
+        b.record(st)
+        torch.cuda.synchronize()
+    finally:
+        if was:
+            gc.enable()
+    return a.seconds_to(b) / iters
+
+
 def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
     """Score kernel alone over `n_sets` distinct (bits, norms, Sq) sets, so the
-    working set exceeds the 256 MB Infinity Cache; returns mean seconds."""
+    working set exceeds the 256 MB Infinity Cache: mean, median, p10 and p90
+    seconds of per-call event times, then the mean of the same number of
+    calls back to back."""
     import workloads as wl
     dev = "cuda:0"
     sets = []
@@ -523,10 +545,11 @@ def time_score_rotating(qj, torch, w, sk, n_sets: int, iters: int):
 
     warm_up(torch, call, n_sets, score_bytes(w) / 5e12)
     ts = per_call_times(torch, call, iters)
+    b2b = back_to_back_mean(torch, call, iters)
     del sets
     torch.cuda.empty_cache()
     pct = lambda p: ts[min(len(ts) - 1, int(p * len(ts)))]
-    return sum(ts) / len(ts), ts[len(ts) // 2], pct(0.1), pct(0.9)
+    return sum(ts) / len(ts), ts[len(ts) // 2], pct(0.1), pct(0.9), b2b
 
 
 def time_attention_rotating(qj, torch, w, sk, n_sets: int, iters: int, d_v: int = 128):
@@ -831,21 +854,22 @@ def main():
         # (cold), and the same call on one input set that stays in that cache
         # (warm).
         sb = score_bytes(w)
-        s_mean, s_med, s_p10, s_p90 = time_score_rotating(qj, torch, w, sk, n_sets=4, iters=100)
-        _, sw_med, _, _ = time_score_rotating(qj, torch, w, sk, n_sets=1, iters=100)
+        s_mean, s_med, s_p10, s_p90, s_b2b = time_score_rotating(qj, torch, w, sk, n_sets=4,
+                                                                 iters=100)
+        _, sw_med, _, _, _ = time_score_rotating(qj, torch, w, sk, n_sets=1, iters=100)
         del K
         torch.cuda.empty_cache()
         wl2 = wl.LONG_CTX
         sk2 = qj.make_sketch(wl2.seed, wl2.d, wl2.m, wl2.variant)
         sb2 = score_bytes(wl2)
-        s2_mean, s2_med, s2_p10, s2_p90 = time_score_rotating(qj, torch, wl2, sk2, n_sets=2,
-                                                              iters=100)
+        s2_mean, s2_med, s2_p10, s2_p90, s2_b2b = time_score_rotating(qj, torch, wl2, sk2,
+                                                                      n_sets=2, iters=100)
         # decode-step attention on the scores (fused: the scores never reach HBM)
         att = {}
         for name, wa, sk_a, n_sets in (("attention_decode7b", w, sk, 2),
                                        ("attention_long_context", wl2, sk2, 2)):
             att[name] = (wa, attention_bytes(wa), n_sets,
-                         time_attention_rotating(qj, torch, wa, sk_a, n_sets, iters=50))
+                         time_attention_rotating(qj, torch, wa, sk_a, n_sets, iters=100))
         sk2.close()
         # the probes: torch's device copy and the plain-read ceilings
         copy_gbps = copy_peak_gbps(torch)
@@ -867,6 +891,7 @@ def main():
                                     "p90_s": s_p90, "bytes": sb,
                                     "rotation": "4 sets x 75.8 MB",
                                     "statistic": "median of 100 per-call HIP-event times",
+                                    "back_to_back_mean_s": s_b2b,
                                     "warm_median_s": sw_med, "warm_GBps": sb / sw_med / 1e9}
         result["score_long_context"] = {"workload": wl2.name, "GBps": sb2 / s2_med / 1e9,
                                         "frac_hbm": sb2 / s2_med / 1e9 / HBM_PEAK_GBPS,
@@ -877,7 +902,8 @@ def main():
                                         "mean_s": s2_mean, "median_s": s2_med,
                                         "p10_s": s2_p10, "p90_s": s2_p90, "bytes": sb2,
                                         "rotation": "2 sets x 302 MB",
-                                        "statistic": "median of 100 per-call HIP-event times"}
+                                        "statistic": "median of 100 per-call HIP-event times",
+                                        "back_to_back_mean_s": s2_b2b}
         for name, (wa, ab, n_sets, (a_mean, a_med, a_p10, a_p90)) in att.items():
             result[name] = {"workload": wa.name, "values": "bf16, d_v 128",
                             "GBps": ab / a_med / 1e9,
