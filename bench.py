@@ -205,6 +205,14 @@ def kernel_tu_hash(src: str = QUANT_KERNEL_SRC) -> str:
 
 
 DENSE_SCHEDULES = ("default", "prefetch", "rt4", "immediate")
+# The instantiation each schedule launches at the 7B decode shape (d = 128,
+# m = 256): <D, M, WAVES, RT, R, DEFER, PF, MAPPED>, as kernel traces name it.
+DENSE_KERNEL_7B = {
+    "default": "quantize_mfma_kernel<128, 256, 4, 2, 4, true, false, false>",
+    "prefetch": "quantize_mfma_kernel<128, 256, 4, 2, 2, true, true, false>",
+    "rt4": "quantize_mfma_kernel<128, 256, 4, 4, 2, false, false, false>",
+    "immediate": "quantize_mfma_kernel<128, 256, 4, 2, 4, false, false, false>",
+}
 
 
 def dense_schedule() -> str:
@@ -834,7 +842,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "context": w.n_k,
                    "head_dim": w.d, "m": w.m, "sketch": w.variant, "queries_per_head": w.n_q,
                    "keys": "bf16 N(0,1), 4 outlier channels x15 per head"},
-        "roofline": {"kernel": "quantize_mfma_kernel<128,256>", "bound": "hbm",
+        "roofline": {"kernel": DENSE_KERNEL_7B[dense_schedule()], "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": qbytes, "avg_launch_s": q_avg,

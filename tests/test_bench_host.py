@@ -95,3 +95,11 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "exactly one GPU" in r.stderr
+
+
+def test_each_schedule_names_the_kernel_its_profile_lists():
+    assert set(bench.DENSE_KERNEL_7B) == set(bench.DENSE_SCHEDULES)
+    text = open(os.path.join(ROOT, "profiles",
+                             "quantize_dense_llama7b_decode_schedules.txt")).read()
+    for schedule, kernel in bench.DENSE_KERNEL_7B.items():
+        assert f"{schedule:10s} {kernel}" in text, schedule
