@@ -24,9 +24,9 @@ Derived variates (all in float64 unless stated):
     N(i)  = sqrt(-2 ln U(2i)) * cos(2 pi U(2i+1))           (Box and Muller, 1958)
 
 Streams: 0 dense S, 1 Rademacher diagonal D, 2 permutation P, 3 Gaussian
-diagonal G, 4 dither.  The dither stream draws one word per coordinate pair
-(see ``dither_pairs``) so a GPU can evaluate it in fp32 from 24-bit
-uniforms that are exact in both precisions.
+diagonal G, 4 dither.  The dither stream draws one word per two coordinate
+pairs (see ``dither_pairs``): each 32-bit half gives a 20-bit radius uniform
+and one of 4096 equally spaced angles, both exact in fp32 and fp64 alike.
 """
 from __future__ import annotations
 
@@ -116,26 +116,35 @@ def gaussian_fast(seed: int, stream: int, idx) -> np.ndarray:
 def dither_pairs(seed: int, key_index: np.ndarray, m: int) -> np.ndarray:
     """Dither noise xi[i, j] for global key indices ``key_index`` and j < m.
 
-    For key i and coordinate pair p < m/2 one word h = r(seed, 4, i*(m/2) + p)
-    gives two 24-bit integers a = h >> 40 and b = (h >> 16) & 0xFFFFFF, and
+    Key i draws m/4 words h_w = r(seed, 4, i*(m/4) + w), w < m/4; word w
+    serves coordinate pairs p = 2w (its high 32 bits) and p = 2w + 1 (its low
+    32 bits).  From a 32-bit half v: a = v >> 12 (20 bits), k = v & 0xFFF, and
 
-        u1 = (a + 1) * 2**-24  in (0, 1],   u2 = b * 2**-24  in [0, 1)
-        R  = sqrt(-2 ln u1),   theta = 2 pi u2
+        u1 = (a + 1) * 2**-20  in (0, 1],   R = sqrt(-2 ln u1)
+        theta = 2 pi (k + 1/2) / 4096
         xi[i, 2p] = R cos(theta),   xi[i, 2p+1] = R sin(theta)
 
-    (the two outputs of one Box-Muller draw).  u1 and u2 are exact in fp32
-    and fp64 alike.
+    Box-Muller (1958) with the angle on 4096 equally spaced values, offset by
+    half a step so that no angle has a zero cosine or sine.  The radius is
+    Rayleigh as in the continuous method (its top 2**-20 of tail mass cut),
+    and since the average of exp(i n theta) over the angles vanishes for
+    0 < |n| < 4096, every joint moment of (xi_2p, xi_2p+1) of total order
+    below 4096 equals that of two independent standard normals.
     """
     key_index = np.asarray(key_index, dtype=np.uint64).reshape(-1)
-    half = m // 2
-    ctr = key_index[:, None] * np.uint64(half) + np.arange(half, dtype=np.uint64)[None, :]
+    if m % 4:
+        raise ValueError("the dither draws one word per two coordinate pairs: m % 4 == 0")
+    words = m // 4
+    ctr = key_index[:, None] * np.uint64(words) + np.arange(words, dtype=np.uint64)[None, :]
     h = draw(seed, STREAM_DITHER, ctr)
-    a = (h >> np.uint64(40)).astype(np.float64)
-    b = ((h >> np.uint64(16)) & np.uint64(0xFFFFFF)).astype(np.float64)
-    u1 = (a + 1.0) * 2.0 ** -24
-    u2 = b * 2.0 ** -24
+    halves = np.empty((key_index.shape[0], 2 * words), dtype=np.uint64)
+    halves[:, 0::2] = h >> np.uint64(32)                    # pair 2w
+    halves[:, 1::2] = h & np.uint64(0xFFFFFFFF)             # pair 2w + 1
+    a = (halves >> np.uint64(12)).astype(np.float64)
+    k = (halves & np.uint64(0xFFF)).astype(np.float64)
+    u1 = (a + 1.0) * 2.0 ** -20
     rad = np.sqrt(-2.0 * np.log(u1))
-    th = TWO_PI * u2
+    th = TWO_PI * (k + 0.5) / 4096.0
     out = np.empty((key_index.shape[0], m), dtype=np.float64)
     out[:, 0::2] = rad * np.cos(th)
     out[:, 1::2] = rad * np.sin(th)

@@ -69,6 +69,30 @@ def test_dither_pairs_moments_and_independence():
     assert np.array_equal(rng.dither_pairs(0, [7], 64), rng.dither_pairs(0, np.array([7]), 64))
 
 
+def test_dither_is_gaussian_where_the_estimator_needs_it():
+    # One word serves two coordinate pairs, each from 32 bits: the noise must
+    # still behave as N(0, 1) in the ways the estimator uses.
+    xi = rng.dither_pairs(5, np.arange(2000), 256)
+    v = xi.reshape(-1)
+    n = v.size
+    # higher moments of N(0, 1): E xi^4 = 3, E xi^6 = 15 (4 standard errors)
+    for p, mom in ((4, 3.0), (6, 15.0)):
+        se = math.sqrt((math.prod(range(2 * p - 1, 0, -2)) - mom * mom) / n)
+        assert abs(np.mean(v ** p) - mom) < 4 * se, p
+    # the dither factor sqrt(1 + rho^2) rests on E exp(-t xi^2) = 1 / sqrt(1 + 2t)
+    for t in (0.005, 0.5, 2.0):
+        e = np.exp(-t * v * v)
+        assert abs(e.mean() - 1 / math.sqrt(1 + 2 * t)) < 4 * e.std() / math.sqrt(n), t
+    # no point mass at zero (an angle grid with a zero cosine would put 1/128
+    # of the draws there): |xi| < 1e-4 as often as a normal density gives
+    # (P = 8.0e-5, ~41 of 512,000)
+    assert np.count_nonzero(np.abs(v) < 1e-4) < 100
+    # the two pairs drawn from one word (its two halves) are uncorrelated
+    for a, b in ((0, 2), (1, 3), (0, 3)):
+        c = np.corrcoef(xi[:, a::4].reshape(-1), xi[:, b::4].reshape(-1))[0, 1]
+        assert abs(c) < 4 / math.sqrt(xi[:, a::4].size), (a, b)
+
+
 @pytest.mark.parametrize("d", [2, 4, 8, 16, 32, 64])
 def test_sylvester_matches_scipy_and_is_orthogonal(d):
     H = sketch.sylvester(d)
