@@ -82,46 +82,50 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_
   return bf16_bits_to_f32(p[i]);
 }
 
-// Dither draw for one coordinate pair (D-FQJL's Gaussian dither, "Fast
-// Quantized Johnson-Lindenstrauss Transforms" page).  One SplitMix64 word
-// h = r(seed, 4, ctr) per pair; a = h >> 40 and b = (h >> 16) & 0xFFFFFF give
-// u1 = (a + 1) 2^-24 and u2 = b 2^-24 (exact in float32); Box-Muller returns
-// R cos(2 pi u2) for the even and R sin(2 pi u2) for the odd coordinate.
-// The gfx950 transcendental instructions evaluate it directly: v_log_f32 is
-// log2 (R^2 = -2 ln 2 log2 u1), v_sin_f32 / v_cos_f32 take their argument in
-// revolutions (sin(2 pi u2) = v_sin_f32(u2), u2 in [0, 1)).  Their float32
-// errors move a dither value by ~1e-6 of its size, far below the band of
-// coordinates whose sign is not compared bit for bit.
-// From the generator's state key + PHI (ctr + 1) (stream_draw's argument to
-// mix64): a loop over consecutive counters forms the state once and adds
-// multiples of PHI, which the compiler would otherwise fold back into a
-// 64-bit multiply-add per pair.
-__device__ __forceinline__ void dither_pair_state(uint64_t state, float &xc, float &xs) {
-  const uint64_t h = mix64(state);
-  const uint32_t a = (uint32_t)(h >> 40);
-  const uint32_t b = (uint32_t)(h >> 16) & 0xFFFFFFu;
-  const float u1 = (float)(a + 1u) * 0x1p-24f;
-  const float u2 = (float)b * 0x1p-24f;
+// Dither draws (D-FQJL's Gaussian dither, "Fast Quantized Johnson-Lindenstrauss
+// Transforms" page).  Key i draws one SplitMix64 word per two coordinate
+// pairs, h = r(seed, 4, i m/4 + w); the high 32 bits of word w serve pair 2w,
+// the low 32 bits pair 2w + 1.  From a half v: u1 = ((v >> 12) + 1) 2^-20 and
+// the angle 2 pi ((v & 0xFFF) + 1/2) / 4096 (both exact in float32), and
+// Box-Muller returns R cos for the even and R sin for the odd coordinate, with
+// R = sqrt(-2 ln u1).  The gfx950 transcendental instructions evaluate it
+// directly: v_log_f32 is log2 (R^2 = -2 ln 2 log2 u1), v_sin_f32 / v_cos_f32
+// take their argument in revolutions, here (2 (v & 0xFFF) + 1) 2^-13 exactly.
+// Their float32 errors move a dither value by ~1e-6 of its size, far below
+// the band of coordinates whose sign is not compared bit for bit.
+__device__ __forceinline__ void dither_half(uint32_t v, float &xc, float &xs) {
+  const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
+  const float t = (float)(2u * (v & 0xFFFu) + 1u) * 0x1p-13f;
   const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
-  xc = r * __builtin_amdgcn_cosf(u2);
-  xs = r * __builtin_amdgcn_sinf(u2);
+  xc = r * __builtin_amdgcn_cosf(t);
+  xs = r * __builtin_amdgcn_sinf(t);
 }
 
-__device__ __forceinline__ void dither_pair(uint64_t key, uint64_t ctr, float &xc, float &xs) {
-  dither_pair_state(key + PHI * (ctr + 1), xc, xs);
+// The four values of one word (coordinates 4w .. 4w + 3 of its key), from the
+// generator's state key + PHI (ctr + 1) (stream_draw's argument to mix64): a
+// loop over consecutive words forms the state once and adds multiples of
+// PHI, which the compiler would otherwise fold back into a 64-bit
+// multiply-add per word.
+__device__ __forceinline__ void dither_word_state(uint64_t state, float (&x)[4]) {
+  const uint64_t h = mix64(state);
+  dither_half((uint32_t)(h >> 32), x[0], x[1]);
+  dither_half((uint32_t)h, x[2], x[3]);
 }
 
-// State of counter ctr, opaque to the optimiser (an empty asm on its
-// register pair), so that state + PHI k stays one 64-bit add per pair.
+// State of word counter ctr, opaque to the optimiser (an empty asm on its
+// register pair), so that state + PHI k stays one 64-bit add per word.
 __device__ __forceinline__ uint64_t dither_state(uint64_t key, uint64_t ctr) {
   uint64_t s = key + PHI * (ctr + 1);
   asm volatile("" : "+v"(s));
   return s;
 }
 
+// Coordinate j of key key_index's dither (m coordinates per key).
 __device__ __forceinline__ float dither_one(uint64_t key, uint64_t key_index, int m, int j) {
+  const uint64_t h = mix64(key + PHI * (key_index * (uint64_t)(m / 4) + (uint64_t)(j >> 2) + 1));
+  const uint32_t v = (j & 2) ? (uint32_t)h : (uint32_t)(h >> 32);
   float c, s;
-  dither_pair(key, key_index * (uint64_t)(m / 2) + (uint64_t)(j >> 1), c, s);
+  dither_half(v, c, s);
   return (j & 1) ? s : c;
 }
 

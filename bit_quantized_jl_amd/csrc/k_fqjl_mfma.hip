@@ -219,15 +219,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
         const int64_t orow = MAPPED ? map_row(map, key < n ? key : 0) : (key < n ? key : 0);
         if (DITHER) {
           const float amp = rho * nrm[rt];
-          const uint64_t pair0 =
-              (uint64_t)(base + orow) * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
-          const uint64_t st0 = dither_state(dkey, pair0);
+          const uint64_t word0 =
+              (uint64_t)(base + orow) * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
+          const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-          for (int c = 0; c < 64; c += 2) {
-            float xc, xs;
-            dither_pair_state(st0 + PHI * (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
-            z[c] += amp * xc;
-            z[c + 1] += amp * xs;
+          for (int c = 0; c < 64; c += 4) {
+            float x[4];
+            dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[c + e] += amp * x[e];
           }
         }
         const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
@@ -295,22 +295,22 @@ __device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const f
   }
 }
 
-// fm_finish: dither of size amp with the pair counters of output row drow
+// fm_finish: dither of size amp with the word counters of output row drow
 // (the coordinates fm_transform left in lane half h), sign, and the two
 // words: 4 b + h and 4 b + 2 + h of the row.
 template <int M, bool DITHER>
 __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float amp, uint64_t dkey,
                                           int64_t drow, uint32_t &w0, uint32_t &w1) {
   if (DITHER) {
-    const uint64_t pair0 =
-        (uint64_t)drow * (uint64_t)(M / 2) + (uint64_t)((128 * b + 32 * h) / 2);
-    const uint64_t st0 = dither_state(dkey, pair0);
+    const uint64_t word0 =
+        (uint64_t)drow * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
+    const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-    for (int c = 0; c < 64; c += 2) {
-      float xc, xs;
-      dither_pair_state(st0 + PHI * (uint64_t)(c / 2 + (c >= 32 ? 16 : 0)), xc, xs);
-      z[c] += amp * xc;
-      z[c + 1] += amp * xs;
+    for (int c = 0; c < 64; c += 4) {
+      float x[4];
+      dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[c + e] += amp * x[e];
     }
   }
   w0 = pack_signs(&z[0]);

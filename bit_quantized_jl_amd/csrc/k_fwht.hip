@@ -117,15 +117,15 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
       } else {
         if (DITHER) {
           const float amp = rho * nrm;
-          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) +
-                                 (uint64_t)(b * D / 2);
-          const uint64_t st0 = dither_state(dkey, pair0);
+          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) +
+                                 (uint64_t)(b * D / 4);
+          const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-          for (int c = 0; c < D; c += 2) {
-            float xc, xs;
-            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
-            u[c] += amp * xc;
-            u[c + 1] += amp * xs;
+          for (int c = 0; c < D; c += 4) {
+            float x[4];
+            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[c + e] += amp * x[e];
           }
         }
         if (valid) {
@@ -265,14 +265,14 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
       } else {
         if (DITHER) {
           const float amp = rho * nrm;
-          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
-          const uint64_t st0 = dither_state(dkey, pair0);
+          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) + (uint64_t)(j0 / 4);
+          const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-          for (int c = 0; c < H; c += 2) {
-            float xc, xs;
-            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
-            t[c] += amp * xc;
-            t[c + 1] += amp * xs;
+          for (int c = 0; c < H; c += 4) {
+            float x[4];
+            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[c + e] += amp * x[e];
           }
         }
         if (valid) {
@@ -386,14 +386,14 @@ __global__ __launch_bounds__(64) void fqjl256_kernel(
       } else {
         if (DITHER) {
           const float amp = rho * nrm;
-          const uint64_t pair0 = (uint64_t)(base + orow) * (uint64_t)(m / 2) + (uint64_t)(j0 / 2);
-          const uint64_t st0 = dither_state(dkey, pair0);
+          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) + (uint64_t)(j0 / 4);
+          const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-          for (int c = 0; c < H; c += 2) {
-            float xc, xs;
-            dither_pair_state(st0 + PHI * (uint64_t)(c / 2), xc, xs);
-            t[c] += amp * xc;
-            t[c + 1] += amp * xs;
+          for (int c = 0; c < H; c += 4) {
+            float x[4];
+            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[c + e] += amp * x[e];
           }
         }
         if (valid) {
