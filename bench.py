@@ -160,9 +160,10 @@ def translation_unit_files(src: str) -> list:
 
 
 def dither_cost():
-    """Nanoseconds per dither pair for the whole chip (all lanes busy), for the
-    generator word plus Box-Muller, the word alone and Box-Muller alone, and
-    what the first costs at the 7B FQJL shape (2,097,152 keys x 128 pairs)."""
+    """Picoseconds per dither pair for the whole chip (every lane drawing: the
+    launch time over the pairs all lanes draw), for the generator word plus
+    Box-Muller, the word alone and Box-Muller alone, and what the first costs
+    at the 7B FQJL shape (2,097,152 keys x 128 pairs)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(PROBE_LIB)
@@ -184,10 +185,10 @@ def dither_cost():
             assert fn(mode, grid, pairs, out.data_ptr(), st.cuda_stream) == 0
         b.record(st)
         torch.cuda.synchronize()
-        res[name + "_ns_per_pair"] = a.seconds_to(b) / 5 / total * 1e9
+        res[name + "_ps_per_pair"] = a.seconds_to(b) / 5 / total * 1e12
     pairs_7b = 2097152 * 128
     res["fqjl_7b_pairs"] = pairs_7b
-    res["fqjl_7b_draw_us_at_full_vector_rate"] = res["word_and_box_muller_ns_per_pair"] * pairs_7b / 1e3
+    res["fqjl_7b_draw_us_at_full_vector_rate"] = res["word_and_box_muller_ps_per_pair"] * pairs_7b / 1e6
     print(json.dumps({"dither_cost": res}), flush=True)
 
 

@@ -225,5 +225,6 @@ def test_probe_library_loads():
     dc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert dc(0, 1, 1, None, None) == 1                 # no output buffer
     assert dc(3, 1, 1, 16, None) == 1                   # bad mode
-    assert dc(0, 0, 1, 16, None) == 1                   # empty grid
+    assert dc(0, 0, 2, 16, None) == 1                   # empty grid
+    assert dc(0, 1, 3, 16, None) == 1                   # pairs come in twos (one word each)
     assert "qjl_probe_read" not in {n for n in dir(qj.load()) if n.startswith("qjl_")}
