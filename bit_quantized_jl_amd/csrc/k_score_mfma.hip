@@ -251,8 +251,8 @@ __device__ __forceinline__ void score_stage(const StageRead<T> &sr, const QueryO
 }
 
 // With DEFER the scores of a pass stay in LDS (sDefer: [queries][chunk]) and
-// leave at the end of the workgroup's keys as 16-byte non-temporal stores;
-// otherwise each stage stores its own.
+// each wave writes those of its own stages as 16-byte non-temporal stores when
+// its last stage is done; otherwise each stage stores its own.
 template <int T, int QP, bool DEFER>
 __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
@@ -312,17 +312,19 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
                                   out + (g * nq + q0) * nk, nk, sDefer, chunk);
       }
       if constexpr (DEFER) {
-        // every wave's scores are in LDS; then the workgroup writes them, four
-        // consecutive keys per lane (scalar stores where a row is not 16-byte
-        // aligned or for the last few keys)
+        // each wave writes the scores of its own 64-key blocks (keys
+        // kbeg + 64 (wave + 4 j)) as soon as its stages are done: it wrote
+        // those LDS slots itself, so no workgroup barrier is needed; 16 lanes
+        // cover one block, four consecutive keys each
+        __builtin_amdgcn_s_waitcnt((15 & 15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
         asm volatile("" ::: "memory");
-        lds_barrier();
         const int nkb = (int)(kend - kbeg);
         for (int qi = 0; qi < nqp; ++qi) {
           float *dst = out + (g * nq + q0 + qi) * nk + kbeg;
           const float *srcq = sDefer + qi * chunk;
           const bool vec = ((uintptr_t)dst & 15) == 0;
-          for (int i = 4 * tid; i < nkb; i += 4 * SM_THREADS) {
+          for (int j = lane >> 4; j < ns; j += 4) {
+            const int i = SM_STAGE * (wave + SM_WAVES * j) + 4 * (lane & 15);
             if (vec && i + 3 < nkb) {
               const v4f_t v = *reinterpret_cast<const v4f_t *>(srcq + i);
               __builtin_nontemporal_store(v, reinterpret_cast<v4f_t *>(dst + i));
@@ -332,9 +334,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
             }
           }
         }
-        // the next pass (more queries, or another group) writes sDefer again
         asm volatile("" ::: "memory");
-        lds_barrier();
       }
     }
   }
