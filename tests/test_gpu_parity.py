@@ -114,6 +114,24 @@ def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     run_quantize_case(w, base=3)
 
 
+@pytest.mark.parametrize("variant,d,m,dt,n", [
+    ("fqjl", 128, 256, "bf16", 20000),   # persistent matrix-core kernel
+    ("fqjl", 128, 256, "bf16", 300),     # short-call matrix-core kernel
+    ("dfqjl", 128, 512, "bf16", 300),
+    ("fqjl", 128, 256, "f32", 300),      # two lanes per row
+    ("fqjl", 64, 128, "bf16", 300),      # one lane per row
+    ("fqjl", 256, 512, "bf16", 300),     # four lanes per row
+    ("fqjl", 16, 64, "f32", 300),        # small d
+    ("dense", 128, 256, "bf16", 300)])   # dense sketch with dither
+def test_dither_counters_at_large_key_indices(variant, d, m, dt, n):
+    # The dither's word counter is (key index) * m/4 + word in 64 bits: key
+    # indices past 2^32, whose products with m/4 pass 2^40, must give the
+    # oracle's draws in every kernel that dithers.
+    w = wl.Workload(f"bigindex_{variant}_{d}_{m}_{dt}", d, m, variant, 1, 1, n, 5, dt, "normal",
+                    0.2, seed=8)
+    run_quantize_case(w, base=(1 << 40) + 12345)
+
+
 @pytest.mark.parametrize("d,m", [(64, 128), (64, 256), (128, 128), (128, 256)])
 def test_dense_schedules_identical(monkeypatch, d, m):
     # The dense quantizer's register schedules (QJL_DENSE_SCHEDULE): each one's
@@ -212,8 +230,21 @@ def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
     # Rows g * cap + first + i get key i of group g, quantized as the oracle
     # does with dither counter base + that row; every other row keeps its
     # sentinel.
-    note("quantize into cache", variant, d, m, dt, rho, G, kpg, cap, first)
-    base = 1234
+    _into_cache_case(variant, d, m, dt, rho, G, kpg, cap, first, 1234)
+
+
+@pytest.mark.parametrize("variant,d,m,dt,rho,G,kpg,cap,first", [
+    ("fqjl", 128, 256, "bf16", 0.1, 2, 9000, 9100, 50),   # persistent kernel, row map
+    ("fqjl", 128, 256, "bf16", 0.1, 6, 45, 64, 19),       # short-call kernel, row map
+    ("dense", 96, 64, "bf16", 0.3, 4, 33, 40, 5)])        # generic kernel
+def test_quantize_into_cache_at_large_key_indices(variant, d, m, dt, rho, G, kpg, cap, first):
+    # The same with a key index base past 2^40: the mapped rows' 64-bit
+    # dither counters.
+    _into_cache_case(variant, d, m, dt, rho, G, kpg, cap, first, (1 << 40) + 1234)
+
+
+def _into_cache_case(variant, d, m, dt, rho, G, kpg, cap, first, base):
+    note("quantize into cache", variant, d, m, dt, rho, G, kpg, cap, first, base)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     gen = torch.Generator().manual_seed(G * 7 + kpg + cap + first)
     K = (torch.randn(G * kpg, d, generator=gen) * 2).to(tdt)
