@@ -430,6 +430,37 @@ def test_score_random_bits(m, G, nq, nk):
     sk.close()
 
 
+@pytest.mark.parametrize("m,nq", [(256, 1), (512, 1), (1024, 3), (256, 6)])
+def test_score_query_edge_values(m, nq):
+    # The query becomes integers X_j = rint(Sq_j 2^F) with F set by its
+    # largest |Sq_j|: a zero query (F = 0, every score exactly 0), a query
+    # whose one large coordinate sets F, queries near the float32 denormal
+    # range and signed zeros, against the oracle on the same bits and norms.
+    note("score edge queries", m, nq)
+    G, nk = 3, 777
+    rs = np.random.default_rng(m + nq)
+    sk = qj.make_sketch(0, 128, m, "dense", 0.0)
+    bits = wl.make_random_bits(G * nk, m, seed=11).to(DEV)
+    norms = torch.from_numpy(np.abs(rs.standard_normal(G * nk)).astype(np.float32) * 10).to(DEV)
+    Sq = (rs.standard_normal((G * nq, m)) * 11).astype(np.float32)
+    Sq[0] = 0.0                                   # a zero query
+    Sq[1, :] = 1e-3
+    Sq[1, 7] = 3e7                                # one coordinate sets the exponent
+    Sq[2] = (rs.standard_normal(m) * 1e-36).astype(np.float32)   # tiny
+    if nq > 1:
+        Sq[3] = np.where(rs.random(m) < 0.5, -0.0, 0.0).astype(np.float32)  # signed zeros
+    Sqd = torch.from_numpy(Sq).to(DEV)
+    out = qj.score(sk, Sqd, bits, norms, G, nq, nk)
+    torch.cuda.synchronize()
+    ref = oq.score(to_np_f64(Sqd), bits_np(bits), to_np_f64(norms), m, 0.0, G, nq, nk)
+    got = to_np_f64(out)
+    check_scores(got, ref)
+    assert np.all(got[0, 0] == 0.0)
+    if nq > 1:
+        assert np.all(got[3 // nq, 3 % nq] == 0.0)   # query row 3: signed zeros
+    sk.close()
+
+
 @pytest.mark.parametrize("variant,d,m,dt,rho", [
     ("dense", 512, 64, "bf16", 0.0),      # largest dense d
     ("dense", 1, 32, "f32", 0.0),         # smallest d and m
