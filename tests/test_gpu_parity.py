@@ -561,6 +561,52 @@ def test_end_to_end_scores(w):
     sk.close()
 
 
+@pytest.mark.parametrize("variant,rho,n", [("dense", 0.0, 300), ("dense", 0.0, 20000),
+                                           ("dense", 0.3, 300), ("fqjl", 0.2, 300),
+                                           ("fqjl", 0.2, 20000), ("dfqjl", 0.1, 300)])
+def test_power_of_two_scaling_is_exact(variant, rho, n):
+    # Scaling bf16 keys by 2^e is exact and commutes with every float32
+    # product, sum and square root of the path (and the dither scales with
+    # the norm), so the bits are identical and the norms scale by exactly
+    # 2^e; scaling the projected queries scales every score by exactly 2^e.
+    note("power-of-two scaling", variant, rho, n)
+    d, m = 128, 256
+    gen = torch.Generator().manual_seed(n + int(rho * 10))
+    K = (torch.randn(n, d, generator=gen) * 3).to(torch.bfloat16).to(DEV)
+    sk = qj.make_sketch(13, d, m, variant, rho)
+    n0, b0 = qj.quantize_keys(sk, K, key_index_base=21)
+    q = (torch.randn(4, d, generator=gen)).to(torch.bfloat16).to(DEV)
+    Sq = qj.project_query(sk, q)
+    s0 = qj.score(sk, Sq, b0, n0, 1, 4, n)
+    for e in (50, -50):
+        f = 2.0 ** e
+        n1, b1 = qj.quantize_keys(sk, (K.float() * f).to(torch.bfloat16), key_index_base=21)
+        s1 = qj.score(sk, Sq * f, b0, n0, 1, 4, n)
+        torch.cuda.synchronize()
+        assert torch.equal(b1, b0), e
+        assert torch.equal(n1, n0 * f), e
+        assert torch.equal(s1, s0 * f), e
+    sk.close()
+
+
+@pytest.mark.parametrize("variant,n", [("dense", 300), ("dense", 20000), ("fqjl", 300),
+                                       ("fqjl", 20000), ("pfqjl", 300)])
+def test_negated_keys_complement_every_bit(variant, n):
+    # Without dither, negating a key negates every product and sum exactly,
+    # so each coordinate changes sign (none is exactly zero for these keys):
+    # the bits of -k are the complement of those of k, the norms are equal.
+    note("negated keys", variant, n)
+    gen = torch.Generator().manual_seed(n + 5)
+    K = (torch.randn(n, 128, generator=gen) * 3).to(torch.bfloat16).to(DEV)
+    sk = qj.make_sketch(17, 128, 256, variant, 0.0)
+    n0, b0 = qj.quantize_keys(sk, K)
+    n1, b1 = qj.quantize_keys(sk, -K)
+    torch.cuda.synchronize()
+    assert torch.equal(b1, ~b0)
+    assert torch.equal(n1, n0)
+    sk.close()
+
+
 def test_zero_key_and_empty_calls():
     note("edge zero/empty")
     for variant, dt in (("dense", torch.float32), ("dense", torch.bfloat16), ("fqjl", torch.bfloat16)):
