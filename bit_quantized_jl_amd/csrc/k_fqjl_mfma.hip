@@ -91,6 +91,19 @@ __device__ __forceinline__ void fm_load(FmKeys<T, RT> &kt, const uint16_t *__res
   }
 }
 
+// With dither up to m = 256 (unmapped launches), the cos and sin of the 4096
+// dither angles sit in LDS: 32 KB beside the image, so one 8-wave workgroup
+// per compute unit instead of two of 4 waves.  The table is built with the
+// instructions the other kernels evaluate inline (dither_angle), so the
+// draws are the same values.  (The row-mapped variant keeps the inline
+// angles: with the table it would spill.)
+#ifndef QJL_FM_DITHER_TABLE
+#define QJL_FM_DITHER_TABLE 1
+#endif
+constexpr bool fm_angle_table(int M, bool dither, bool mapped) {
+  return dither && !mapped && M <= 256 && QJL_FM_DITHER_TABLE;
+}
+
 template <int M, int WAVES, int RT, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Fimg,
@@ -99,13 +112,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
   constexpr int D = 128, T = D / 16, NB = M / D, W = M / 32;
   constexpr int NF = NB * 4 * T;  // S fragments per tile walk
   constexpr int R = FM_RING;
+  constexpr bool TAB = fm_angle_table(M, DITHER, MAPPED);
   __shared__ uint4 sF[M * D / 8];
   __shared__ float sG[M];
+  __shared__ float2 sCS[TAB ? 4096 : 1];
   const int tid = threadIdx.x;
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(Fimg);
     for (int i = tid; i < M * D / 8; i += 64 * WAVES) sF[i] = src[i];
     for (int i = tid; i < M; i += 64 * WAVES) sG[i] = fabsf(Gs[i]);
+    if constexpr (TAB)
+      for (int i = tid; i < 4096; i += 64 * WAVES) sCS[i] = dither_angle((uint32_t)i);
   }
   __syncthreads();
   const int lane = tid & 63;
@@ -225,7 +242,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
 #pragma unroll
           for (int c = 0; c < 64; c += 4) {
             float x[4];
-            dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
+            if constexpr (TAB)
+              dither_word_state_tab(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), sCS, x);
+            else
+              dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) z[c + e] += amp * x[e];
           }
@@ -444,7 +464,9 @@ hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t
     return hipGetLastError();
   }
   constexpr int RT = QJL_FM_RT;
-  constexpr int WAVES = M <= 256 ? 4 : 8;
+  // two 4-wave workgroups per compute unit, or one of 8 waves where the
+  // image (m = 512) or the dither's angle table leaves LDS for one
+  constexpr int WAVES = (M <= 256 && !fm_angle_table(M, DITHER, MAPPED)) ? 4 : 8;
   auto kern = fqjl_mfma_kernel<M, WAVES, RT, DITHER, MAPPED>;
   static PerDevice pd_res;  // workgroups resident on the whole device
   const int resident = per_device(pd_res, [&] { return resident_workgroups(kern, 64 * WAVES); });
