@@ -299,6 +299,16 @@ def score_bytes(w) -> float:
             + w.groups * w.n_q * w.m * 4)
 
 
+def score_write_bytes(w) -> float:
+    """The scores the score kernel writes (the rest of score_bytes is read)."""
+    return w.groups * w.n_q * w.n_k * 4
+
+
+def quantize_write_bytes(w) -> float:
+    """The bits and norms the quantize kernel writes (the keys are read)."""
+    return w.n_keys * (w.m / 8 + 4)
+
+
 def project_bytes(w) -> float:
     esz = 2 if w.dtype == "bf16" else 4
     return w.n_queries * (w.d * esz + w.m * 4)
@@ -494,6 +504,60 @@ def read_ceiling(torch, nbytes: int, n_sets: int, iters: int = 40):
     best["bytes"] = n16 * 16
     best["rotation"] = f"{n_sets} buffers"
     best["best_GBps_by_pattern"] = {k: n16 * 16 / v / 1e9 for k, v in per_pattern.items()}
+    best["frac_hbm"] = best["GBps"] / HBM_PEAK_GBPS
+    return best
+
+
+def read_write_ceiling(torch, read_bytes: int, write_bytes: int, n_sets: int, iters: int = 40):
+    """Measured ceiling for a kernel that reads `read_bytes` and writes
+    `write_bytes`: the plain read kernels of read_ceiling, each workgroup then
+    writing its contiguous share of the output with 16-byte non-temporal
+    stores (libqjl_probe.so), over `n_sets` rotated (input, output) pairs,
+    timed the same way; the best of the same 18 configurations.  The rate is
+    (read + write bytes) / median time."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.qjl_probe_read_write
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    n16 = (read_bytes + 15) // 16
+    m16 = (write_bytes + 15) // 16
+    bufs = [(torch.full((n16 * 4,), 1.0, dtype=torch.float32, device="cuda:0"),
+             torch.empty(m16 * 4, dtype=torch.float32, device="cuda:0")) for _ in range(n_sets)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream()
+    best = None
+    for pattern in (0, 1):
+        for unroll in (2, 4, 8):
+            for wpc in (1, 2, 4):
+                grid = cus * wpc
+
+                def call(i):
+                    src, dst = bufs[i % n_sets]
+                    rc = fn(src.data_ptr(), n16 * 16, dst.data_ptr(), m16 * 16, pattern, unroll,
+                            grid, st.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"qjl_probe_read_write failed ({rc})")
+
+                for i in range(2 * n_sets):
+                    call(i)
+                torch.cuda.synchronize()
+                ts = per_call_times(torch, call, iters)
+                med = ts[len(ts) // 2]
+                if best is None or med < best["median_s"]:
+                    best = {"median_s": med, "mean_s": sum(ts) / len(ts),
+                            "GBps": (n16 + m16) * 16 / med / 1e9,
+                            "pattern": ("chunked" if pattern == 0 else "grid-stride")
+                                       + " reads, then each workgroup's share of the writes",
+                            "loads_in_flight_per_lane": unroll, "workgroups_per_cu": wpc}
+    del bufs
+    torch.cuda.empty_cache()
+    best["read_bytes"] = n16 * 16
+    best["write_bytes"] = m16 * 16
+    best["rotation"] = f"{n_sets} input/output pairs"
     best["frac_hbm"] = best["GBps"] / HBM_PEAK_GBPS
     return best
 
@@ -891,13 +955,27 @@ def main():
         result["read_ceiling"] = {"score_decode7b_bytes": rc84, "score_long_context_bytes": rc302,
                                   "quantize_bytes": rc612,
                                   "attention_long_context_bytes": rc1359}
+        # the same byte counts split as the kernels split them into reads and
+        # writes (the writes after the reads, as the score kernel defers them)
+        sw1, sw2 = score_write_bytes(w), score_write_bytes(wl2)
+        qw = quantize_write_bytes(w)
+        rw84 = read_write_ceiling(torch, int(sb - sw1), int(sw1), n_sets=4)
+        rw302 = read_write_ceiling(torch, int(sb2 - sw2), int(sw2), n_sets=2)
+        rw612 = read_write_ceiling(torch, int(qbytes - qw), int(qw), n_sets=2)
+        result["read_write_ceiling"] = {"score_decode7b_bytes": rw84,
+                                        "score_long_context_bytes": rw302,
+                                        "quantize_bytes": rw612}
         # the 7B attention moves the quantize's byte count within 0.1%
         att_rc = {"attention_decode7b": rc612, "attention_long_context": rc1359}
         if rc612:
             result["roofline"]["frac_read_ceiling"] = achieved / rc612["GBps"]
+        if rw612:
+            result["roofline"]["frac_read_write_ceiling"] = achieved / rw612["GBps"]
         result["score_decode7b"] = {"GBps": sb / s_med / 1e9, "frac_hbm": sb / s_med / 1e9 / HBM_PEAK_GBPS,
                                     "frac_read_ceiling": (sb / s_med / 1e9 / rc84["GBps"]
                                                           if rc84 else None),
+                                    "frac_read_write_ceiling": (sb / s_med / 1e9 / rw84["GBps"]
+                                                                if rw84 else None),
                                     "frac_copy_peak": sb / s_med / 1e9 / copy_gbps,
                                     "scores_per_s": w.groups * w.n_q * w.n_k / s_med,
                                     "mean_s": s_mean, "median_s": s_med, "p10_s": s_p10,
@@ -910,6 +988,8 @@ def main():
                                         "frac_hbm": sb2 / s2_med / 1e9 / HBM_PEAK_GBPS,
                                         "frac_read_ceiling": (sb2 / s2_med / 1e9 / rc302["GBps"]
                                                               if rc302 else None),
+                                        "frac_read_write_ceiling": (
+                                            sb2 / s2_med / 1e9 / rw302["GBps"] if rw302 else None),
                                         "frac_copy_peak": sb2 / s2_med / 1e9 / copy_gbps,
                                         "scores_per_s": wl2.groups * wl2.n_k / s2_med,
                                         "mean_s": s2_mean, "median_s": s2_med,
