@@ -162,8 +162,9 @@ def translation_unit_files(src: str) -> list:
 def dither_cost():
     """Picoseconds per dither pair for the whole chip (every lane drawing: the
     launch time over the pairs all lanes draw), for the generator word plus
-    Box-Muller, the word alone and Box-Muller alone, and what the first costs
-    at the 7B FQJL shape (2,097,152 keys x 128 pairs)."""
+    Box-Muller, the word alone, Box-Muller alone and word plus Box-Muller with
+    the angle from an LDS table, and what the first and the last cost at the
+    7B FQJL shape (2,097,152 keys x 128 pairs)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(PROBE_LIB)
@@ -176,7 +177,8 @@ def dither_cost():
     st = torch.cuda.current_stream()
     total = grid * 256 * pairs
     res = {}
-    for mode, name in ((0, "word_and_box_muller"), (1, "word_only"), (2, "box_muller_only")):
+    for mode, name in ((0, "word_and_box_muller"), (1, "word_only"), (2, "box_muller_only"),
+                       (3, "word_and_box_muller_table_angle")):
         assert fn(mode, grid, 16, out.data_ptr(), st.cuda_stream) == 0
         torch.cuda.synchronize()
         a, b = HipEvent(), HipEvent()
@@ -189,6 +191,8 @@ def dither_cost():
     pairs_7b = 2097152 * 128
     res["fqjl_7b_pairs"] = pairs_7b
     res["fqjl_7b_draw_us_at_full_vector_rate"] = res["word_and_box_muller_ps_per_pair"] * pairs_7b / 1e6
+    res["fqjl_7b_draw_us_table_angle"] = (res["word_and_box_muller_table_angle_ps_per_pair"]
+                                          * pairs_7b / 1e6)
     print(json.dumps({"dither_cost": res}), flush=True)
 
 

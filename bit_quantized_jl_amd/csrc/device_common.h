@@ -93,35 +93,12 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_
 // take their argument in revolutions, here (2 (v & 0xFFF) + 1) 2^-13 exactly.
 // Their float32 errors move a dither value by ~1e-6 of its size, far below
 // the band of coordinates whose sign is not compared bit for bit.
-__device__ __forceinline__ float dither_radius(uint32_t v) {
-  const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
-  return __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
-}
-
-// cos and sin of dither angle a (0 <= a < 4096), 2 pi (a + 1/2) / 4096.  A
-// kernel that keeps these 4096 pairs in LDS (built with this function)
-// reads the very values the others compute inline.
-__device__ __forceinline__ float2 dither_angle(uint32_t a) {
-  const float t = (float)(2u * a + 1u) * 0x1p-13f;
-  return make_float2(__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t));
-}
-
 __device__ __forceinline__ void dither_half(uint32_t v, float &xc, float &xs) {
-  const float r = dither_radius(v);
-  const float2 cs = dither_angle(v & 0xFFFu);
-  xc = r * cs.x;
-  xs = r * cs.y;
-}
-
-// The same draw with the angle's cos and sin read from a table of
-// dither_angle(0 .. 4095) (in LDS: one read instead of two transcendentals
-// and the angle arithmetic).
-__device__ __forceinline__ void dither_half_tab(uint32_t v, const float2 *cs_tab, float &xc,
-                                                float &xs) {
-  const float r = dither_radius(v);
-  const float2 cs = cs_tab[v & 0xFFFu];
-  xc = r * cs.x;
-  xs = r * cs.y;
+  const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
+  const float t = (float)(2u * (v & 0xFFFu) + 1u) * 0x1p-13f;
+  const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
+  xc = r * __builtin_amdgcn_cosf(t);
+  xs = r * __builtin_amdgcn_sinf(t);
 }
 
 // The four values of one word (coordinates 4w .. 4w + 3 of its key), from the
@@ -133,13 +110,6 @@ __device__ __forceinline__ void dither_word_state(uint64_t state, float (&x)[4])
   const uint64_t h = mix64(state);
   dither_half((uint32_t)(h >> 32), x[0], x[1]);
   dither_half((uint32_t)h, x[2], x[3]);
-}
-
-__device__ __forceinline__ void dither_word_state_tab(uint64_t state, const float2 *cs_tab,
-                                                      float (&x)[4]) {
-  const uint64_t h = mix64(state);
-  dither_half_tab((uint32_t)(h >> 32), cs_tab, x[0], x[1]);
-  dither_half_tab((uint32_t)h, cs_tab, x[2], x[3]);
 }
 
 // State of word counter ctr, opaque to the optimiser (an empty asm on its

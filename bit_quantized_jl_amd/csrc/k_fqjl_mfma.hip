@@ -44,6 +44,7 @@
 // in the same order, so a key's bits do not depend on the call's size and
 // a projected key has the signs of its bits.
 #include "device_common.h"
+#include "dither_table.h"
 #include "fwht_common.h"
 #include "mfma_image.h"
 
@@ -69,6 +70,7 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int FM_RING = 4;  // S fragments in flight from LDS
+
 
 template <int T, int RT>
 struct FmKeys {
