@@ -1,8 +1,9 @@
-// The dither's angle from a table (D-FQJL's Gaussian dither, "Fast Quantized
-// Johnson-Lindenstrauss Transforms" page; the draw is dither_half in
-// device_common.h).  A kernel that keeps the cos and sin of the 4096 dither
-// angles in LDS reads them with one instruction instead of evaluating two
-// transcendentals and the angle arithmetic per coordinate pair.
+// Dither draws of the matrix-core FQJL kernels (D-FQJL's Gaussian dither,
+// "Fast Quantized Johnson-Lindenstrauss Transforms" page; the draw is
+// dither_half in device_common.h).  A kernel that keeps the cos and sin of
+// the 4096 dither angles in LDS reads them with one instruction instead of
+// evaluating two transcendentals and the angle arithmetic per coordinate
+// pair; and the dither is added with the amplitude folded into the radius.
 #pragma once
 
 #include "device_common.h"
@@ -35,6 +36,27 @@ __device__ __forceinline__ void dither_word_state_tab(uint64_t state, const floa
   const uint64_t h = mix64(state);
   dither_half_tab((uint32_t)(h >> 32), cs_tab, x[0], x[1]);
   dither_half_tab((uint32_t)h, cs_tab, x[2], x[3]);
+}
+
+// Add the dither of one word (coordinates 4w .. 4w + 3 of its key) of size
+// amp to z[0..3]: per pair the radius is scaled by amp once, and each
+// coordinate takes one fused multiply-add, z += (amp R) cos, z += (amp R) sin.
+// TAB: the angle's cos and sin from cs_tab (dither_angle values); otherwise
+// evaluated inline with the same instructions, so both give the same sums.
+template <bool TAB>
+__device__ __forceinline__ void dither_word_add(uint64_t state, const float2 *cs_tab, float amp,
+                                                float *z) {
+  const uint64_t h = mix64(state);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t v = half == 0 ? (uint32_t)(h >> 32) : (uint32_t)h;
+    const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
+    const float ar =
+        amp * __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
+    const float2 cs = TAB ? cs_tab[v & 0xFFFu] : dither_angle(v & 0xFFFu);
+    z[2 * half] = fmaf(ar, cs.x, z[2 * half]);
+    z[2 * half + 1] = fmaf(ar, cs.y, z[2 * half + 1]);
+  }
 }
 
 }  // namespace qjl

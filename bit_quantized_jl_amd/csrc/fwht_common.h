@@ -8,11 +8,13 @@
 namespace qjl {
 
 // In-place unnormalised Walsh-Hadamard transform of D values in Sylvester
-// (natural) order: log2(D) butterfly stages, D/2 add/subtract pairs each.
-template <int D>
+// (natural) order: log2(D) butterfly stages, D/2 add/subtract pairs each
+// (H0 > 1: only the stages from pair distance H0 on, the earlier ones done
+// by the caller).
+template <int D, int H0 = 1>
 __device__ __forceinline__ void fwht_reg(float (&u)[D]) {
 #pragma unroll
-  for (int h = 1; h < D; h <<= 1) {
+  for (int h = H0; h < D; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < D; i += 2 * h) {
 #pragma unroll

@@ -212,14 +212,21 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
       for (int rt = 0; rt < RT; ++rt) {
         float z[64];
         const float4 *gp = reinterpret_cast<const float4 *>(sG + 128 * b + 64 * h);
+        // z = |G_b| u with the first butterfly stage (pairs 2i, 2i + 1)
+        // fused in: one multiply and two fused multiply-adds per pair
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const float4 gv = gp[k];
           const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[4 * k + e] = acc[rt][k / 4][4 * (k % 4) + e] * g4[e];
+          for (int e = 0; e < 4; e += 2) {
+            const float ua = acc[rt][k / 4][4 * (k % 4) + e];
+            const float t = acc[rt][k / 4][4 * (k % 4) + e + 1] * g4[e + 1];
+            z[4 * k + e] = fmaf(ua, g4[e], t);
+            z[4 * k + e + 1] = fmaf(ua, g4[e], -t);
+          }
         }
-        fwht_reg<64>(z);
+        fwht_reg<64, 2>(z);
         // Top stage across the lane halves, two coordinates (i, i + 32) at a
         // time: one swap brings a_0 and a_1 of coordinate i to half 0 and of
         // i + 32 to half 1, and each half keeps both the sum and the
@@ -242,15 +249,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
               (uint64_t)(base + orow) * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
           const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-          for (int c = 0; c < 64; c += 4) {
-            float x[4];
-            if constexpr (TAB)
-              dither_word_state_tab(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), sCS, x);
-            else
-              dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[c + e] += amp * x[e];
-          }
+          for (int c = 0; c < 64; c += 4)
+            dither_word_add<TAB>(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), sCS, amp,
+                                 &z[c]);
         }
         const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
         if constexpr (NB != 2) {
@@ -291,8 +292,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
 // two kernels' bits identical; that kernel keeps its own copy, since at its
 // 256-register limit the inlined helpers spill.
 // fm_transform: z = |G_b| * u (gp: this lane half's 64 values of
-// |G_b| / sqrt d), then y = H z: H_64 per lane half and the top stage across
-// the halves; afterwards lane half h holds y[64 h .. 64 h + 63].
+// |G_b| / sqrt d), then y = H z: H_64 per lane half (its first stage fused
+// with the scaling, as in fqjl_mfma_kernel) and the top stage across the
+// halves; afterwards lane half h holds y[64 h .. 64 h + 63].
 __device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const float4 *gp,
                                              float (&z)[64]) {
 #pragma unroll
@@ -300,9 +302,14 @@ __device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const f
     const float4 gv = gp[k];
     const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[4 * k + e] = acc[k / 4][4 * (k % 4) + e] * g4[e];
+    for (int e = 0; e < 4; e += 2) {
+      const float ua = acc[k / 4][4 * (k % 4) + e];
+      const float t = acc[k / 4][4 * (k % 4) + e + 1] * g4[e + 1];
+      z[4 * k + e] = fmaf(ua, g4[e], t);
+      z[4 * k + e + 1] = fmaf(ua, g4[e], -t);
+    }
   }
-  fwht_reg<64>(z);
+  fwht_reg<64, 2>(z);
   // Top stage, two coordinates (i, i + 32) at a time: one swap brings a_0
   // and a_1 of coordinate i to half 0 and of i + 32 to half 1, and each half
   // keeps both the sum and the difference: lane half h then holds
@@ -328,12 +335,9 @@ __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float am
         (uint64_t)drow * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
     const uint64_t st0 = dither_state(dkey, word0);
 #pragma unroll
-    for (int c = 0; c < 64; c += 4) {
-      float x[4];
-      dither_word_state(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[c + e] += amp * x[e];
-    }
+    for (int c = 0; c < 64; c += 4)
+      dither_word_add<false>(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), nullptr, amp,
+                             &z[c]);
   }
   w0 = pack_signs(&z[0]);
   w1 = pack_signs(&z[32]);
