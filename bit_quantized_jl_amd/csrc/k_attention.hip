@@ -181,19 +181,20 @@ constexpr int attn_ring() {
   return 3;
 }
 
-// The key stream of one wave: stages wave, wave + 4, ... of the workgroup's
-// keys through a ring of R register stages (stage i lives in b[i % R]).
+// The key stream of one wave: the workgroup's stages wave, wave + 4, ...
+// (stage i: keys key0 + kstride i + [0, AT_STAGE) of the range) through a
+// ring of R register stages (stage i lives in b[i % R]).
 template <int T, int QP, bool PAIR, int R>
 __device__ __forceinline__ void stream_keys(AttnStage<T> (&b)[R], const KeyRange &kr,
                                             const QueryOperands<T, QP> &qo, int wave, int lane,
-                                            int nsr, int nkb, int nqp, float sl2,
-                                            SoftmaxState<QP> &st) {
+                                            int nsr, int key0, int kstride, int nkb, int nqp,
+                                            float sl2, SoftmaxState<QP> &st) {
   for (int j = 0; j < nsr; j += R) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int k0 = AT_STAGE * (wave + SM_WAVES * (j + r));
+      const int k0 = key0 + kstride * (wave + SM_WAVES * (j + r));
       attn_stage<T, QP, PAIR>(b[r], qo, k0, nkb, lane, nqp, sl2, st);
-      load_attn_stage<T>(b[r], kr, k0 + R * AT_STAGE * SM_WAVES, lane);
+      load_attn_stage<T>(b[r], kr, k0 + kstride * R * SM_WAVES, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -207,7 +208,7 @@ template <int T, int QP, bool PAIR>
 __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kernel(
     const float *__restrict__ Sq, const uint32_t *__restrict__ bits,
     const float *__restrict__ norms, const uint16_t *__restrict__ V, int64_t G, int64_t nq,
-    int64_t nk, int chunk, float cscale, float sl2, float *__restrict__ ws,
+    int64_t nk, int chunk, int inter, float cscale, float sl2, float *__restrict__ ws,
     float *__restrict__ out) {
   static_assert(QP == 1 || QP == 2, "one or two query pairs per pass");
   constexpr int W = 4 * T;
@@ -221,11 +222,27 @@ __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kern
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = gridDim.x;
   // key positions within a group fit an int, and byte offsets into a
-  // group's rows a uint32 (the fused path takes nk < 2^22)
-  const int kbeg = (int)blockIdx.x * chunk;
-  const int kend = (int64_t)kbeg + chunk < nk ? kbeg + chunk : (int)nk;
-  const int nkb = kend > kbeg ? kend - kbeg : 0;  // keys of this workgroup
-  const int nstage_blk = (nkb + AT_STAGE - 1) / AT_STAGE;
+  // group's rows a uint32 (the fused path takes nk < 2^22).  The loads go
+  // through descriptors over [kbeg, kend); the workgroup's stage i holds keys
+  // key0 + kstride i + [0, AT_STAGE) of that range, which ends at nkb.  inter
+  // = 0: a contiguous chunk of `chunk` keys; inter = 1: every P-th stage of
+  // the whole group (the group's workgroups sweep its keys together).
+  int kbeg, kend, key0, kstride, nstage_blk;
+  if (inter) {
+    const int nst = (int)((nk + AT_STAGE - 1) / AT_STAGE), x = (int)blockIdx.x;
+    kbeg = 0;
+    kend = (int)nk;
+    key0 = AT_STAGE * x;
+    kstride = AT_STAGE * P;
+    nstage_blk = x < nst ? (nst - x + P - 1) / P : 0;
+  } else {
+    kbeg = (int)blockIdx.x * chunk;
+    kend = (int64_t)kbeg + chunk < nk ? kbeg + chunk : (int)nk;
+    key0 = 0;
+    kstride = AT_STAGE;
+    nstage_blk = ((kend > kbeg ? kend - kbeg : 0) + AT_STAGE - 1) / AT_STAGE;
+  }
+  const int nkb = kend > kbeg ? kend - kbeg : 0;  // keys of the descriptors' range
   const int ns = (nstage_blk - wave + SM_WAVES - 1) / SM_WAVES;
   constexpr int R = attn_ring<T>();
   const int nsr = (ns + R - 1) / R * R;  // whole rounds of the ring
@@ -244,7 +261,8 @@ __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kern
       __builtin_amdgcn_sched_barrier(0);
       AttnStage<T> ring[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) load_attn_stage<T>(ring[r], kr, AT_STAGE * (wave + SM_WAVES * r), lane);
+      for (int r = 0; r < R; ++r)
+        load_attn_stage<T>(ring[r], kr, key0 + kstride * (wave + SM_WAVES * r), lane);
       SoftmaxState<QP> st;
 #pragma unroll
       for (int qp = 0; qp < QP; ++qp)
@@ -255,7 +273,8 @@ __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kern
 #pragma unroll
           for (int d = 0; d < 8; ++d) st.acc[qp][h][d] = 0.f;
         }
-      stream_keys<T, QP, PAIR, R>(ring, kr, qo, wave, lane, nsr, nkb, nqp, sl2, st);
+      stream_keys<T, QP, PAIR, R>(ring, kr, qo, wave, lane, nsr, key0, kstride, nkb, nqp, sl2,
+                                  st);
       // ---- this wave's partials: sum the four lane groups (each saw every
       // fourth value row); lanes 0..15 then hold dims 8 lane .. 8 lane + 7
 #pragma unroll
@@ -439,12 +458,14 @@ hipError_t launch_attn_t(const float *Sq, const uint32_t *bits, const float *nor
   attn_grid<T, QP>(G, nk, &chunk, &gx);
   const int P = gx;
   dim3 grid((unsigned)gx, (unsigned)(G < 65535 ? G : 65535));
+  // A group's workgroups interleave its stages rather than take a chunk each.
+  const int inter = P > 1 ? 1 : 0;
   if (nq > 1)
     hipLaunchKernelGGL((attn_partial_kernel<T, QP, true>), grid, dim3(SM_THREADS), 0, st, Sq,
-                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws, out);
+                       bits, norms, V, G, nq, nk, (int)chunk, inter, c, sl2, ws, out);
   else
     hipLaunchKernelGGL((attn_partial_kernel<T, 1, false>), grid, dim3(SM_THREADS), 0, st, Sq,
-                       bits, norms, V, G, nq, nk, (int)chunk, c, sl2, ws, out);
+                       bits, norms, V, G, nq, nk, (int)chunk, inter, c, sl2, ws, out);
   if (P > 1) {  // with one workgroup per group the kernel wrote the output itself
     const int64_t rows = G * nq;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(rows < 65535 ? rows : 65535)),
