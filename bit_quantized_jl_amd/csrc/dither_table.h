@@ -18,26 +18,6 @@ __device__ __forceinline__ float2 dither_angle(uint32_t a) {
   return make_float2(__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t));
 }
 
-// dither_half with the angle's cos and sin read from a table of
-// dither_angle(0 .. 4095) in LDS: one read instead of two transcendentals
-// and the angle arithmetic; the radius and products as in dither_half.
-__device__ __forceinline__ void dither_half_tab(uint32_t v, const float2 *cs_tab, float &xc,
-                                                float &xs) {
-  const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
-  const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
-  const float2 cs = cs_tab[v & 0xFFFu];
-  xc = r * cs.x;
-  xs = r * cs.y;
-}
-
-// dither_word_state with the table angle.
-__device__ __forceinline__ void dither_word_state_tab(uint64_t state, const float2 *cs_tab,
-                                                      float (&x)[4]) {
-  const uint64_t h = mix64(state);
-  dither_half_tab((uint32_t)(h >> 32), cs_tab, x[0], x[1]);
-  dither_half_tab((uint32_t)h, cs_tab, x[2], x[3]);
-}
-
 // Add the dither of one word (coordinates 4w .. 4w + 3 of its key) of size
 // amp to z[0..3]: per pair the radius is scaled by amp once, and each
 // coordinate takes one fused multiply-add, z += (amp R) cos, z += (amp R) sin.

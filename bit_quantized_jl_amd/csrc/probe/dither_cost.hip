@@ -5,9 +5,10 @@
 //   0  word and Box-Muller (what the FQJL kernels do per two coordinate pairs)
 //   1  the SplitMix64 word alone (its four exact float32 inputs converted)
 //   2  Box-Muller alone, on inputs from a cheap counter sequence
-//   3  word and Box-Muller with the angle's cos and sin from an LDS table (what
-//      the persistent matrix-core FQJL kernel does with dither at m <= 256;
-//      the table is built once per workgroup)
+//   3  word and Box-Muller with the angle's cos and sin from an LDS table, added
+//      with the amplitude folded into the radius (what the persistent
+//      matrix-core FQJL kernel does with dither at m <= 256; the table is
+//      built once per workgroup)
 // Measurement code for the benchmark, not part of the method.
 #include "../device_common.h"
 #include "../dither_table.h"
@@ -27,13 +28,14 @@ __global__ __launch_bounds__(256) void dither_cost_kernel(uint64_t key, int pair
   uint32_t seq = (uint32_t)tid * 2654435761u;
   float acc = 0.f;
   for (int i = 0; i < pairs; i += 2) {  // two pairs per word
-    if (MODE == 0 || MODE == 3) {
+    if (MODE == 0) {
       float x[4];
-      if (MODE == 3)
-        qjl::dither_word_state_tab(st, sCS, x);
-      else
-        qjl::dither_word_state(st, x);
+      qjl::dither_word_state(st, x);
       acc += (x[0] + x[1]) + (x[2] + x[3]);
+    } else if (MODE == 3) {
+      float z[4] = {0.f, 0.f, 0.f, 0.f};
+      qjl::dither_word_add<true>(st, sCS, 1.f, z);
+      acc += (z[0] + z[1]) + (z[2] + z[3]);
     } else if (MODE == 1) {
       const uint64_t h = qjl::mix64(st);
       const uint32_t v[2] = {(uint32_t)(h >> 32), (uint32_t)h};
