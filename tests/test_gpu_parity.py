@@ -322,13 +322,21 @@ def test_fqjl256_unaligned_keys(variant, dt, rho):
                                                ("dense", 0.0, 512, 40, 420),
                                                ("fqjl", 0.2, 256, 64, 300),
                                                ("fqjl", 0.0, 512, 40, 420),
-                                               ("fqjl", 0.0, 128, 48, 380)])
+                                               ("fqjl", 0.0, 128, 48, 380),
+                                               # dither angle from the LDS table (whole cache)
+                                               # against the inline angle (appends)
+                                               ("dfqjl", 0.1, 256, 64, 300),
+                                               ("fqjl", 0.3, 128, 48, 380),
+                                               ("fqjl", 0.1, 512, 40, 420)])
 def test_cache_built_by_appends_equals_whole(variant, rho, m, G, T):
     # Appending one key per group per step, then a block of four, fills the
     # cache exactly as one call over the whole cache (dither counters given
     # by the cache row).  The cases with G T > 16384 keys compare the
     # persistent matrix-core kernel (whole cache) with the short-call kernel
-    # (appends): the same sums in the same order, so the same bits.
+    # (appends): the same sums in the same order, so the same bits.  With
+    # dither at m <= 256 the whole-cache call reads the dither angles' cos
+    # and sin from its LDS table and the appends evaluate them inline (at
+    # m = 128 the appends take the persistent kernel's row-mapped variant).
     note("appends vs whole", variant, rho, m, G, T)
     d = 128
     gen = torch.Generator().manual_seed(5)
