@@ -739,3 +739,46 @@ def test_full_size_prefill():
 @pytest.mark.parametrize("w", [wl.FQJL_7B, wl.FQJL_7B_DITHER, wl.DFQJL_7B], ids=lambda w: w.name)
 def test_full_size_fqjl(w):
     _full(w, scores=True)
+
+
+@pytest.mark.parametrize("variant", ["dense", "fqjl"])
+def test_buffers_past_4gb(variant):
+    # 2^26 + 4173 bf16 keys at d = 128, m = 512: the keys take 17 GB and the
+    # bits 4.3 GB, so the last rows sit past byte offset 2^32 in both, and
+    # one query scored against every key (a single group) writes 268 MB of
+    # scores.  The first, the last and randomly chosen rows (bits, norms and
+    # scores) are checked against the oracle.
+    n, d, m = (1 << 26) + 4173, 128, 512
+    note("buffers past 4 GB", variant, n)
+    gen = torch.Generator(device=DEV).manual_seed(31)
+    K = torch.empty(n, d, dtype=torch.bfloat16, device=DEV)
+    step = 1 << 22
+    for i in range(0, n, step):
+        j = min(n, i + step)
+        K[i:j] = torch.randn(j - i, d, generator=gen, device=DEV).to(torch.bfloat16)
+    q = torch.randn(1, d, generator=gen, device=DEV).to(torch.bfloat16)
+    sk = qj.make_sketch(0, d, m, variant, 0.0)
+    norms, bits = qj.quantize_keys(sk, K)
+    Sq = qj.project_query(sk, q)
+    s = qj.score(sk, Sq, bits, norms, 1, 1, n)
+    torch.cuda.synchronize()
+    pick = np.random.default_rng(5).choice(n, 1500, replace=False)
+    rows = np.unique(np.concatenate([np.arange(300), np.arange(n - 300, n), pick]))
+    assert rows[-1] * (m // 8) >= (1 << 32)  # the checked rows include bits past 4 GB
+    idx = torch.from_numpy(rows).to(DEV)
+    Kh = K.index_select(0, idx).cpu()
+    gb = bits_np(bits.index_select(0, idx))
+    gn = to_np_f64(norms.index_select(0, idx))
+    gs = to_np_f64(s.reshape(-1).index_select(0, idx)).reshape(1, 1, -1)
+    del K, bits, norms, s
+    torch.cuda.empty_cache()
+    ref = oracle_sketch(0, d, m, variant, 0.0)
+    rb, rn, mg, _ = oq.quantize(ref, to_np_f64(Kh), "bf16")
+    nband = check_bits(gb, rb, mg, m)
+    check_norms(gn, rn)
+    Sq_ref = oq.project(ref, to_np_f64(q.cpu()), "bf16")
+    k = len(rows)
+    s_ref = oq.score(Sq_ref, rb, rn, m, 0.0, 1, 1, k)
+    check_scores(gs, s_ref, inband_slack(gb, rb, Sq_ref, rn, m, 0.0, 1, 1, k))
+    report_inband(f"{variant}_n{n}_m{m} ({k} sampled keys; bits and keys past 4 GB)", k * m, nband)
+    sk.close()
