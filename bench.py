@@ -14,8 +14,9 @@ and extra per-kernel figures: keys quantized/s, the score kernel's GB/s on
 caches rotated beyond the 256 MB Infinity Cache (cold) and on one cache that
 stays in it (warm), the long-context (131072 tokens, m = 512) score, fused
 decode attention, the other quantize configurations, the per-token decode
-path, and each rate as a fraction of both the 8 TB/s HBM peak and the
-stream-copy rate measured in the same run.
+path, and each rate as a fraction of the 8 TB/s HBM peak, of the stream-copy
+rate and of the plain read (and read-then-write) ceilings measured in the
+same run.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
