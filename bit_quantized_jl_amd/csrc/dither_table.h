@@ -30,7 +30,19 @@ __device__ __forceinline__ void dither_word_add(uint64_t state, const float2 *cs
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const uint32_t v = half == 0 ? (uint32_t)(h >> 32) : (uint32_t)h;
-    const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
+    // u1 = ((v >> 12) + 1) 2^-20.  With the table, as one fused multiply-add
+    // (exact, so the same value): one instruction less per pair; the shift
+    // is written out, since left to the compiler it becomes a shift of the
+    // 64-bit word and the conversion a 64-bit one.  (In the row-mapped
+    // kernel, at its register limit, that form spills.)
+    float u1;
+    if constexpr (TAB) {
+      uint32_t a;
+      asm("v_lshrrev_b32 %0, 12, %1" : "=v"(a) : "v"(v));
+      u1 = fmaf((float)a, 0x1p-20f, 0x1p-20f);
+    } else {
+      u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
+    }
     const float ar =
         amp * __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
     const float2 cs = TAB ? cs_tab[v & 0xFFFu] : dither_angle(v & 0xFFFu);
