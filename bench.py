@@ -63,8 +63,9 @@ def parse():
                    help="print the hash of a kernel source and every header it includes "
                         "(the value recorded in profiles/*_pmc.txt) and exit")
     p.add_argument("--sustain", type=float, default=0.0, metavar="SECONDS",
-                   help="run only the dense quantize launch back to back for SECONDS while "
-                        "sampling socket power and graphics clocks with amd-smi")
+                   help="run only the 7B-shape quantize launch (dense; with --only fqjl or "
+                        "fqjl_dither the FQJL sketch) back to back for SECONDS while sampling "
+                        "socket power and graphics clocks with amd-smi")
     return p.parse_args()
 
 
@@ -81,11 +82,12 @@ def calibrate_copy():
                       "calibrate_copy_bytes_written": a.numel() * 4}), flush=True)
 
 
-def sustain(seconds: float):
-    """The dominant kernel under sustained load: the 7B-shape quantize launched
-    back to back for `seconds`, with amd-smi sampling socket power and the
-    graphics clocks of every XCD in a child process meanwhile.  Prints one JSON
-    line: mean launch time, mean power, mean clock (samples of the first
+def sustain(seconds: float, kind: str | None = None):
+    """A quantize kernel under sustained load: the 7B-shape quantize (dense, or
+    with --only fqjl / fqjl_dither the FQJL sketch without or with dither)
+    launched back to back for `seconds`, with amd-smi sampling socket power and
+    the graphics clocks of every XCD in a child process meanwhile.  Prints one
+    JSON line: mean launch time, mean power, mean clock (samples of the first
     second, while the clocks settle, are dropped)."""
     import re
     import subprocess
@@ -95,7 +97,8 @@ def sustain(seconds: float):
     import workloads as wl
 
     qj.load()
-    w = wl.DECODE_7B
+    w = {None: wl.DECODE_7B, "quantize": wl.DECODE_7B, "fqjl": wl.FQJL_7B,
+         "fqjl_dither": wl.FQJL_7B_DITHER}[kind]
     dev = "cuda:0"
     K = wl.make_keys(w, dev)
     sk = qj.make_sketch(w.seed, w.d, w.m, w.variant, w.rho)
@@ -131,7 +134,8 @@ def sustain(seconds: float):
         clk = re.match(r"\s*CLK: (\d+) MHz", line)
         if clk and section.startswith("GFX_"):  # graphics clock of one XCD
             clocks.append(float(clk.group(1)))
-    print(json.dumps({"sustain_s": seconds, "dense_schedule": dense_schedule(),
+    print(json.dumps({"sustain_s": seconds, "workload": w.name, "sketch": w.variant, "rho": w.rho,
+                      "dense_schedule": dense_schedule(),
                       "launches": launches,
                       "mean_launch_s": a.seconds_to(b) / launches,
                       "socket_power_w_mean": sum(power) / len(power) if power else None,
@@ -822,7 +826,7 @@ def main():
         calibrate_copy()
         return
     if args.sustain > 0:
-        sustain(args.sustain)
+        sustain(args.sustain, args.only)
         return
     if args.only:
         run_only(args.only)
