@@ -20,7 +20,8 @@ __device__ __forceinline__ float2 dither_angle(uint32_t a) {
 
 // Add the dither of one word (coordinates 4w .. 4w + 3 of its key) of size
 // amp to z[0..3]: per pair the radius is scaled by amp once, and each
-// coordinate takes one fused multiply-add, z += (amp R) cos, z += (amp R) sin.
+// coordinate takes one fused multiply-add, z += (amp R) cos, z += (amp R) sin
+// (R = sqrt(-2 ln u1) as in dither_half, up to float32 rounding).
 // TAB: the angle's cos and sin from cs_tab (dither_angle values); otherwise
 // evaluated inline with the same instructions, so both give the same sums.
 template <bool TAB>
@@ -43,8 +44,11 @@ __device__ __forceinline__ void dither_word_add(uint64_t state, const float2 *cs
     } else {
       u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
     }
+    // amp R = (amp sqrt(2 ln 2)) sqrt(-log2 u1): the first factor is the
+    // same for every pair of the key (formed once), and the negation is a
+    // source modifier of v_sqrt_f32, so a pair takes one multiply here
     const float ar =
-        amp * __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
+        (amp * 1.1774100225154747f) * __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(u1));
     const float2 cs = TAB ? cs_tab[v & 0xFFFu] : dither_angle(v & 0xFFFu);
     z[2 * half] = fmaf(ar, cs.x, z[2 * half]);
     z[2 * half + 1] = fmaf(ar, cs.y, z[2 * half + 1]);
