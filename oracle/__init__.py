@@ -26,8 +26,11 @@ Parity status of each function:
                    3 standard errors), the closed-form variance, error ~ m^-1/2,
                    the dither factor sqrt(1 + rho^2), invariances and special
                    cases.
-  rng.dither_pairs pinned: moments, pair independence, and the dither-factor
-                   Monte Carlo.
+  rng.dither_magnitudes / dither_signs / dither
+                   pinned: sign words written out by hand from the
+                   definition; half-normal magnitudes; one key's dither is
+                   N(0, 1) over sketch draws (moments, KS, E exp(-t xi^2));
+                   fair, per-key signs; the dither-factor Monte Carlo.
   FQJL distortion magnitude: no closed form on the pages -> "parity unpinned";
                    only its decrease with m is tested.
   attention.softmax_rows / decode_attention

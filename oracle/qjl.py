@@ -87,7 +87,7 @@ def quantize(sk, K: np.ndarray, in_dtype: str, key_index_base: int = 0, key_inde
         if sk.rho > 0:
             ids = (np.arange(key_index_base + s, key_index_base + e) if key_index is None
                    else np.asarray(key_index)[s:e])
-            xi = rng.dither_pairs(sk.seed, ids, m)
+            xi = rng.dither(sk.seed, ids, m, sk.dmag)
             Y = Y + sk.rho * norms[s:e, None] * xi
         bits[s:e] = pack_bits(Y >= 0)
         scale = norms[s:e, None] * math.sqrt(d)

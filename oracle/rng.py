@@ -24,9 +24,11 @@ Derived variates (all in float64 unless stated):
     N(i)  = sqrt(-2 ln U(2i)) * cos(2 pi U(2i+1))           (Box and Muller, 1958)
 
 Streams: 0 dense S, 1 Rademacher diagonal D, 2 permutation P, 3 Gaussian
-diagonal G, 4 dither.  The dither stream draws one word per two coordinate
-pairs (see ``dither_pairs``): each 32-bit half gives a 20-bit radius uniform
-and one of 4096 equally spaced angles, both exact in fp32 and fp64 alike.
+diagonal G, 4 dither magnitudes, 5 dither signs.  A sketch with dither holds
+m Gaussian magnitudes |N(j)| (stream 4, drawn once with the sketch, like G);
+each key draws its own m random signs from stream 5, one 64-bit word per 64
+coordinates (see ``dither_signs``), so the dither of any one key is m
+independent N(0, 1) values, independent of the transform.
 """
 from __future__ import annotations
 
@@ -44,7 +46,8 @@ STREAM_DENSE = 0
 STREAM_D = 1
 STREAM_P = 2
 STREAM_G = 3
-STREAM_DITHER = 4
+STREAM_DITHER = 4       # the sketch's dither magnitudes
+STREAM_DITHER_SIGN = 5  # each key's dither signs
 
 
 def mix64(z) -> np.ndarray:
@@ -113,39 +116,41 @@ def gaussian_fast(seed: int, stream: int, idx) -> np.ndarray:
     return np.sqrt(-2.0 * np.log(u_a)) * np.cos(TWO_PI * u_b)
 
 
-def dither_pairs(seed: int, key_index: np.ndarray, m: int) -> np.ndarray:
-    """Dither noise xi[i, j] for global key indices ``key_index`` and j < m.
+def dither_magnitudes(seed: int, m: int, exact: bool = True) -> np.ndarray:
+    """The sketch's dither magnitudes a[j] = |N(j)|, j < m, on stream 4,
+    rounded to float32 (returned as float64): drawn once per sketch, as the
+    Gaussian diagonal G is, and held in float32 on both sides."""
+    g = (gaussian_exact(seed, STREAM_DITHER, m) if exact
+         else gaussian_fast(seed, STREAM_DITHER, np.arange(m)))
+    return np.abs(g).astype(np.float32).astype(np.float64)
 
-    Key i draws m/4 words h_w = r(seed, 4, i*(m/4) + w), w < m/4; word w
-    serves coordinate pairs p = 2w (its high 32 bits) and p = 2w + 1 (its low
-    32 bits).  From a 32-bit half v: a = v >> 12 (20 bits), k = v & 0xFFF, and
 
-        u1 = (a + 1) * 2**-20  in (0, 1],   R = sqrt(-2 ln u1)
-        theta = 2 pi (k + 1/2) / 4096
-        xi[i, 2p] = R cos(theta),   xi[i, 2p+1] = R sin(theta)
+def dither_signs(seed: int, key_index: np.ndarray, m: int) -> np.ndarray:
+    """Dither signs s[i, j] in {+1, -1} for global key indices ``key_index``
+    and coordinates j < m.
 
-    Box-Muller (1958) with the angle on 4096 equally spaced values, offset by
-    half a step so that no angle has a zero cosine or sine.  The radius is
-    Rayleigh as in the continuous method (its top 2**-20 of tail mass cut),
-    and since the average of exp(i n theta) over the angles vanishes for
-    0 < |n| < 4096, every joint moment of (xi_2p, xi_2p+1) of total order
-    below 4096 equals that of two independent standard normals.
+    Key i draws W = ceil(m / 64) words h_w = r(seed, 5, i*W + w).  The 32-bit
+    sign word v (coordinates 32v .. 32v + 31) is the high half of h_{v//2}
+    for even v and its low half for odd v; bit j % 32 of word j // 32
+    (least significant first) is 1 for s[i, j] = -1 and 0 for +1.
     """
     key_index = np.asarray(key_index, dtype=np.uint64).reshape(-1)
-    if m % 4:
-        raise ValueError("the dither draws one word per two coordinate pairs: m % 4 == 0")
-    words = m // 4
+    words = (m + 63) // 64
     ctr = key_index[:, None] * np.uint64(words) + np.arange(words, dtype=np.uint64)[None, :]
-    h = draw(seed, STREAM_DITHER, ctr)
-    halves = np.empty((key_index.shape[0], 2 * words), dtype=np.uint64)
-    halves[:, 0::2] = h >> np.uint64(32)                    # pair 2w
-    halves[:, 1::2] = h & np.uint64(0xFFFFFFFF)             # pair 2w + 1
-    a = (halves >> np.uint64(12)).astype(np.float64)
-    k = (halves & np.uint64(0xFFF)).astype(np.float64)
-    u1 = (a + 1.0) * 2.0 ** -20
-    rad = np.sqrt(-2.0 * np.log(u1))
-    th = TWO_PI * (k + 0.5) / 4096.0
-    out = np.empty((key_index.shape[0], m), dtype=np.float64)
-    out[:, 0::2] = rad * np.cos(th)
-    out[:, 1::2] = rad * np.sin(th)
-    return out
+    h = draw(seed, STREAM_DITHER_SIGN, ctr)
+    w32 = np.empty((key_index.shape[0], 2 * words), dtype=np.uint64)
+    w32[:, 0::2] = h >> np.uint64(32)
+    w32[:, 1::2] = h & np.uint64(0xFFFFFFFF)
+    j = np.arange(m)
+    bit = (w32[:, j // 32] >> (j % 32).astype(np.uint64)[None, :]) & np.uint64(1)
+    return np.where(bit == 1, -1.0, 1.0)
+
+
+def dither(seed: int, key_index: np.ndarray, m: int, magnitudes: np.ndarray) -> np.ndarray:
+    """Dither noise xi[i, j] = s[i, j] * a[j]: each key's own random signs on
+    the sketch's magnitudes.  For any one key the m values are independent
+    N(0, 1) over the sketch's draw (a[j] half-normal, s[i, j] a fair sign
+    independent of it), which is all the dithered estimator's unbiasing
+    factor sqrt(1 + rho^2) needs; distinct keys get independent signs, so
+    their dither vectors are uncorrelated."""
+    return dither_signs(seed, key_index, m) * np.asarray(magnitudes, np.float64)[None, :]

@@ -103,6 +103,7 @@ class DenseSketch:
     S32: np.ndarray   # float32-rounded (as float64)
     S16: np.ndarray   # bfloat16-rounded from S32 (as float64)
     variant: str = "dense"
+    dmag: np.ndarray | None = None   # [m] dither magnitudes (rho > 0), float32-rounded
 
     def effective(self, in_dtype: str) -> np.ndarray:
         """The S actually applied: bf16 inputs use S16, fp32 inputs use S32."""
@@ -119,6 +120,7 @@ class FqjlSketch:
     P: np.ndarray     # [m/d, d] permutations of range(d)
     G: np.ndarray     # [m/d, d] float32-rounded Gaussians (as float64)
     variant: str = "fqjl"
+    dmag: np.ndarray | None = None   # [m] dither magnitudes (rho > 0), float32-rounded
 
     def explicit(self) -> np.ndarray:
         """The m x d matrix: blocks H diag(G) Pi (H/sqrt d) diag(D) stacked."""
@@ -148,7 +150,8 @@ def make_dense(seed: int, d: int, m: int, rho: float = 0.0, exact: bool = True) 
         S64 = rng.gaussian_fast(seed, rng.STREAM_DENSE, np.arange(m * d)).reshape(m, d)
     S32 = round_to_f32(S64)
     S16 = round_f32_to_bf16(S32)
-    return DenseSketch(seed, d, m, rho, S64, S32, S16)
+    dmag = rng.dither_magnitudes(seed, m, exact) if rho > 0 else None
+    return DenseSketch(seed, d, m, rho, S64, S32, S16, dmag=dmag)
 
 
 def fisher_yates(seed: int, block: int, d: int) -> np.ndarray:
@@ -165,11 +168,12 @@ def fisher_yates(seed: int, block: int, d: int) -> np.ndarray:
 
 
 def make_fqjl(seed: int, d: int, m: int, rho: float = 0.0, permute: bool = True,
-              variant: str = "fqjl") -> FqjlSketch:
+              variant: str = "fqjl", exact: bool = True) -> FqjlSketch:
     """Per block b < m/d: D_b from the top bit of r(seed, 1, b d + c)
     (0 -> +1, 1 -> -1); P_b by Fisher-Yates on stream 2 (the identity when
     ``permute`` is false: the D-FQJL construction has no permutation);
-    G_b[c] = fp32(N(b d + c)) on stream 3."""
+    G_b[c] = fp32(N(b d + c)) on stream 3; with dither (rho > 0) the m
+    magnitudes of rng.dither_magnitudes."""
     assert m % d == 0
     nb = m // d
     D = np.empty((nb, d))
@@ -180,7 +184,8 @@ def make_fqjl(seed: int, d: int, m: int, rho: float = 0.0, permute: bool = True,
         D[b] = np.where((r >> np.uint64(63)) == 0, 1.0, -1.0)
         P[b] = fisher_yates(seed, b, d) if permute else np.arange(d)
         G[b] = round_to_f32(rng.gaussian_exact(seed, rng.STREAM_G, d, offset=b * d))
-    return FqjlSketch(seed, d, m, rho, D, P, G, variant)
+    dmag = rng.dither_magnitudes(seed, m, exact) if rho > 0 else None
+    return FqjlSketch(seed, d, m, rho, D, P, G, variant, dmag=dmag)
 
 
 def make_sketch(seed: int, d: int, m: int, variant: str, rho: float = 0.0, exact: bool = True):
@@ -190,11 +195,11 @@ def make_sketch(seed: int, d: int, m: int, variant: str, rho: float = 0.0, exact
     if variant == "dense":
         return make_dense(seed, d, m, rho, exact)
     if variant == "fqjl":
-        return make_fqjl(seed, d, m, rho)
+        return make_fqjl(seed, d, m, rho, exact=exact)
     if variant == "dfqjl":
         if not rho > 0:
             raise ValueError("D-FQJL is the dithered construction: rho > 0")
-        return make_fqjl(seed, d, m, rho, permute=False, variant="dfqjl")
+        return make_fqjl(seed, d, m, rho, permute=False, variant="dfqjl", exact=exact)
     if variant == "pfqjl":
         if rho != 0:
             raise ValueError("P-FQJL is the undithered construction: rho = 0")

@@ -88,7 +88,7 @@ def test_brute_force_tiny(variant, rho):
     Q = rs.standard_normal((G * nq, d))
     bits, norms, _, _ = qjl.quantize(sk, K, "f32", key_index_base=10)
     out = qjl.score(qjl.project(sk, Q, "f32"), bits, norms, m, rho, G, nq, nk)
-    xi = rng.dither_pairs(3, np.arange(10, 10 + G * nk), m)
+    xi = rng.dither(3, np.arange(10, 10 + G * nk), m, sk.dmag) if rho > 0 else None
     for g in range(G):
         for i in range(nq):
             for t in range(nk):
@@ -303,7 +303,8 @@ def test_variant_rho_rules():
 def test_dfqjl_unbiased_conditional_on_D():
     # with P = I the Gaussian second diagonal still makes every coordinate
     # pair jointly Gaussian given D, so the dithered estimator with
-    # sqrt(1 + rho^2) is unbiased over G and the dither alone
+    # sqrt(1 + rho^2) is unbiased over G and the dither (its magnitudes and
+    # the key's signs) alone
     d, m, N, rho = 16, 32, 6000, 0.5
     base = sketch.make_sketch(0, d, m, "dfqjl", rho)
     rs = np.random.default_rng(13)
@@ -312,7 +313,9 @@ def test_dfqjl_unbiased_conditional_on_D():
     est = np.empty(N)
     for t in range(N):
         G = rng.gaussian_fast(300 + t, rng.STREAM_G, np.arange(m)).reshape(m // d, d)
-        sk = sketch.FqjlSketch(0, d, m, rho, base.D, base.P, sketch.round_to_f32(G), "dfqjl")
+        # the dither magnitudes are drawn with the sketch, as G is
+        sk = sketch.FqjlSketch(0, d, m, rho, base.D, base.P, sketch.round_to_f32(G), "dfqjl",
+                               dmag=rng.dither_magnitudes(300 + t, m, exact=False))
         est[t] = qjl.estimate_inner_product(sk, q, k, key_index=t)
     se = est.std(ddof=1) / math.sqrt(N)
     assert abs(est.mean() - q @ k) <= 3 * se

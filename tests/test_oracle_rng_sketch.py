@@ -53,44 +53,78 @@ def test_gaussian_exact_matches_vectorised():
     assert np.max(np.abs(a - b)) < 1e-12
 
 
-def test_dither_pairs_moments_and_independence():
-    xi = rng.dither_pairs(0, np.arange(4000), 64)
-    assert xi.shape == (4000, 64)
+def test_dither_sign_words_by_hand():
+    # Key i's sign words, written out from the definition with Python ints:
+    # W = ceil(m / 64) draws r(seed, 5, i W + w); 32-bit word v is the high
+    # half of draw v // 2 for even v, the low half for odd v; bit j % 32 of
+    # word j // 32 (LSB first) set means -1.
+    seed = 9
+    key = rng.mix64_int((seed + rng.PHI * (5 + 1)) & rng.MASK64)
+    for m, keys in ((32, [0, 1, 77]), (64, [3]), (96, [5, 2**40 + 7]), (256, [0, 12345])):
+        W = (m + 63) // 64
+        got = rng.dither_signs(seed, keys, m)
+        assert got.shape == (len(keys), m)
+        for r, i in enumerate(keys):
+            for j in range(m):
+                v = j // 32
+                h = rng.mix64_int((key + rng.PHI * (i * W + v // 2 + 1)) & rng.MASK64)
+                word = (h >> 32) if v % 2 == 0 else (h & 0xFFFFFFFF)
+                want = -1.0 if (word >> (j % 32)) & 1 else 1.0
+                assert got[r, j] == want, (m, i, j)
+
+
+def test_dither_magnitudes_are_float32_half_normals():
+    a = rng.dither_magnitudes(4, 512)
+    g = rng.gaussian_exact(4, rng.STREAM_DITHER, 512)
+    assert np.array_equal(a, np.abs(g).astype(np.float32).astype(np.float64))
+    assert np.all(a >= 0)
+    assert np.max(np.abs(a - np.abs(g))) <= 2.0 ** -24 * np.max(np.abs(g))
+    # half-normal over many draws: E a = sqrt(2 / pi), E a^2 = 1
+    x = rng.dither_magnitudes(6, 200000, exact=False)
+    n = x.size
+    assert abs(x.mean() - math.sqrt(2 / math.pi)) < 4 * math.sqrt((1 - 2 / math.pi) / n)
+    assert abs((x * x).mean() - 1.0) < 4 * math.sqrt(2 / n)
+    assert scipy.stats.kstest(x, "halfnorm").pvalue > 1e-3
+
+
+def test_dither_of_one_key_is_gaussian_over_sketches():
+    # The estimator's unbiasing factor sqrt(1 + rho^2) needs, for one key,
+    # m independent N(0, 1) dither values independent of the transform.
+    # Over 3000 sketch seeds (magnitudes drawn with each sketch, the key's
+    # signs with its index):
+    m, N = 64, 3000
+    xi = np.vstack([rng.dither(s, [17], m, rng.dither_magnitudes(s, m, exact=False))
+                    for s in range(N)])
     v = xi.reshape(-1)
     n = v.size
     assert abs(v.mean()) < 4 / math.sqrt(n)
     assert abs(v.var() - 1.0) < 4 * math.sqrt(2 / n)
     assert scipy.stats.kstest(v, "norm").pvalue > 1e-3
-    # the cosine and sine halves of one Box-Muller draw are uncorrelated
-    c = np.corrcoef(xi[:, 0::2].reshape(-1), xi[:, 1::2].reshape(-1))[0, 1]
-    assert abs(c) < 4 / math.sqrt(xi[:, 0::2].size)
-    # the counter is (key index, pair): distinct keys give distinct noise
-    assert not np.allclose(rng.dither_pairs(0, [7], 64), rng.dither_pairs(0, [8], 64))
-    assert np.array_equal(rng.dither_pairs(0, [7], 64), rng.dither_pairs(0, np.array([7]), 64))
-
-
-def test_dither_is_gaussian_where_the_estimator_needs_it():
-    # One word serves two coordinate pairs, each from 32 bits: the noise must
-    # still behave as N(0, 1) in the ways the estimator uses.
-    xi = rng.dither_pairs(5, np.arange(2000), 256)
-    v = xi.reshape(-1)
-    n = v.size
-    # higher moments of N(0, 1): E xi^4 = 3, E xi^6 = 15 (4 standard errors)
     for p, mom in ((4, 3.0), (6, 15.0)):
         se = math.sqrt((math.prod(range(2 * p - 1, 0, -2)) - mom * mom) / n)
         assert abs(np.mean(v ** p) - mom) < 4 * se, p
-    # the dither factor sqrt(1 + rho^2) rests on E exp(-t xi^2) = 1 / sqrt(1 + 2t)
     for t in (0.005, 0.5, 2.0):
         e = np.exp(-t * v * v)
         assert abs(e.mean() - 1 / math.sqrt(1 + 2 * t)) < 4 * e.std() / math.sqrt(n), t
-    # no point mass at zero (an angle grid with a zero cosine would put 1/128
-    # of the draws there): |xi| < 1e-4 as often as a normal density gives
-    # (P = 8.0e-5, ~41 of 512,000)
-    assert np.count_nonzero(np.abs(v) < 1e-4) < 100
-    # the two pairs drawn from one word (its two halves) are uncorrelated
-    for a, b in ((0, 2), (1, 3), (0, 3)):
-        c = np.corrcoef(xi[:, a::4].reshape(-1), xi[:, b::4].reshape(-1))[0, 1]
-        assert abs(c) < 4 / math.sqrt(xi[:, a::4].size), (a, b)
+    # coordinates of one key are uncorrelated (adjacent, and across the two
+    # halves of one draw)
+    for a, b in ((0, 1), (0, 32), (5, 40)):
+        c = np.corrcoef(xi[:, a], xi[:, b])[0, 1]
+        assert abs(c) < 4 / math.sqrt(N), (a, b)
+
+
+def test_dither_signs_fair_and_distinct_per_key():
+    s = rng.dither_signs(0, np.arange(4000), 256)
+    n = s.size
+    assert abs(s.mean()) < 4 / math.sqrt(n)
+    # distinct keys: uncorrelated sign vectors (so uncorrelated dither)
+    c = (s[:-1] * s[1:]).mean()
+    assert abs(c) < 4 / math.sqrt(s[1:].size)
+    assert not np.array_equal(rng.dither_signs(0, [7], 256), rng.dither_signs(0, [8], 256))
+    assert np.array_equal(rng.dither_signs(0, [7], 256), rng.dither_signs(0, np.array([7]), 256))
+    # one key's two 32-bit halves of a draw are uncorrelated
+    c2 = (s[:, 0:32] * s[:, 32:64]).mean()
+    assert abs(c2) < 4 / math.sqrt(s[:, 0:32].size)
 
 
 @pytest.mark.parametrize("d", [2, 4, 8, 16, 32, 64])
