@@ -56,9 +56,6 @@ def parse():
     p.add_argument("--only", choices=["quantize", "fqjl", "fqjl_dither", "score", "attention"],
                    help="run only a few launches of one kernel on its 7B-decode-shape workload "
                         "(for hardware-counter passes)")
-    p.add_argument("--dither-cost", action="store_true",
-                   help="time the dither generator's parts per coordinate pair (the library's "
-                        "own generator code, in libqjl_probe.so) and exit")
     p.add_argument("--tu-hash", metavar="SOURCE",
                    help="print the hash of a kernel source and every header it includes "
                         "(the value recorded in profiles/*_pmc.txt) and exit")
@@ -162,43 +159,6 @@ def translation_unit_files(src: str) -> list:
 
     visit(src)
     return order
-
-
-def dither_cost():
-    """Picoseconds per dither pair for the whole chip (every lane drawing: the
-    launch time over the pairs all lanes draw), for the generator word plus
-    Box-Muller, the word alone, Box-Muller alone and word plus Box-Muller with
-    the angle from an LDS table, and what the first and the last cost at the
-    7B FQJL shape (2,097,152 keys x 128 pairs)."""
-    import ctypes
-    import torch
-    lib = ctypes.CDLL(PROBE_LIB)
-    fn = lib.qjl_probe_dither_cost
-    fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    grid, pairs = cus * 8, 4096
-    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda:0")
-    st = torch.cuda.current_stream()
-    total = grid * 256 * pairs
-    res = {}
-    for mode, name in ((0, "word_and_box_muller"), (1, "word_only"), (2, "box_muller_only"),
-                       (3, "word_and_box_muller_table_angle")):
-        assert fn(mode, grid, 16, out.data_ptr(), st.cuda_stream) == 0
-        torch.cuda.synchronize()
-        a, b = HipEvent(), HipEvent()
-        a.record(st)
-        for _ in range(5):
-            assert fn(mode, grid, pairs, out.data_ptr(), st.cuda_stream) == 0
-        b.record(st)
-        torch.cuda.synchronize()
-        res[name + "_ps_per_pair"] = a.seconds_to(b) / 5 / total * 1e12
-    pairs_7b = 2097152 * 128
-    res["fqjl_7b_pairs"] = pairs_7b
-    res["fqjl_7b_draw_us_at_full_vector_rate"] = res["word_and_box_muller_ps_per_pair"] * pairs_7b / 1e6
-    res["fqjl_7b_draw_us_table_angle"] = (res["word_and_box_muller_table_angle_ps_per_pair"]
-                                          * pairs_7b / 1e6)
-    print(json.dumps({"dither_cost": res}), flush=True)
 
 
 def kernel_tu_hash(src: str = QUANT_KERNEL_SRC) -> str:
@@ -813,9 +773,6 @@ def main():
     args = parse()
     if args.tu_hash:
         print(kernel_tu_hash(os.path.abspath(args.tu_hash)))
-        return
-    if args.dither_cost:
-        dither_cost()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "

@@ -48,7 +48,7 @@ def _declare(lib: ctypes.CDLL) -> None:
         "qjl_sketch_info": (c.c_int, [vp, c.POINTER(u64), c.POINTER(i32), c.POINTER(i32),
                                       c.POINTER(i32), c.POINTER(f32), c.POINTER(i32)]),
         "qjl_sketch_export": (c.c_int, [vp, vp, vp]),
-        "qjl_generate_sketch_host": (c.c_int, [u64, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "qjl_generate_sketch_host": (c.c_int, [u64, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "qjl_quantize_keys": (c.c_int, [vp, vp, i32, i64, i64, vp, vp, vp]),
         "qjl_quantize_keys_into": (c.c_int, [vp, vp, i32, i64, i64, i64, i64, i64, vp, vp, vp]),
         "qjl_project_query": (c.c_int, [vp, vp, i32, i64, vp, vp]),
@@ -216,21 +216,24 @@ def sketch_export(sk: Sketch, bf16: bool = False):
 def generate_sketch_host(seed: int, d: int, m: int, variant: str = "dense") -> dict:
     """Host-only draw of the sketch parameters (works without a GPU)."""
     out = {}
+    dmag = np.empty(max(m, 0), np.float32)
     if variant == "dense":
         s32 = np.empty((m, d), np.float32)
         s16 = np.empty((m, d), np.uint16)
         _check(load().qjl_generate_sketch_host(seed, d, m, 0, s32.ctypes.data, s16.ctypes.data,
-                                               None, None, None), "qjl_generate_sketch_host")
-        out.update(S_f32=s32, S_bf16=s16)
+                                               None, None, None, dmag.ctypes.data),
+               "qjl_generate_sketch_host")
+        out.update(S_f32=s32, S_bf16=s16, dither_mag=dmag)
     else:
         nb = m // d if d > 0 else 0
         D = np.empty((nb, d), np.int8)
         P = np.empty((nb, d), np.int32)
         G = np.empty((nb, d), np.float32)
         _check(load().qjl_generate_sketch_host(seed, d, m, VARIANTS[variant], None, None,
-                                               D.ctypes.data, P.ctypes.data, G.ctypes.data),
+                                               D.ctypes.data, P.ctypes.data, G.ctypes.data,
+                                               dmag.ctypes.data),
                "qjl_generate_sketch_host")
-        out.update(D=D, P=P, G=G)
+        out.update(D=D, P=P, G=G, dither_mag=dmag)
     return out
 
 

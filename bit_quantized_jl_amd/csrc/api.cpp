@@ -43,7 +43,7 @@ const char *qjl_version(void) { return "qjl 0.1.0 gfx950"; }
 
 qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t variant,
                                     float *S_f32, uint16_t *S_bf16, int8_t *D_signs,
-                                    int32_t *perm, float *G) {
+                                    int32_t *perm, float *G, float *dither_mag) {
   qjl_status st = validate_sketch_params(d, m, variant, 0.f, /*check_rho=*/false);
   if (st != QJL_OK) return st;
   HostSketch hs;
@@ -65,6 +65,7 @@ qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t
     if (perm) std::memcpy(perm, hs.P.data(), hs.P.size() * sizeof(int32_t));
     if (G) std::memcpy(G, hs.G.data(), hs.G.size() * sizeof(float));
   }
+  if (dither_mag) std::memcpy(dither_mag, hs.Dmag.data(), (size_t)m * sizeof(float));
   return QJL_OK;
 }
 
@@ -88,7 +89,7 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
   hs.m = m;
   hs.variant = variant;
   hs.rho = rho;
-  sk->dither_key = stream_key(seed, STREAM_DITHER);
+  sk->dither_key = stream_key(seed, STREAM_DITHER_SIGN);
   try {
     generate_host_sketch(hs);
   } catch (const std::bad_alloc &) {
@@ -99,7 +100,7 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
   // Lay out every device array in one allocation.
   const size_t md = (size_t)m * d;
   std::vector<unsigned char> blob;
-  size_t off_a = 0, off_b = 0, off_c = 0, off_d = 0, off_e = 0, total = 0;
+  size_t off_a = 0, off_b = 0, off_c = 0, off_d = 0, off_e = 0, off_f = 0, total = 0;
   try {
     if (variant == QJL_VARIANT_DENSE) {
       off_a = 0;                                             // S32   float[md]
@@ -107,7 +108,8 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
       off_c = round_up(off_b + md * 4, 256);                 // S16mfma u16[md]
       off_d = round_up(off_c + md * 2, 256);                 // S32T  float[md]
       off_e = round_up(off_d + md * 4, 256);                 // S16fT float[md]
-      total = round_up(off_e + md * 4, 256);
+      off_f = round_up(off_e + md * 4, 256);                 // Dmag  float[m]
+      total = round_up(off_f + (size_t)m * 4, 256);
       blob.assign(total, 0);
       std::memcpy(blob.data() + off_a, hs.S32.data(), md * 4);
       float *s16f = reinterpret_cast<float *>(blob.data() + off_b);
@@ -129,7 +131,8 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
       off_b = round_up(off_a + nbd * 4, 256);     // P     i32[nbd]
       off_c = round_up(off_b + nbd * 4, 256);     // Gs    f32[nbd]
       off_d = round_up(off_c + nbd * 4, 256);     // Fmfma u16[md] (matrix-core first stage)
-      total = round_up(off_d + (fqjl_mfma_image_shape(d, m) ? md * 2 : 0), 256);
+      off_f = round_up(off_d + (fqjl_mfma_image_shape(d, m) ? md * 2 : 0), 256);  // Dmag f32[m]
+      total = round_up(off_f + (size_t)m * 4, 256);
       blob.assign(total, 0);
       if (fqjl_mfma_image_shape(d, m))
         build_fqjl_mfma_image(hs, reinterpret_cast<uint16_t *>(blob.data() + off_d));
@@ -142,6 +145,7 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
       }
       std::memcpy(blob.data() + off_b, hs.P.data(), nbd * 4);
     }
+    std::memcpy(blob.data() + off_f, hs.Dmag.data(), (size_t)m * 4);
   } catch (const std::bad_alloc &) {
     delete sk;
     return QJL_ERR_OUT_OF_MEMORY;
@@ -169,6 +173,7 @@ qjl_status qjl_make_sketch(uint64_t seed, int32_t d, int32_t m, int32_t variant,
     sk->Gs = reinterpret_cast<const float *>(base + off_c);
     if (fqjl_mfma_image_shape(d, m)) sk->Fmfma = reinterpret_cast<const uint16_t *>(base + off_d);
   }
+  sk->Dmag = reinterpret_cast<const float *>(base + off_f);
   *out = sk;
   return QJL_OK;
 }

@@ -82,51 +82,63 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, int64_
   return bf16_bits_to_f32(p[i]);
 }
 
-// Dither draws (D-FQJL's Gaussian dither, "Fast Quantized Johnson-Lindenstrauss
-// Transforms" page).  Key i draws one SplitMix64 word per two coordinate
-// pairs, h = r(seed, 4, i m/4 + w); the high 32 bits of word w serve pair 2w,
-// the low 32 bits pair 2w + 1.  From a half v: u1 = ((v >> 12) + 1) 2^-20 and
-// the angle 2 pi ((v & 0xFFF) + 1/2) / 4096 (both exact in float32), and
-// Box-Muller returns R cos for the even and R sin for the odd coordinate, with
-// R = sqrt(-2 ln u1).  The gfx950 transcendental instructions evaluate it
-// directly: v_log_f32 is log2 (R^2 = -2 ln 2 log2 u1), v_sin_f32 / v_cos_f32
-// take their argument in revolutions, here (2 (v & 0xFFF) + 1) 2^-13 exactly.
-// Their float32 errors move a dither value by ~1e-6 of its size, far below
-// the band of coordinates whose sign is not compared bit for bit.
-__device__ __forceinline__ void dither_half(uint32_t v, float &xc, float &xs) {
-  const float u1 = (float)((v >> 12) + 1u) * 0x1p-20f;
-  const float t = (float)(2u * (v & 0xFFFu) + 1u) * 0x1p-13f;
-  const float r = __builtin_amdgcn_sqrtf(-1.3862943611198906f * __builtin_amdgcn_logf(u1));
-  xc = r * __builtin_amdgcn_cosf(t);
-  xs = r * __builtin_amdgcn_sinf(t);
+// Dither (D-FQJL's Gaussian dither, "Fast Quantized Johnson-Lindenstrauss
+// Transforms" page, Key concepts): coordinate j of key i gets s_ij a_j, with
+// a_j the sketch's float32 magnitude |N(j)| (drawn once with the sketch) and
+// s_ij a fair sign of the key's own: word u of key i is the SplitMix64 draw
+// r(seed, 5, i ceil(m/64) + u), its high half the 32-bit sign word 2u and its
+// low half word 2u + 1; bit j % 32 of sign word j / 32 set means s_ij = -1.
+// Per key the m values are independent N(0, 1) over the sketch's draw, as
+// the dithered estimator's factor sqrt(1 + rho^2) requires.
+
+// SplitMix64 draw u of key key_index's signs (dkey = key(seed, 5)).
+__device__ __forceinline__ uint64_t dither_draw(uint64_t dkey, uint64_t key_index, int m, int u) {
+  return mix64(dkey + PHI * (key_index * (uint64_t)((m + 63) >> 6) + (uint64_t)u + 1));
 }
 
-// The four values of one word (coordinates 4w .. 4w + 3 of its key), from the
-// generator's state key + PHI (ctr + 1) (stream_draw's argument to mix64): a
-// loop over consecutive words forms the state once and adds multiples of
-// PHI, which the compiler would otherwise fold back into a 64-bit
-// multiply-add per word.
-__device__ __forceinline__ void dither_word_state(uint64_t state, float (&x)[4]) {
-  const uint64_t h = mix64(state);
-  dither_half((uint32_t)(h >> 32), x[0], x[1]);
-  dither_half((uint32_t)h, x[2], x[3]);
+// Sign word v (coordinates 32 v .. 32 v + 31) of key key_index.
+__device__ __forceinline__ uint32_t dither_word(uint64_t dkey, uint64_t key_index, int m, int v) {
+  const uint64_t h = dither_draw(dkey, key_index, m, v >> 1);
+  return (v & 1) ? (uint32_t)h : (uint32_t)(h >> 32);
 }
 
-// State of word counter ctr, opaque to the optimiser (an empty asm on its
-// register pair), so that state + PHI k stays one 64-bit add per word.
-__device__ __forceinline__ uint64_t dither_state(uint64_t key, uint64_t ctr) {
-  uint64_t s = key + PHI * (ctr + 1);
-  asm volatile("" : "+v"(s));
-  return s;
+// z + amp s a for the coordinate at bit b of sign word sw (a = its
+// magnitude, nonnegative, so its sign bit is clear): the sign bit of a is set
+// from bit b (a shift and one v_and_or_b32), then one fused multiply-add.
+// Every kernel adds the dither in this one form, so kernels that compute
+// the same transformed coordinate agree bit for bit.
+__device__ __forceinline__ float dither_fma(float z, float amp, uint32_t sw, int b, float a) {
+  const uint32_t sa = __float_as_uint(a) | ((sw << (31 - b)) & 0x80000000u);
+  return fmaf(amp, __uint_as_float(sa), z);
 }
 
-// Coordinate j of key key_index's dither (m coordinates per key).
-__device__ __forceinline__ float dither_one(uint64_t key, uint64_t key_index, int m, int j) {
-  const uint64_t h = mix64(key + PHI * (key_index * (uint64_t)(m / 4) + (uint64_t)(j >> 2) + 1));
-  const uint32_t v = (j & 2) ? (uint32_t)h : (uint32_t)(h >> 32);
-  float c, s;
-  dither_half(v, c, s);
-  return (j & 1) ? s : c;
+// z[0 .. n) += amp s a for coordinates 32 v + b0 + i of sign word sw
+// (a: their magnitudes).
+template <int N>
+__device__ __forceinline__ void dither_add(float *z, float amp, uint32_t sw, int b0,
+                                           const float *a) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) z[i] = dither_fma(z[i], amp, sw, b0 + i, a[i]);
+}
+
+// z[0 .. 32 NW) += amp s a for the coordinates of sign words v0 .. v0 + NW - 1
+// of key key_index (a: their magnitudes).  For NW >= 2, v0 is even and each
+// draw serves two words.
+template <int NW>
+__device__ __forceinline__ void dither_words_add(float *z, float amp, uint64_t dkey,
+                                                 uint64_t key_index, int m, int v0,
+                                                 const float *a) {
+  if constexpr (NW == 1) {
+    dither_add<32>(z, amp, dither_word(dkey, key_index, m, v0), 0, a);
+  } else {
+    static_assert(NW % 2 == 0, "whole draws");
+#pragma unroll
+    for (int p = 0; p < NW; p += 2) {
+      const uint64_t h = dither_draw(dkey, key_index, m, (v0 + p) >> 1);
+      dither_add<32>(z + 32 * p, amp, (uint32_t)(h >> 32), 0, a + 32 * p);
+      dither_add<32>(z + 32 * p + 32, amp, (uint32_t)h, 0, a + 32 * p + 32);
+    }
+  }
 }
 
 }  // namespace qjl

@@ -44,7 +44,6 @@
 // in the same order, so a key's bits do not depend on the call's size and
 // a projected key has the signs of its bits.
 #include "device_common.h"
-#include "dither_table.h"
 #include "fwht_common.h"
 #include "mfma_image.h"
 
@@ -93,38 +92,40 @@ __device__ __forceinline__ void fm_load(FmKeys<T, RT> &kt, const uint16_t *__res
   }
 }
 
-// With dither up to m = 256 (unmapped launches), the cos and sin of the 4096
-// dither angles sit in LDS: 32 KB beside the image, so one 8-wave workgroup
-// per compute unit instead of two of 4 waves.  The table is built with the
-// instructions the other kernels evaluate inline (dither_angle), so the
-// draws are the same values.  (The row-mapped variant keeps the inline
-// angles: with the table it would spill.)
-#ifndef QJL_FM_DITHER_TABLE
-#define QJL_FM_DITHER_TABLE 1
-#endif
-constexpr bool fm_angle_table(int M, bool dither, bool mapped) {
-  return dither && !mapped && M <= 256 && QJL_FM_DITHER_TABLE;
+// The dither of the coordinates a lane half holds after the second stage of
+// block b (z[0 .. 31]: sign word 4 b + h of the key, z[32 .. 63]: word
+// 4 b + 2 + h; a128: the magnitudes of block b's 128 coordinates).  Lane half
+// h draws word 2 b + h of the key's signs (sign words 4 b + 2 h and
+// 4 b + 2 h + 1), and one swap hands half 0 the high halves of the two
+// draws (words 4 b, 4 b + 2) and half 1 the low halves (4 b + 1, 4 b + 3).
+template <int M>
+__device__ __forceinline__ void fm_dither(float (&z)[64], int b, int h, float amp, uint64_t dkey,
+                                          int64_t key_index, const float *a128) {
+  const uint64_t dw = dither_draw(dkey, (uint64_t)key_index, M, 2 * b + h);
+  const auto sw =
+      __builtin_amdgcn_permlane32_swap((uint32_t)(dw >> 32), (uint32_t)dw, false, false);
+  dither_add<32>(&z[0], amp, sw[0], 0, a128 + 32 * h);
+  dither_add<32>(&z[32], amp, sw[1], 0, a128 + 64 + 32 * h);
 }
 
 template <int M, int WAVES, int RT, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Fimg,
     const float *__restrict__ Gs, int64_t n, int64_t base, RowMap map, float rho, uint64_t dkey,
-    float *__restrict__ norms, uint32_t *__restrict__ bits) {
+    const float *__restrict__ Dmag, float *__restrict__ norms, uint32_t *__restrict__ bits) {
   constexpr int D = 128, T = D / 16, NB = M / D, W = M / 32;
   constexpr int NF = NB * 4 * T;  // S fragments per tile walk
   constexpr int R = FM_RING;
-  constexpr bool TAB = fm_angle_table(M, DITHER, MAPPED);
   __shared__ uint4 sF[M * D / 8];
   __shared__ float sG[M];
-  __shared__ float2 sCS[TAB ? 4096 : 1];
+  __shared__ float sA[DITHER ? M : 1];  // dither magnitudes
   const int tid = threadIdx.x;
   {
     const uint4 *src = reinterpret_cast<const uint4 *>(Fimg);
     for (int i = tid; i < M * D / 8; i += 64 * WAVES) sF[i] = src[i];
     for (int i = tid; i < M; i += 64 * WAVES) sG[i] = fabsf(Gs[i]);
-    if constexpr (TAB)
-      for (int i = tid; i < 4096; i += 64 * WAVES) sCS[i] = dither_angle((uint32_t)i);
+    if constexpr (DITHER)
+      for (int i = tid; i < M; i += 64 * WAVES) sA[i] = Dmag[i];
   }
   __syncthreads();
   const int lane = tid & 63;
@@ -159,12 +160,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
     uint32_t held[RT][2];  // the previous (even) block's two words, see the stores
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      // Without dither, the wave issuing its matrix-core chain runs at a
-      // raised priority and drops it for the vector epilogue, so the other
-      // wave's epilogue fills the gaps without delaying the chain: 212
-      // against 231 us at m = 256, 406 against 427 us at m = 512.  With
-      // dither the epilogue dominates and the raise costs up to 4%.
-      if constexpr (!DITHER) __builtin_amdgcn_s_setprio(1);
+      // The wave issuing its matrix-core chain runs at a raised priority and
+      // drops it for the vector epilogue, so the other wave's epilogue fills
+      // the gaps without delaying the chain: 212 against 231 us at m = 256,
+      // 406 against 427 us at m = 512; with dither 261 against 267 us.
+      __builtin_amdgcn_s_setprio(1);
       floatx16_t acc[RT][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
                                         norms + (MAPPED ? map_row(map, key) : key));
         }
       }
-      if constexpr (!DITHER) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
       // ---- second stage of block b, per column tile
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -243,16 +243,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void fqjl_mfma_kern
         }
         const int64_t key = k0 + 32 * rt + r;
         const int64_t orow = MAPPED ? map_row(map, key < n ? key : 0) : (key < n ? key : 0);
-        if (DITHER) {
-          const float amp = rho * nrm[rt];
-          const uint64_t word0 =
-              (uint64_t)(base + orow) * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
-          const uint64_t st0 = dither_state(dkey, word0);
-#pragma unroll
-          for (int c = 0; c < 64; c += 4)
-            dither_word_add<TAB>(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), sCS, amp,
-                                 &z[c]);
-        }
+        if (DITHER) fm_dither<M>(z, b, h, rho * nrm[rt], dkey, base + orow, sA + 128 * b);
         const uint32_t w0 = pack_signs(&z[0]), w1 = pack_signs(&z[32]);
         if constexpr (NB != 2) {
           // One swap gives lane half h words 4 b + 2 h and 4 b + 2 h + 1.
@@ -324,21 +315,13 @@ __device__ __forceinline__ void fm_transform(const floatx16_t (&acc)[4], const f
   }
 }
 
-// fm_finish: dither of size amp with the word counters of output row drow
-// (the coordinates fm_transform left in lane half h), sign, and the two
-// words: 4 b + h and 4 b + 2 + h of the row.
+// fm_finish: dither of size amp for key drow (a128: block b's magnitudes),
+// sign, and the two words: 4 b + h and 4 b + 2 + h of the row.
 template <int M, bool DITHER>
 __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float amp, uint64_t dkey,
-                                          int64_t drow, uint32_t &w0, uint32_t &w1) {
-  if (DITHER) {
-    const uint64_t word0 =
-        (uint64_t)drow * (uint64_t)(M / 4) + (uint64_t)((128 * b + 32 * h) / 4);
-    const uint64_t st0 = dither_state(dkey, word0);
-#pragma unroll
-    for (int c = 0; c < 64; c += 4)
-      dither_word_add<false>(st0 + PHI * (uint64_t)(c / 4 + (c >= 32 ? 8 : 0)), nullptr, amp,
-                             &z[c]);
-  }
+                                          int64_t drow, const float *a128, uint32_t &w0,
+                                          uint32_t &w1) {
+  if (DITHER) fm_dither<M>(z, b, h, amp, dkey, drow, a128);
   w0 = pack_signs(&z[0]);
   w1 = pack_signs(&z[32]);
 }
@@ -347,8 +330,7 @@ __device__ __forceinline__ void fm_finish(float (&z)[64], int b, int h, float am
 // block b, the block's 32 image fragments read from global memory (L2)
 // instead of staging the whole image in LDS, and the blocks of a key on
 // different waves.  Measured per call at m = 256: 7.8 us against 10.2 us
-// for 256 keys (11.1 against 14.4 us with dither); at m = 512 with dither
-// 11.3 against 35.7 us.  From ~64K keys on, the persistent kernel is as
+// for 256 keys.  From ~64K keys on, the persistent kernel is as
 // fast or faster (at the 7B shape 242 against 512 us).  Same key fragments,
 // the same matrix-core accumulations in the same order, the same norm chain
 // and the same second stage as fqjl_mfma_kernel, so the bits and norms are
@@ -358,13 +340,18 @@ template <int M, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(64) void fqjl_mfma_small_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ Fimg,
     const float *__restrict__ Gs, int64_t n, int64_t base, RowMap map, float rho, uint64_t dkey,
-    float *__restrict__ norms, uint32_t *__restrict__ bits) {
+    const float *__restrict__ Dmag, float *__restrict__ norms, uint32_t *__restrict__ bits) {
   constexpr int D = 128, T = D / 16, W = M / 32;
   __shared__ float sG[D];
+  __shared__ float sA[DITHER ? D : 1];  // block b's dither magnitudes
   const int lane = threadIdx.x, r = lane & 31, h = lane >> 5;
   const int b = blockIdx.y;
   sG[lane] = fabsf(Gs[D * b + lane]);
   sG[lane + 64] = fabsf(Gs[D * b + lane + 64]);
+  if constexpr (DITHER) {
+    sA[lane] = Dmag[D * b + lane];
+    sA[lane + 64] = Dmag[D * b + lane + 64];
+  }
   const int64_t k0 = (int64_t)blockIdx.x * 32;
   FmKeys<T, 1> kt;
   fm_load<T, 1>(kt, K, k0, n, r, h);
@@ -399,7 +386,7 @@ __global__ __launch_bounds__(64) void fqjl_mfma_small_kernel(
   float z[64];
   fm_transform(acc, reinterpret_cast<const float4 *>(sG + 64 * h), z);
   uint32_t w0, w1;
-  fm_finish<M, DITHER>(z, b, h, DITHER ? rho * nrm : 0.f, dkey, base + orow, w0, w1);
+  fm_finish<M, DITHER>(z, b, h, DITHER ? rho * nrm : 0.f, dkey, base + orow, sA, w0, w1);
   const auto sw = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);  // words 4b + 2h, +1
   if (key < n)
     __builtin_nontemporal_store(u32x2_t{sw[0], sw[1]},
@@ -466,13 +453,14 @@ hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t
   if (M >= 256 && n <= QJL_FS_MAX) {
     const dim3 grid((unsigned)((n + 31) / 32), M / 128);
     hipLaunchKernelGGL((fqjl_mfma_small_kernel<M, DITHER, MAPPED>), grid, dim3(64), 0, st, K,
-                       sk->Fmfma, sk->Gs, n, base, map, sk->host.rho, sk->dither_key, norms, bits);
+                       sk->Fmfma, sk->Gs, n, base, map, sk->host.rho, sk->dither_key, sk->Dmag,
+                       norms, bits);
     return hipGetLastError();
   }
   constexpr int RT = QJL_FM_RT;
   // two 4-wave workgroups per compute unit, or one of 8 waves where the
-  // image (m = 512) or the dither's angle table leaves LDS for one
-  constexpr int WAVES = (M <= 256 && !fm_angle_table(M, DITHER, MAPPED)) ? 4 : 8;
+  // image (m = 512) leaves LDS for one
+  constexpr int WAVES = M <= 256 ? 4 : 8;
   auto kern = fqjl_mfma_kernel<M, WAVES, RT, DITHER, MAPPED>;
   static PerDevice pd_res;  // workgroups resident on the whole device
   const int resident = per_device(pd_res, [&] { return resident_workgroups(kern, 64 * WAVES); });
@@ -480,7 +468,7 @@ hipError_t launch_fm(const qjl_sketch *sk, const uint16_t *K, int64_t n, int64_t
   const int64_t want = (ntiles + WAVES - 1) / WAVES;
   const int grid = (int)(want < resident ? want : resident);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WAVES), 0, st, K, sk->Fmfma, sk->Gs, n, base,
-                     map, sk->host.rho, sk->dither_key, norms, bits);
+                     map, sk->host.rho, sk->dither_key, sk->Dmag, norms, bits);
   return hipGetLastError();
 }
 

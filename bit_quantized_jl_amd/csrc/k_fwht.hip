@@ -56,7 +56,8 @@ template <int D, typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM, boo
 __global__ __launch_bounds__(64) void fqjl_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, const float *__restrict__ Dmag,
+    float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   __shared__ float lds[D * 64];
   const int lane = threadIdx.x;
@@ -115,19 +116,9 @@ __global__ __launch_bounds__(64) void fqjl_kernel(
           for (int c = 0; c < D; ++c) yr[c] = u[c];
         }
       } else {
-        if (DITHER) {
-          const float amp = rho * nrm;
-          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) +
-                                 (uint64_t)(b * D / 4);
-          const uint64_t st0 = dither_state(dkey, word0);
-#pragma unroll
-          for (int c = 0; c < D; c += 4) {
-            float x[4];
-            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) u[c + e] += amp * x[e];
-          }
-        }
+        if (DITHER)
+          dither_words_add<D / 32>(u, rho * nrm, dkey, (uint64_t)(base + orow), m, b * D / 32,
+                                   Dmag + b * D);
         if (valid) {
           uint32_t *br = bits + orow * (int64_t)W + b * (D / 32);
 #pragma unroll
@@ -153,7 +144,8 @@ template <typename T, bool PROJECT, bool DITHER, bool PERM, bool MAPPED>
 __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, const float *__restrict__ Dmag,
+    float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   constexpr int D = 128, H = 64;
   __shared__ float lds[D * 32];
@@ -263,18 +255,9 @@ __global__ __launch_bounds__(64, sizeof(T) == 2 ? 2 : 1) void fqjl128_kernel(
           for (int c = 0; c < H; ++c) yr[c] = t[c];
         }
       } else {
-        if (DITHER) {
-          const float amp = rho * nrm;
-          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) + (uint64_t)(j0 / 4);
-          const uint64_t st0 = dither_state(dkey, word0);
-#pragma unroll
-          for (int c = 0; c < H; c += 4) {
-            float x[4];
-            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[c + e] += amp * x[e];
-          }
-        }
+        if (DITHER)
+          dither_words_add<H / 32>(t, rho * nrm, dkey, (uint64_t)(base + orow), m, j0 / 32,
+                                   Dmag + j0);
         if (valid) {
           uint32_t *br = bits + orow * (int64_t)W + j0 / 32;
 #pragma unroll
@@ -303,7 +286,8 @@ template <typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM, bool MAPPE
 __global__ __launch_bounds__(64) void fqjl256_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, const float *__restrict__ Dmag,
+    float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   constexpr int D = 256, H = 64;
   __shared__ float lds[D * 16];
@@ -384,18 +368,9 @@ __global__ __launch_bounds__(64) void fqjl256_kernel(
           for (int c = 0; c < H; ++c) yr[c] = t[c];
         }
       } else {
-        if (DITHER) {
-          const float amp = rho * nrm;
-          const uint64_t word0 = (uint64_t)(base + orow) * (uint64_t)(m / 4) + (uint64_t)(j0 / 4);
-          const uint64_t st0 = dither_state(dkey, word0);
-#pragma unroll
-          for (int c = 0; c < H; c += 4) {
-            float x[4];
-            dither_word_state(st0 + PHI * (uint64_t)(c / 4), x);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) t[c + e] += amp * x[e];
-          }
-        }
+        if (DITHER)
+          dither_words_add<H / 32>(t, rho * nrm, dkey, (uint64_t)(base + orow), m, j0 / 32,
+                                   Dmag + j0);
         if (valid) {
           uint32_t *br = bits + orow * (int64_t)W + j0 / 32;
           br[0] = pack_nonneg(&t[0]);
@@ -414,7 +389,8 @@ template <int D, typename T, bool PROJECT, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(64) void fqjl_small_kernel(
     const T *__restrict__ X, int nb, int m, const uint32_t *__restrict__ Dsign,
     const int32_t *__restrict__ P, const float *__restrict__ Gs, int64_t n, int64_t base,
-    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits,
+    RowMap map, float rho, uint64_t dkey, const float *__restrict__ Dmag,
+    float *__restrict__ norms, uint32_t *__restrict__ bits,
     float *__restrict__ Y) {
   const int lane = threadIdx.x;
   const int W = m / 32;
@@ -452,7 +428,9 @@ __global__ __launch_bounds__(64) void fqjl_small_kernel(
           Y[row * (int64_t)m + j] = y;
           continue;
         }
-        if (DITHER) y += (rho * nrm) * dither_one(dkey, (uint64_t)(base + orow), m, j);
+        if (DITHER)
+          y = dither_fma(y, rho * nrm, dither_word(dkey, (uint64_t)(base + orow), m, j >> 5),
+                         j & 31, Dmag[j]);
         word |= (y >= 0.f ? 1u : 0u) << (j & 31);
         if ((j & 31) == 31) {
           bits[orow * (int64_t)W + (j >> 5)] = word;
@@ -473,6 +451,7 @@ struct FqjlArgs {
   RowMap map;
   float rho;
   uint64_t dkey;
+  const float *Dmag;
   float *norms;
   uint32_t *bits;
   float *Y;
@@ -482,11 +461,11 @@ template <typename T, bool PROJECT, bool DITHER, bool PERM>
 void launch_fqjl128(const T *X, const FqjlArgs &a, dim3 grid, hipStream_t st) {
   if (!PROJECT && a.map.per_group != 0)
     hipLaunchKernelGGL((fqjl128_kernel<T, PROJECT, DITHER, PERM, true>), grid, dim3(64), 0, st,
-                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
   else
     hipLaunchKernelGGL((fqjl128_kernel<T, PROJECT, DITHER, PERM, false>), grid, dim3(64), 0, st,
-                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
 }
 
@@ -494,11 +473,11 @@ template <typename T, bool PROJECT, bool DITHER, bool VEC, bool PERM>
 void launch_fqjl256(const T *X, const FqjlArgs &a, dim3 grid, hipStream_t st) {
   if (!PROJECT && a.map.per_group != 0)
     hipLaunchKernelGGL((fqjl256_kernel<T, PROJECT, DITHER, VEC, PERM, true>), grid, dim3(64), 0,
-                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
   else
     hipLaunchKernelGGL((fqjl256_kernel<T, PROJECT, DITHER, VEC, PERM, false>), grid, dim3(64), 0,
-                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
 }
 
@@ -517,22 +496,22 @@ void launch_fqjl_row(const T *X, const FqjlArgs &a, int grid, hipStream_t st) {
   if (!PROJECT && a.map.per_group != 0)
     hipLaunchKernelGGL((fqjl_kernel<D, T, PROJECT, DITHER, VEC, PERM, true>), dim3(grid),
                        dim3(64), 0, st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map,
-                       a.rho, a.dkey, a.norms, a.bits, a.Y);
+                       a.rho, a.dkey, a.Dmag, a.norms, a.bits, a.Y);
   else
     hipLaunchKernelGGL((fqjl_kernel<D, T, PROJECT, DITHER, VEC, PERM, false>), dim3(grid),
                        dim3(64), 0, st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map,
-                       a.rho, a.dkey, a.norms, a.bits, a.Y);
+                       a.rho, a.dkey, a.Dmag, a.norms, a.bits, a.Y);
 }
 
 template <int D, typename T, bool PROJECT, bool DITHER>
 void launch_fqjl_small(const T *X, const FqjlArgs &a, int grid, hipStream_t st) {
   if (!PROJECT && a.map.per_group != 0)
     hipLaunchKernelGGL((fqjl_small_kernel<D, T, PROJECT, DITHER, true>), dim3(grid), dim3(64), 0,
-                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
   else
     hipLaunchKernelGGL((fqjl_small_kernel<D, T, PROJECT, DITHER, false>), dim3(grid), dim3(64), 0,
-                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey,
+                       st, X, a.nb, a.m, a.Dsign, a.P, a.Gs, a.n, a.base, a.map, a.rho, a.dkey, a.Dmag,
                        a.norms, a.bits, a.Y);
 }
 
@@ -554,7 +533,7 @@ hipError_t launch_fqjl_t(const qjl_sketch *sk, const T *X, int64_t n, int64_t ba
                          hipStream_t st) {
   const HostSketch &h = sk->host;
   const FqjlArgs a{h.m / D, h.m, sk->Dsign, sk->P, sk->Gs, n, base, map, h.rho,
-                   sk->dither_key, norms, bits, Y};
+                   sk->dither_key, sk->Dmag, norms, bits, Y};
   const int64_t tiles = (n + 63) / 64;
   const int grid = (int)(tiles < 16384 ? tiles : 16384);
   const bool proj = Y != nullptr;

@@ -20,7 +20,8 @@ constexpr int GEN_KEYS = 16;  // rows per block tile
 template <typename T, bool DITHER, bool MAPPED>
 __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
     const T *__restrict__ X, const float *__restrict__ S, int d, int m, int64_t n, int64_t base,
-    RowMap map, float rho, uint64_t dkey, float *__restrict__ norms, uint32_t *__restrict__ bits) {
+    RowMap map, float rho, uint64_t dkey, const float *__restrict__ Dmag, float *__restrict__ norms,
+    uint32_t *__restrict__ bits) {
   auto out_row = [&](int64_t r) -> int64_t { return MAPPED ? map_row(map, r) : r; };
   extern __shared__ float smem[];
   float *sX = smem;                        // [GEN_KEYS][d]
@@ -64,7 +65,9 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
       for (int r = 0; r < GEN_KEYS; ++r) {
         float y = acc[r];
         if (DITHER && valid)
-          y += (rho * sNorm[r]) * dither_one(dkey, (uint64_t)(base + out_row(r0 + r)), m, j);
+          y = dither_fma(y, rho * sNorm[r],
+                         dither_word(dkey, (uint64_t)(base + out_row(r0 + r)), m, j >> 5), j & 31,
+                         Dmag[j]);
         const uint64_t msk = __ballot(valid && y >= 0.f);
         if (r < nr) {
           uint32_t *brow = bits + out_row(r0 + r) * (int64_t)W;
@@ -79,17 +82,17 @@ __global__ __launch_bounds__(GEN_THREADS) void dense_generic_kernel(
 
 template <typename T, bool DITHER>
 hipError_t launch_generic_t(const T *X, const float *S, int d, int m, int64_t n, int64_t base,
-                            const RowMap &map, float rho, uint64_t dkey, float *norms,
-                            uint32_t *bits, hipStream_t st) {
+                            const RowMap &map, float rho, uint64_t dkey, const float *Dmag,
+                            float *norms, uint32_t *bits, hipStream_t st) {
   const int64_t tiles = (n + GEN_KEYS - 1) / GEN_KEYS;
   const int grid = (int)(tiles < 8192 ? tiles : 8192);
   const size_t shmem = (size_t)(GEN_KEYS * d + GEN_KEYS) * sizeof(float);
   if (map.per_group != 0)
     hipLaunchKernelGGL((dense_generic_kernel<T, DITHER, true>), dim3(grid), dim3(GEN_THREADS),
-                       shmem, st, X, S, d, m, n, base, map, rho, dkey, norms, bits);
+                       shmem, st, X, S, d, m, n, base, map, rho, dkey, Dmag, norms, bits);
   else
     hipLaunchKernelGGL((dense_generic_kernel<T, DITHER, false>), dim3(grid), dim3(GEN_THREADS),
-                       shmem, st, X, S, d, m, n, base, map, rho, dkey, norms, bits);
+                       shmem, st, X, S, d, m, n, base, map, rho, dkey, Dmag, norms, bits);
   return hipGetLastError();
 }
 
@@ -103,15 +106,15 @@ hipError_t launch_quantize_generic(const qjl_sketch *sk, const void *K, int dtyp
   if (dtype == QJL_DTYPE_F32) {
     const float *X = static_cast<const float *>(K);
     return dith ? launch_generic_t<float, true>(X, sk->S32, h.d, h.m, n, base, map, h.rho,
-                                               sk->dither_key, norms, bits, st)
+                                               sk->dither_key, sk->Dmag, norms, bits, st)
                 : launch_generic_t<float, false>(X, sk->S32, h.d, h.m, n, base, map, h.rho,
-                                                sk->dither_key, norms, bits, st);
+                                                sk->dither_key, sk->Dmag, norms, bits, st);
   }
   const uint16_t *X = static_cast<const uint16_t *>(K);
   return dith ? launch_generic_t<uint16_t, true>(X, sk->S16f, h.d, h.m, n, base, map, h.rho,
-                                                sk->dither_key, norms, bits, st)
+                                                sk->dither_key, sk->Dmag, norms, bits, st)
               : launch_generic_t<uint16_t, false>(X, sk->S16f, h.d, h.m, n, base, map, h.rho,
-                                                 sk->dither_key, norms, bits, st);
+                                                 sk->dither_key, sk->Dmag, norms, bits, st);
 }
 
 namespace {

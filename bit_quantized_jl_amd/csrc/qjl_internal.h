@@ -29,11 +29,20 @@ __host__ __device__ inline uint64_t stream_draw(uint64_t key, uint64_t i) {
   return mix64(key + PHI * (i + 1));
 }
 
-enum : int { STREAM_DENSE = 0, STREAM_D = 1, STREAM_P = 2, STREAM_G = 3, STREAM_DITHER = 4 };
+// Streams: 0 dense S, 1 D, 2 P, 3 G, 4 dither magnitudes (per sketch),
+// 5 dither signs (per key).
+enum : int {
+  STREAM_DENSE = 0,
+  STREAM_D = 1,
+  STREAM_P = 2,
+  STREAM_G = 3,
+  STREAM_DITHER = 4,
+  STREAM_DITHER_SIGN = 5
+};
 
 // Output row of quantized key r in a cache laid out by group: key r is key
 // r % per_group of group r / per_group and goes to row
-// (r / per_group) * stride + first + r % per_group; its dither counter is
+// (r / per_group) * stride + first + r % per_group; its dither key index is
 // key_index_base plus that row.  per_group == 0 is the identity (row r).
 // The division is 32-bit: callers keep r below 2^32.
 struct RowMap {
@@ -55,6 +64,7 @@ struct HostSketch {
   std::vector<int8_t> D;       // FQJL: nb*d, +1/-1
   std::vector<int32_t> P;      // FQJL: nb*d, permutation of [0, d) per block
   std::vector<float> G;        // FQJL: nb*d, float32 Gaussians
+  std::vector<float> Dmag;     // m dither magnitudes fp32(|N(j)|), stream 4 (every variant)
 };
 
 qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float rho,
@@ -77,7 +87,7 @@ void build_fqjl_mfma_image(const HostSketch &hs, uint16_t *out);
 struct qjl_sketch {
   qjl::HostSketch host;
   int device = -1;
-  uint64_t dither_key = 0;       // key(seed, 4)
+  uint64_t dither_key = 0;       // key(seed, 5): the stream of each key's dither signs
   void *dmem = nullptr;
   // dense
   const float *S32 = nullptr;    // m*d  float32 S (row-major)
@@ -91,6 +101,8 @@ struct qjl_sketch {
   const float *Gs = nullptr;          // nb*d  G_b[c] / sqrt(d), rounded to float32
   const uint16_t *Fmfma = nullptr;    // m*d bf16 (+-1): Pi_b H diag(D_b) in matrix-core operand
                                       // order (k_fqjl_mfma), for d = 128; null otherwise
+  // every variant
+  const float *Dmag = nullptr;        // m  dither magnitudes |N(j)| (float32)
 };
 
 namespace qjl {

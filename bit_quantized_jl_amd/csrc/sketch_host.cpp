@@ -11,6 +11,10 @@
 // P_b by Fisher-Yates with t = floor(U(b d + i) (i + 1)) on stream 2;
 // G_b[c] = float32(N(b d + c)) on stream 3.
 //
+// Dither magnitudes (same page, Key concepts: D-FQJL's Gaussian dither), for
+// every variant: a_j = float32(|N(j)|), j < m, on stream 4; each key's signs
+// are drawn on the device (device_common.h).
+//
 // U(i) = ((r >> 11) + 0.5) 2^-53 and N(i) = sqrt(-2 ln U(2i)) cos(2 pi U(2i+1))
 // (Box-Muller), evaluated in double with the C library's log and cos.
 #include <cmath>
@@ -63,6 +67,11 @@ qjl_status validate_sketch_params(int32_t d, int32_t m, int32_t variant, float r
 
 void generate_host_sketch(HostSketch &hs) {
   const int d = hs.d, m = hs.m;
+  {
+    const uint64_t key = stream_key(hs.seed, STREAM_DITHER);
+    hs.Dmag.resize((size_t)m);
+    for (int j = 0; j < m; ++j) hs.Dmag[(size_t)j] = (float)std::fabs(gaussian(key, (uint64_t)j));
+  }
   if (hs.variant == QJL_VARIANT_DENSE) {
     const uint64_t key = stream_key(hs.seed, STREAM_DENSE);
     hs.S32.resize((size_t)m * d);

@@ -40,8 +40,12 @@
  *   one seed they differ only in the permutation and the dither.
  *
  * Every random quantity comes from SplitMix64 counter streams keyed by the
- * seed (stream 0: dense S, 1: D, 2: P, 3: G, 4: dither), so a sketch and its
- * dither are reproducible from (seed, d, m, variant, rho) alone.
+ * seed (stream 0: dense S, 1: D, 2: P, 3: G, 4: dither magnitudes, 5: dither
+ * signs), so a sketch and its dither are reproducible from (seed, d, m,
+ * variant, rho) alone.  The dither of coordinate j of key i is
+ * rho ||k_i|| s_ij a_j: a_j = |N(j)| is drawn once with the sketch and s_ij
+ * is a random sign of the key's own (one stream-5 word per 64 coordinates of
+ * the key), so each key's dither is m independent standard normals.
  *
  * Layouts (all dense, row-major, no strides):
  *   K[n_keys][d], q[n_queries][d]      float32 or bfloat16 (qjl_dtype)
@@ -142,19 +146,22 @@ qjl_status qjl_sketch_export(const qjl_sketch *sk, float *S_f32, uint16_t *S_bf1
  * Host-only: generate the random parameters of a sketch without a GPU, into
  * caller-owned host buffers (any may be NULL).  Dense: S_f32[m*d],
  * S_bf16[m*d].  FQJL variants: D_signs[(m/d)*d] (+1/-1), perm[(m/d)*d]
- * (the identity for DFQJL), G[(m/d)*d].  Same validation as
- * qjl_make_sketch, except that there is no rho to check.
+ * (the identity for DFQJL), G[(m/d)*d].  Every variant: dither_mag[m], the
+ * float32 magnitudes |N(j)| that a dithered sketch's keys put their own
+ * random signs on (the Fast Quantized JL page's D-FQJL dither, Key
+ * concepts).  Same validation as qjl_make_sketch, except that there is no
+ * rho to check.
  */
 qjl_status qjl_generate_sketch_host(uint64_t seed, int32_t d, int32_t m, int32_t variant,
                                     float *S_f32, uint16_t *S_bf16, int8_t *D_signs,
-                                    int32_t *perm, float *G);
+                                    int32_t *perm, float *G, float *dither_mag);
 
 /*
  * Quantize n_keys keys: bits_out[i] = packed signs of S k_i (+ dither),
  * norms_out[i] = ||k_i||_2 (QJL abstract: a JL projection whose coordinates
  * are reduced to their signs; no per-block constants, one norm per key).
- * key_index_base is the global index of row 0; the dither of key i is drawn
- * from counter (key_index_base + i), so a cache appended in pieces gets the
+ * key_index_base is the global index of row 0; key i draws its dither signs
+ * as key index (key_index_base + i), so a cache appended in pieces gets the
  * same bits as one quantized whole.  (Which kernel runs depends on the
  * dtype, the shape and whether K and bits_out are 16-byte aligned; calls
  * that take different kernels can differ in coordinates within float32
@@ -186,7 +193,7 @@ qjl_status qjl_quantize_keys(const qjl_sketch *sk, const void *K, int32_t dtype,
  *     g * cache_rows_per_group + first_row + i
  * of norms_cache (device float[n_groups * cache_rows_per_group]) and
  * bits_cache (device uint32[n_groups * cache_rows_per_group][m/32]); no
- * other row is touched.  The dither counter of a key is key_index_base plus
+ * other row is touched.  The dither key index of a key is key_index_base plus
  * its cache row, so a cache filled by appends holds the same bits as one
  * qjl_quantize_keys call over the whole cache with the same key_index_base.
  * Errors: NULL pointers (with keys to write), negative counts or indices,

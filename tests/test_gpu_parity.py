@@ -124,8 +124,8 @@ def test_quantize_persistent_kernel_shapes(variant, d, m, rho):
     ("fqjl", 16, 64, "f32", 300),        # small d
     ("dense", 128, 256, "bf16", 300)])   # dense sketch with dither
 def test_dither_counters_at_large_key_indices(variant, d, m, dt, n):
-    # The dither's word counter is (key index) * m/4 + word in 64 bits: key
-    # indices past 2^32, whose products with m/4 pass 2^40, must give the
+    # The dither's sign-word counter is (key index) * ceil(m/64) + word in 64
+    # bits: key indices past 2^40, whose products pass 2^42, must give the
     # oracle's draws in every kernel that dithers.
     w = wl.Workload(f"bigindex_{variant}_{d}_{m}_{dt}", d, m, variant, 1, 1, n, 5, dt, "normal",
                     0.2, seed=8)
@@ -228,7 +228,7 @@ SENTINEL_NORM = -7.0
     ("fqjl", 16, 64, "f32", 0.0, 3, 5, 12, 2)])           # narrow blocks
 def test_quantize_into_cache(variant, d, m, dt, rho, G, kpg, cap, first):
     # Rows g * cap + first + i get key i of group g, quantized as the oracle
-    # does with dither counter base + that row; every other row keeps its
+    # does with dither key index base + that row; every other row keeps its
     # sentinel.
     _into_cache_case(variant, d, m, dt, rho, G, kpg, cap, first, 1234)
 
@@ -323,8 +323,8 @@ def test_fqjl256_unaligned_keys(variant, dt, rho):
                                                ("fqjl", 0.2, 256, 64, 300),
                                                ("fqjl", 0.0, 512, 40, 420),
                                                ("fqjl", 0.0, 128, 48, 380),
-                                               # dither angle from the LDS table (whole cache)
-                                               # against the inline angle (appends)
+                                               # dithered: persistent kernel (whole cache)
+                                               # against the short-call kernel (appends)
                                                ("dfqjl", 0.1, 256, 64, 300),
                                                ("fqjl", 0.3, 128, 48, 380),
                                                ("fqjl", 0.1, 512, 40, 420)])
@@ -333,10 +333,9 @@ def test_cache_built_by_appends_equals_whole(variant, rho, m, G, T):
     # cache exactly as one call over the whole cache (dither counters given
     # by the cache row).  The cases with G T > 16384 keys compare the
     # persistent matrix-core kernel (whole cache) with the short-call kernel
-    # (appends): the same sums in the same order, so the same bits.  With
-    # dither at m <= 256 the whole-cache call reads the dither angles' cos
-    # and sin from its LDS table and the appends evaluate them inline (at
-    # m = 128 the appends take the persistent kernel's row-mapped variant).
+    # (appends): the same sums in the same order, so the same bits, the
+    # dither included (at m = 128 the appends take the persistent kernel's
+    # row-mapped variant).
     note("appends vs whole", variant, rho, m, G, T)
     d = 128
     gen = torch.Generator().manual_seed(5)
