@@ -64,7 +64,11 @@ constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
 
 template <int T>
 struct Ring {
-  static constexpr int R = T <= 2 ? 4 : (T <= 4 ? 3 : 2);  // stages in the ring
+  // stages in the ring: two from m = 256 up (one stage in flight while one
+  // is computed) measured faster than three or four: 7B decode 15.8-15.9
+  // against 16.4-16.6 us (with four workgroups per group), long context
+  // 51.6-51.7 against 53.0-53.1 us
+  static constexpr int R = T <= 1 ? 4 : 2;
   static constexpr int BITS_BYTES = SM_STAGE * 16 * T;     // 64 keys x 4T words
   static constexpr int STAGE_BYTES = BITS_BYTES + SM_STAGE * 4;
   static constexpr int L = T + 1;                          // DMA instructions per stage
@@ -399,11 +403,16 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   // chunk: a multiple of the 256 keys one block step covers
   int64_t chunk = (G * nk + cus - 1) / cus;
   chunk = (chunk + 255) / 256 * 256;
-  // With a group per compute unit or more, two equal halves of each group
-  // beat the resident-round split (whose last chunk is short and which sets
-  // up each query more often): 18.0 against 19.1 us at the 7B decode shape;
-  // one workgroup per group leaves the chip a wave per SIMD and is slower.
-  if (G >= cus && 2 * G <= resident) chunk = ((nk + 1) / 2 + 255) / 256 * 256;
+  // With a group per compute unit or more, each group splits into up to four
+  // equal parts, as many as stay resident at once: at the 7B decode shape
+  // four parts (four workgroups per unit) took 15.8-15.9 us against 16.4-16.6
+  // us for two and 17.4 us for eight; two halves had beaten the resident-round
+  // split (whose last chunk is short) 18.0 against 19.1 us, and one
+  // workgroup per group leaves the chip a wave per SIMD and is slower.
+  if (G >= cus && 2 * G <= resident) {
+    const int64_t parts = 4 * G <= resident ? 4 : 2;
+    chunk = ((nk + parts - 1) / parts + 255) / 256 * 256;
+  }
   dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
   // Scores written per stage cost more than the same bytes written in one
   // burst per workgroup (long context: 56 against 53.5 us): defer them to
