@@ -13,7 +13,7 @@
 // weighted sum) per query in the caller's workspace; attn_combine_kernel
 // merges the partials of a query.
 //
-// The stream uses plain loads into registers, a ring of three 16-key stages: the
+// The stream uses plain loads into registers, a ring of three (m >= 512: two) 16-key stages: the
 // bits and norms of a stage (as the score kernel loads them) and its value
 // rows, lane l holding bf16 dimensions [8 (l % 16), 8 (l % 16) + 8) of key
 // 4 j + l / 16 of each 16-key tile (one 16-byte load covers four rows).
@@ -176,9 +176,13 @@ __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOpe
 }
 
 // Stages held in registers per wave: one is computed while the others load.
+// Three up to m = 256; two from m = 512 up, where each lane also holds twice
+// the query operand registers: long context (m = 512) 219.9 against 226.4 us
+// with three, while at the 7B decode shape (m = 256) three stay faster
+// (101.8 against 105.1 us with two).
 template <int T>
 constexpr int attn_ring() {
-  return 3;
+  return T >= 4 ? 2 : 3;
 }
 
 // The key stream of one wave: the workgroup's stages wave, wave + 4, ...
