@@ -290,9 +290,9 @@ __device__ __forceinline__ float limb_rows_combine(const v4f_t &acc, const float
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// One 16-key tile: e[qp] is the exact sum_j (2 b_j - 1) X_j of query
-// 2 qp + (lane group / 2) against key lane % 16 (in lane groups 0-1 and 2-3
-// alike).
+// One 16-key tile: e[qp] is sum_j (2 b_j - 1) X_j of query 2 qp + (lane
+// group / 2) against key lane % 16 (in lane groups 0-1 and 2-3 alike): exact
+// limb rows, combined in float32 as limb_rows_combine describes.
 template <int T, int QP>
 __device__ __forceinline__ void tile_limb_sums(const uint32_t *wb, const QueryOperands<T, QP> &qo,
                                                float (&e)[QP]) {

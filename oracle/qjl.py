@@ -4,9 +4,9 @@ Test infrastructure only: nothing in the product path imports this module.
 
 Source: the QJL abstract (Zandieh, Daliri, Han) on Majid Daliri's
 scholarfeed page.  A key is JL-projected and only the sign of each sketched
-coordinate is kept (1 bit each, no zero-point or scale); the query gets the
-same JL transform without quantization; the product of the two is an
-unbiased estimate of the inner product.
+coordinate is kept (1 bit each, no zero-point or scale); the query is
+projected by the same matrix and left in full precision; the product of the
+two is an unbiased estimate of the inner product.
 
 Plainest reading of what the abstract leaves open (each is one line here):
   * the per-key norm ||k|| is stored beside the bits (one float per key, not

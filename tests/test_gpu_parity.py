@@ -419,7 +419,11 @@ def test_projected_keys_reproduce_their_bits(variant, d, m):
 @pytest.mark.parametrize("m,G,nq,nk", [(256, 1, 16, 4096), (256, 3, 1, 1000), (512, 2, 1, 777),
                                        (32, 2, 3, 65), (96, 1, 2, 130), (1024, 1, 1, 300),
                                        (128, 5, 4, 17), (256, 2, 7, 1), (2048, 1, 2, 64),
-                                       (1024, 2, 3, 300), (1024, 1, 4, 5000)])
+                                       (1024, 2, 3, 300), (1024, 1, 4, 5000),
+                                       # at least a group per compute unit: each group
+                                       # split into up to four parts, the last one short
+                                       (256, 300, 1, 1000), (256, 256, 3, 2500),
+                                       (512, 260, 2, 777), (128, 256, 1, 4097)])
 def test_score_random_bits(m, G, nq, nk):
     # m = 1024 with query pairs: the kernel whose stage ring and query image
     # leave the least LDS for deferred scores (and no room for the default
