@@ -64,24 +64,31 @@ constexpr int SM_STAGE = 64;  // keys per stage (4 MFMA tiles of 16)
 
 template <int T>
 struct Ring {
-  // stages in the ring: two from m = 256 up (one stage in flight while one
-  // is computed) measured faster than three or four: 7B decode 15.8-15.9
-  // against 16.4-16.6 us (with four workgroups per group), long context
-  // 51.6-51.7 against 53.0-53.1 us
-  static constexpr int R = T <= 1 ? 4 : 2;
   static constexpr int BITS_BYTES = SM_STAGE * 16 * T;     // 64 keys x 4T words
   static constexpr int STAGE_BYTES = BITS_BYTES + SM_STAGE * 4;
   static constexpr int L = T + 1;                          // DMA instructions per stage
 };
 
-template <int T>
+// Stages in the ring.  One query pair per pass, from m = 256 up: two (one
+// stage in flight while one is computed), which measured faster than three
+// or four (7B decode 15.8-15.9 against 16.4-16.6 us with four workgroups per
+// group, long context 51.6-51.7 against 53.0-53.1 us).  More query pairs per
+// pass compute longer per stage and keep the deeper rings: with two stages,
+// eight and sixteen queries per group took 47 and 91 against 41 and 79 us.
+template <int T, int QP>
+constexpr int ring_depth() {
+  if (QP == 1 && T >= 2) return 2;
+  return T <= 2 ? 4 : (T <= 4 ? 3 : 2);
+}
+
+template <int T, int R>
 __device__ __forceinline__ void wait_stages(int pending) {
   constexpr int L = Ring<T>::L;
   switch (pending) {
     case 0: wait_vmcnt<0>(); break;
     case 1: wait_vmcnt<L>(); break;
-    case 2: if constexpr (Ring<T>::R > 2) wait_vmcnt<2 * L>(); break;
-    default: if constexpr (Ring<T>::R > 3) wait_vmcnt<3 * L>(); break;
+    case 2: if constexpr (R > 2) wait_vmcnt<2 * L>(); break;
+    default: if constexpr (R > 3) wait_vmcnt<3 * L>(); break;
   }
 }
 
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
   constexpr int W = 4 * T;         // 32-bit words per key (m = 128 T)
   constexpr int m = 32 * W;
   constexpr int NQ = 2 * QP;       // queries per pass
-  constexpr int R = Ring<T>::R;
+  constexpr int R = ring_depth<T, QP>();
   constexpr int SB = Ring<T>::STAGE_BYTES;
   constexpr int JL = (m + 63) / 64;            // query coordinates per lane
   __shared__ __attribute__((aligned(16))) unsigned char sAimg[QueryOperands<T, QP>::IMAGE_BYTES];
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(SM_THREADS) void score_mfma_kernel(
         // stages issued after stage j: up to the last real one, and at least
         // the R - 2 issued before the loop
         const int last = (ns - 1) < (j + R - 1) ? (ns - 1) : (j + R - 1);
-        wait_stages<T>((last > R - 2 ? last : R - 2) - j);
+        wait_stages<T, R>((last > R - 2 ? last : R - 2) - j);
         const unsigned char *slot = &sRing[wave][j % R][0];
         const int64_t k0 = kbeg + SM_STAGE * (wave + SM_WAVES * j);
         StageRead<T> sr;
@@ -400,26 +407,6 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
   const int resident =
       per_device(pd_res, [] { return resident_workgroups(score_mfma_kernel<T, QP, false>, SM_THREADS); });
   const int cus = per_device(pd_cus, device_compute_units);
-  // chunk: a multiple of the 256 keys one block step covers
-  int64_t chunk = (G * nk + cus - 1) / cus;
-  chunk = (chunk + 255) / 256 * 256;
-  // With a group per compute unit or more, each group splits into up to four
-  // equal parts, as many as stay resident at once: at the 7B decode shape
-  // four parts (four workgroups per unit) took 15.8-15.9 us against 16.4-16.6
-  // us for two and 17.4 us for eight; two halves had beaten the resident-round
-  // split (whose last chunk is short) 18.0 against 19.1 us, and one
-  // workgroup per group leaves the chip a wave per SIMD and is slower.
-  if (G >= cus && 2 * G <= resident) {
-    const int64_t parts = 4 * G <= resident ? 4 : 2;
-    chunk = ((nk + parts - 1) / parts + 255) / 256 * 256;
-  }
-  dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
-  // Scores written per stage cost more than the same bytes written in one
-  // burst per workgroup (long context: 56 against 53.5 us): defer them to
-  // LDS when a pass's scores of the workgroup's keys fit and the extra LDS
-  // leaves as many of this launch's workgroups resident at once.
-  const int64_t nqd = nq < 2 * QP ? nq : 2 * QP;
-  const size_t dyn = (size_t)(nqd * chunk) * sizeof(float);
   static PerDevice pd_lds, pd_static;
   const int lds_cu = per_device(pd_lds, [] {
     int dev = 0, v = 0;
@@ -439,12 +426,39 @@ hipError_t launch_sm(const float *Sq, const uint32_t *bits, const float *norms, 
     }
     return (int)a.sharedSizeBytes + 1;
   }) - 1;
-  const int64_t wgs = (int64_t)grid.x * grid.y;
+  // Scores written per stage cost more than the same bytes written in one
+  // burst per workgroup (long context: 56 against 53.5 us): a launch defers
+  // them to LDS when a pass's scores of the workgroup's keys fit and the
+  // extra LDS leaves as many of its workgroups resident at once.
+  const int64_t nqd = nq < 2 * QP ? nq : 2 * QP;
   const int64_t per_cu_plain = resident / cus;
-  const int64_t per_cu_defer = (int64_t)lds_cu / ((int64_t)lds_static + (int64_t)dyn);
-  const int64_t need_per_cu = (wgs + cus - 1) / cus;
-  const int64_t want = need_per_cu < per_cu_plain ? need_per_cu : per_cu_plain;
-  if (dyn > 0 && dyn <= defer_limit<T, QP>() && per_cu_defer >= want)
+  auto defers = [&](int64_t ch, int64_t wgs) {
+    const size_t dyn = (size_t)(nqd * ch) * sizeof(float);
+    const int64_t per_cu_defer = (int64_t)lds_cu / ((int64_t)lds_static + (int64_t)dyn);
+    const int64_t need_per_cu = (wgs + cus - 1) / cus;
+    const int64_t want = need_per_cu < per_cu_plain ? need_per_cu : per_cu_plain;
+    return dyn > 0 && dyn <= defer_limit<T, QP>() && per_cu_defer >= want;
+  };
+  auto chunk_of = [&](int64_t parts) { return ((nk + parts - 1) / parts + 255) / 256 * 256; };
+  // chunk: a multiple of the 256 keys one block step covers
+  int64_t chunk = (G * nk + cus - 1) / cus;
+  chunk = (chunk + 255) / 256 * 256;
+  // With a group per compute unit or more, each group splits into equal parts
+  // (no short last chunk as in the resident-round split: two halves took 18.0
+  // against 19.1 us at the 7B decode shape; one workgroup per group leaves the
+  // chip a wave per SIMD and is slower).  Four parts, where all stay resident
+  // and still defer their scores: 15.8-15.9 against 16.4-16.6 us for two (17.4
+  // us for eight) at the 7B decode shape; with eight or sixteen queries per
+  // group, whose scores are stored per stage, four parts were slower (47 and
+  // 91 against 41 and 79 us), so those keep two.
+  if (G >= cus && 2 * G <= resident) {
+    const int64_t c4 = chunk_of(4);
+    const int64_t rows = G < 65535 ? G : 65535;  // the grid's groups at a time
+    chunk = 4 * G <= resident && defers(c4, rows * ((nk + c4 - 1) / c4)) ? c4 : chunk_of(2);
+  }
+  dim3 grid((unsigned)((nk + chunk - 1) / chunk), (unsigned)(G < 65535 ? G : 65535));
+  const size_t dyn = (size_t)(nqd * chunk) * sizeof(float);
+  if (defers(chunk, (int64_t)grid.x * grid.y))
     launch_sm_kernel<T, QP, true>(grid, dyn, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);
   else
     launch_sm_kernel<T, QP, false>(grid, 0, st, Sq, bits, norms, G, nq, nk, (int)chunk, c, scores);
