@@ -13,7 +13,7 @@
 // weighted sum) per query in the caller's workspace; attn_combine_kernel
 // merges the partials of a query.
 //
-// The stream uses plain loads into registers, a ring of three (m >= 512: two) 16-key stages: the
+// The stream uses plain loads into registers, a ring of 16-key stages: the
 // bits and norms of a stage (as the score kernel loads them) and its value
 // rows, lane l holding bf16 dimensions [8 (l % 16), 8 (l % 16) + 8) of key
 // 4 j + l / 16 of each 16-key tile (one 16-byte load covers four rows).
@@ -176,13 +176,13 @@ __device__ __forceinline__ void attn_stage(const AttnStage<T> &s, const QueryOpe
 }
 
 // Stages held in registers per wave: one is computed while the others load.
-// Three up to m = 256; two from m = 512 up, where each lane also holds twice
-// the query operand registers: long context (m = 512) 219.9 against 226.4 us
-// with three, while at the 7B decode shape (m = 256) three stay faster
-// (101.8 against 105.1 us with two).
-template <int T>
+// Three, except two for a single query from m = 512 up: at long context
+// (m = 512) one query took 219.9 against 226.4 us with three, but a query
+// pair 239.4 against 221.3 us; at the 7B decode shape (m = 256) three stay
+// faster for one query too (101.8 against 105.1 us with two).
+template <int T, bool PAIR>
 constexpr int attn_ring() {
-  return T >= 4 ? 2 : 3;
+  return T >= 4 && !PAIR ? 2 : 3;
 }
 
 // The key stream of one wave: the workgroup's stages wave, wave + 4, ...
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(SM_THREADS, QP == 1 ? 2 : 1) void attn_partial_kern
   }
   const int nkb = kend > kbeg ? kend - kbeg : 0;  // keys of the descriptors' range
   const int ns = (nstage_blk - wave + SM_WAVES - 1) / SM_WAVES;
-  constexpr int R = attn_ring<T>();
+  constexpr int R = attn_ring<T, PAIR>();
   const int nsr = (ns + R - 1) / R * R;  // whole rounds of the ring
 
   for (int64_t g = blockIdx.y; g < G; g += gridDim.y) {
@@ -446,7 +446,7 @@ void attn_grid(int64_t G, int64_t nk, int64_t *chunk_out, int *gx_out) {
   static PerDevice pd_cus;
   const int cus = per_device(pd_cus, device_compute_units);
   int64_t chunk = (G * nk + cus - 1) / cus;
-  constexpr int round = attn_ring<T>() * AT_STAGE * SM_WAVES;
+  constexpr int round = 3 * AT_STAGE * SM_WAVES;  // whole rounds of a three-stage ring
   chunk = (chunk + round - 1) / round * round;
   if (G >= cus) chunk = (nk + round - 1) / round * round;
   *chunk_out = chunk;
